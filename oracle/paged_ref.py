@@ -1,0 +1,230 @@
+"""fp64 CPU oracle for paged KV-cache decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or links
+this module: only the test suite, the smoke check and the benchmark's CPU
+baseline leg may use it.  It shares no code with the HIP kernels (no common
+headers, helpers, tables or pre/post-processing); the only thing both sides
+consume is the seeded input generator in ``workloads/``.
+
+What it computes, and where that comes from
+-------------------------------------------
+* Paged cache layout: fixed-size blocks plus one block table per sequence
+  (nanoserve write-up, section "What I built", paged KV cache item).  The pool
+  layout is ``[num_blocks, block_size, num_kv_heads, head_dim]``, one pool for
+  K and one for V.
+* Decode attention: one new query token per sequence attends over all of its
+  cached positions, reached through the block table (same section, fused
+  paged-attention decode item).  The write-up compares that kernel against a
+  "gather the K/V, then run dense scaled-dot-product attention" path (section
+  "Results"); the plain definition of what both compute is
+
+      K_b[t] = K_pool[table[b, t // bs], t % bs, kvh(h)]      t < ctx_b
+      out[b, h] = softmax(scale * K_b q[b, h]) @ V_b
+
+  and that definition is what this module writes out, in fp64, from the fp16
+  inputs (fp16 -> fp64 is exact).  Online softmax and the split-context merge
+  reach the same value up to rounding order, so there is nothing else to model.
+* Split-context decode ("flash-decoding style" arm, author's post thread, the
+  Day 74 post): each sequence's positions are cut into partitions of
+  ``partition_size`` tokens; each partition yields its normalised output and
+  the natural-log log-sum-exp of its logits; the merge weights partition p by
+  exp(lse_p - LSE).  The pages name the arm but not the merge; the LSE-weighted
+  merge is the plainest exact reading.
+* Cache write: each step writes the new token's K and V into its slot of the
+  pool (Inference Engineering, Day 11 post on how vLLM works: the executor
+  updates the cache with the new key and value vectors).  Slots are addressed
+  by ``slot = physical_block * block_size + offset``; a negative slot is
+  skipped.
+
+Readings where the pages are silent (all listed in the design doc):
+* GQA: query head h uses KV head ``h // (Hq // Hkv)`` (contiguous groups).
+* ``context_lens`` counts the attended positions, including the token the
+  same step appended.
+* ctx == 0 gives a zero output and lse = -inf.
+* The scale the kernel receives is an fp32 value; the oracle uses that fp32
+  value widened to fp64 and applies it to the fp64 dot product.
+
+Every function here is pinned by ``tests/test_oracle.py`` against things other
+than itself (torch's fp64 SDPA on contiguous K/V, closed forms, block-id
+permutation invariance, split == unsplit, pure-Python brute force, and the
+chunked-prefill block arithmetic printed on the Inference Engineering Day 12
+page); ``tests/test_oracle_mutants.py`` plants plausible mistakes here and
+checks that a pin catches each one.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "kv_head_of",
+    "heads_of_kv_head",
+    "gather_sequence_kv",
+    "attend",
+    "merge_partitions",
+    "paged_attention_decode",
+    "paged_attention_decode_split",
+    "split_reduce",
+    "kv_cache_append",
+    "fp32_scale",
+]
+
+
+def fp32_scale(scale: float) -> float:
+    """The softmax scale exactly as an fp32 kernel argument carries it."""
+    return float(np.float64(np.float32(scale)))
+
+
+def kv_head_of(h: int, num_q_heads: int, num_kv_heads: int) -> int:
+    """KV head serving query head ``h``: contiguous groups of Hq/Hkv heads."""
+    group = num_q_heads // num_kv_heads
+    return h // group
+
+
+def gather_sequence_kv(pool: np.ndarray, table_row: np.ndarray, n: int,
+                       block_size: int, kvh: int) -> np.ndarray:
+    """Rows 0..n-1 of one sequence's K (or V) for one KV head, as fp64 [n, D].
+
+    Logical position t lives in physical block ``table_row[t // block_size]``
+    at offset ``t % block_size`` (nanoserve, "What I built": block allocator
+    plus per-sequence block tables).
+    """
+    t = np.arange(n, dtype=np.int64)
+    phys = table_row[t // block_size].astype(np.int64)
+    off = t % block_size
+    return pool[phys, off, kvh, :].astype(np.float64)
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+    """Softmax attention of query rows q [G, D] over K, V [n, D], in fp64.
+
+    Returns (out [G, D], lse [G]) with lse the natural-log log-sum-exp of the
+    scaled logits.  n == 0 gives zeros and -inf.
+    """
+    G, D = q.shape
+    n = K.shape[0]
+    if n == 0:
+        return np.zeros((G, D)), np.full(G, -np.inf)
+    s = scale * (q @ K.T)                      # [G, n]
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    out = (e @ V) / l
+    lse = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+def heads_of_kv_head(kvh: int, num_q_heads: int, num_kv_heads: int):
+    """Query heads served by KV head ``kvh`` (inverse of ``kv_head_of``)."""
+    return [h for h in range(num_q_heads)
+            if kv_head_of(h, num_q_heads, num_kv_heads) == kvh]
+
+
+def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens,
+                           scale, return_lse: bool = False, seqs=None):
+    """Single-token decode over the paged cache (plain definition, fp64).
+
+    q [B, Hq, D] fp16; pools [NB, bs, Hkv, D] fp16; block_tables [B, maxb]
+    int32; context_lens [B] int32.  Returns out [B, Hq, D] fp64 (and lse
+    [B, Hq] when asked).  ``seqs`` restricts the work to some sequences; the
+    rows of the others stay zero / -inf.  One gather per (sequence, KV head)
+    serves the whole query group.
+    """
+    B, Hq, D = q.shape
+    _, bs, Hkv, _ = k_pool.shape
+    sc = fp32_scale(scale)
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b in (range(B) if seqs is None else seqs):
+        n = int(context_lens[b])
+        for kvh in range(Hkv):
+            heads = heads_of_kv_head(kvh, Hq, Hkv)
+            K = gather_sequence_kv(k_pool, block_tables[b], n, bs, kvh)
+            V = gather_sequence_kv(v_pool, block_tables[b], n, bs, kvh)
+            o, ls = attend(q[b, heads].astype(np.float64), K, V, sc)
+            out[b, heads] = o
+            lse[b, heads] = ls
+    return (out, lse) if return_lse else out
+
+
+def paged_attention_decode_split(q, k_pool, v_pool, block_tables, context_lens,
+                                 scale, partition_size: int,
+                                 max_partitions: int):
+    """Split-context pass: per partition p of ``partition_size`` logical
+    positions, the normalised partial output and its log-sum-exp.
+
+    Returns partial_out [B, Hq, P_max, D] and partial_lse [B, Hq, P_max]
+    (fp64).  A partition that starts at or past ctx is empty: lse = -inf and
+    a zero output.
+    """
+    B, Hq, D = q.shape
+    _, bs, Hkv, _ = k_pool.shape
+    sc = fp32_scale(scale)
+    po = np.zeros((B, Hq, max_partitions, D))
+    pl = np.full((B, Hq, max_partitions), -np.inf)
+    for b in range(B):
+        n = int(context_lens[b])
+        for kvh in range(Hkv):
+            K = gather_sequence_kv(k_pool, block_tables[b], n, bs, kvh)
+            V = gather_sequence_kv(v_pool, block_tables[b], n, bs, kvh)
+            heads = heads_of_kv_head(kvh, Hq, Hkv)
+            qg = q[b, heads].astype(np.float64)
+            for p in range(max_partitions):
+                lo, hi = p * partition_size, min((p + 1) * partition_size, n)
+                if lo >= hi:
+                    continue
+                o, ls = attend(qg, K[lo:hi], V[lo:hi], sc)
+                po[b, heads, p] = o
+                pl[b, heads, p] = ls
+    return po, pl
+
+
+def merge_partitions(outs: np.ndarray, lses: np.ndarray):
+    """LSE-weighted merge of partial results for one query head.
+
+    outs [P, D], lses [P] (natural log; -inf marks an empty partition).
+    LSE = log sum_p exp(lse_p); out = sum_p exp(lse_p - LSE) * out_p.
+    """
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    if lses.size == 0 or np.all(np.isneginf(lses)):
+        return np.zeros(outs.shape[-1]), -np.inf
+    mx = lses[np.isfinite(lses)].max()
+    w = np.where(np.isneginf(lses), 0.0, np.exp(lses - mx))
+    total = w.sum()
+    L = mx + np.log(total)
+    out = (w[:, None] * np.where(np.isneginf(lses)[:, None], 0.0, outs)).sum(0) / total
+    return out, L
+
+
+def split_reduce(partial_out, partial_lse, context_lens, partition_size: int):
+    """Merge the ceil(ctx/partition_size) valid partitions of every
+    (sequence, query head).  Returns out [B, Hq, D] and lse [B, Hq] (fp64)."""
+    B, Hq, Pm, D = partial_out.shape
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = int(context_lens[b])
+        used = min(Pm, -(-n // partition_size))
+        for h in range(Hq):
+            out[b, h], lse[b, h] = merge_partitions(partial_out[b, h, :used],
+                                                    partial_lse[b, h, :used])
+    return out, lse
+
+
+def kv_cache_append(k_pool, v_pool, k_new, v_new, slot_mapping):
+    """Write each new token's K/V rows into its slot; returns new pools.
+
+    k_new, v_new [N, Hkv, D]; slot_mapping [N] int64 with
+    slot = physical_block * block_size + offset; slot < 0 is skipped.  The
+    inputs are not modified.
+    """
+    kp = k_pool.copy()
+    vp = v_pool.copy()
+    nb, bs = kp.shape[0], kp.shape[1]
+    flat_k = kp.reshape(nb * bs, *kp.shape[2:])
+    flat_v = vp.reshape(nb * bs, *vp.shape[2:])
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    keep = slots >= 0
+    flat_k[slots[keep]] = k_new[keep]
+    flat_v[slots[keep]] = v_new[keep]
+    return kp, vp

@@ -1,0 +1,146 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that at least
+one pin from ``test_oracle.py`` fails for every one of them."""
+import numpy as np
+import pytest
+
+from oracle import paged_ref as ref
+import test_oracle as pins
+
+
+def _attend_factory(kind):
+    def attend(q, K, V, scale):
+        G, D = q.shape
+        n = K.shape[0]
+        if n == 0:
+            return np.zeros((G, D)), np.full(G, -np.inf)
+        s = (q @ K.T) if kind == "no_scale" else scale * (q @ K.T)
+        if kind == "keys_as_values":
+            V = K
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(-(s - m)) if kind == "sign" else np.exp(s - m)
+        if kind == "sign":
+            e = e / e.max(axis=1, keepdims=True)
+        l = e.sum(axis=1, keepdims=True)
+        out = (e @ V) if kind == "no_norm" else (e @ V) / l
+        lse = (m + (l if kind == "lse_no_log" else np.log(l)))[:, 0]
+        if kind == "drop_last":
+            o2, _ = ref_attend_orig(q, K[:-1], V[:-1], scale) if n > 1 else (out, None)
+            out = o2
+        return out, lse
+    return attend
+
+
+ref_attend_orig = ref.attend
+
+
+def _gather_factory(kind):
+    orig = ref.gather_sequence_kv
+
+    def gather(pool, table_row, n, block_size, kvh):
+        t = np.arange(n, dtype=np.int64)
+        if kind == "offset_shift":
+            phys = table_row[t // block_size].astype(np.int64)
+            off = (t + 1) % block_size
+        elif kind == "swapped_index":
+            phys = table_row[(t % block_size) % len(table_row)].astype(np.int64)
+            off = (t // block_size) % block_size
+        elif kind == "identity_table":
+            phys = (t // block_size)
+            off = t % block_size
+        else:
+            return orig(pool, table_row, n, block_size, kvh)
+        return pool[phys, off, kvh, :].astype(np.float64)
+    return gather
+
+
+def _merge_factory(kind):
+    def merge(outs, lses):
+        outs = np.asarray(outs, dtype=np.float64)
+        lses = np.asarray(lses, dtype=np.float64)
+        if lses.size == 0 or np.all(np.isneginf(lses)):
+            return np.zeros(outs.shape[-1]), -np.inf
+        mx = lses[np.isfinite(lses)].max()
+        if kind == "sign":
+            w = np.where(np.isneginf(lses), 0.0, np.exp(mx - lses))
+        else:  # unweighted
+            w = np.where(np.isneginf(lses), 0.0, 1.0)
+        total = w.sum()
+        L = mx + np.log(total)
+        out = (w[:, None] * np.where(np.isneginf(lses)[:, None], 0.0, outs)).sum(0) / total
+        return out, L
+    return merge
+
+
+def _append_transposed(k_pool, v_pool, k_new, v_new, slot_mapping):
+    kp, vp = k_pool.copy(), v_pool.copy()
+    nb, bs = kp.shape[:2]
+    for i, s in enumerate(np.asarray(slot_mapping)):
+        if s < 0:
+            continue
+        blk, off = int(s) % nb, (int(s) // nb) % bs      # wrong decomposition
+        kp[blk, off] = k_new[i]
+        vp[blk, off] = v_new[i]
+    return kp, vp
+
+
+def _append_no_skip(k_pool, v_pool, k_new, v_new, slot_mapping):
+    kp, vp = k_pool.copy(), v_pool.copy()
+    fk = kp.reshape(-1, *kp.shape[2:])
+    fv = vp.reshape(-1, *vp.shape[2:])
+    s = np.asarray(slot_mapping, dtype=np.int64)
+    fk[s] = k_new                      # negative slot writes the last row
+    fv[s] = v_new
+    return kp, vp
+
+
+def _split_factory(kind):
+    orig = ref.paged_attention_decode_split
+
+    def split(q, k_pool, v_pool, block_tables, context_lens, scale, partition_size,
+              max_partitions):
+        po, pl = orig(q, k_pool, v_pool, block_tables, context_lens, scale,
+                      partition_size, max_partitions)
+        if kind == "lse_log2":
+            pl = pl / np.log(2.0)
+        return po, pl
+    return split
+
+
+MUTANTS = {
+    "gqa_modulo": ("kv_head_of", lambda h, Hq, Hkv: h % Hkv),
+    "no_scale": ("attend", _attend_factory("no_scale")),
+    "softmax_sign": ("attend", _attend_factory("sign")),
+    "no_normalise": ("attend", _attend_factory("no_norm")),
+    "keys_as_values": ("attend", _attend_factory("keys_as_values")),
+    "lse_without_log": ("attend", _attend_factory("lse_no_log")),
+    "drops_last_token": ("attend", _attend_factory("drop_last")),
+    "offset_shift": ("gather_sequence_kv", _gather_factory("offset_shift")),
+    "swapped_block_offset": ("gather_sequence_kv", _gather_factory("swapped_index")),
+    "ignores_block_table": ("gather_sequence_kv", _gather_factory("identity_table")),
+    "merge_sign": ("merge_partitions", _merge_factory("sign")),
+    "merge_unweighted": ("merge_partitions", _merge_factory("unweighted")),
+    "append_transposed_slot": ("kv_cache_append", _append_transposed),
+    "append_no_skip": ("kv_cache_append", _append_no_skip),
+    "split_lse_base2": ("paged_attention_decode_split", _split_factory("lse_log2")),
+    "scale_not_fp32": ("fp32_scale", lambda s: float(s) * (1 + 1e-7)),
+}
+
+
+def _fails(fn):
+    try:
+        fn()
+    except (AssertionError, IndexError, ValueError, FloatingPointError):
+        return True
+    return False
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_a_pin_catches_mutant(name, monkeypatch):
+    attr, repl = MUTANTS[name]
+    monkeypatch.setattr(ref, attr, repl)
+    caught = [i for i, p in enumerate(pins.ALL_PINS) if _fails(p)]
+    assert caught, f"no pin catches the planted mistake {name!r}"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert not [i for i, p in enumerate(pins.ALL_PINS) if _fails(p)]
