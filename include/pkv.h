@@ -1,0 +1,215 @@
+/*
+ * pkv.h -- paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpkv.so.  Four entry points make up the decode hot path of a
+ * paged KV cache:
+ *
+ *   kv_cache_append               write each new token's K/V into its slot
+ *   paged_attention_decode        one query token per sequence, attending over
+ *                                 the sequence's cached K/V reached through its
+ *                                 block table, with an online softmax
+ *   paged_attention_decode_split  the same over fixed-size partitions of each
+ *                                 sequence's context ("flash-decoding" style
+ *                                 split), writing per-partition results
+ *   split_reduce                  log-sum-exp weighted merge of the partitions
+ *
+ * Sources (the pages describing the method):
+ *   - nanoserve project write-up, section "What I built": a paged KV cache
+ *     (block allocator plus per-sequence block tables) and a fused decode
+ *     kernel that runs an online softmax over the block table.
+ *   - the nanoserve author's post thread, Day 74 post: a split-attention
+ *     ("flash-decoding style") decode arm next to the plain one.
+ *   - Inference Engineering, Day 11 post (how vLLM works): every step writes
+ *     the new key and value vectors into the cache, whose fixed-size blocks
+ *     are handed out per request through a block table.
+ * The pages give no signatures, layouts or merge rule; the choices below are
+ * this library's and are the plainest reading of the pages.
+ *
+ * Conventions common to every call
+ * --------------------------------
+ *  - fp16 means IEEE binary16 (_Float16).  Every tensor is dense, row-major,
+ *    with the shape given in its comment.
+ *  - Every pointer is device memory owned by the caller.  The library holds
+ *    no state, never allocates, never synchronises and never reads device
+ *    data on the host.  Work is enqueued on `stream` (a hipStream_t passed as
+ *    void*; NULL is the null stream) and runs asynchronously.
+ *  - K/V pools have the layout [num_blocks, block_size, num_kv_heads,
+ *    head_dim]; one pool holds K, another V.  Logical position t of sequence
+ *    b lives in physical block block_tables[b, t / block_size] at offset
+ *    t % block_size.
+ *  - GQA: query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *  - Supported shapes: head_dim 64 or 128; block_size a multiple of 16 in
+ *    [16, 256]; num_q_heads / num_kv_heads <= 16.
+ *  - Alignment: fp16 and fp32 tensors 16 bytes, int32 arrays 4 bytes,
+ *    slot_mapping 8 bytes.
+ *  - Empty calls (num_tokens == 0, B == 0) return PKV_OK without launching;
+ *    their per-token / per-sequence pointers may then be NULL.
+ *  - Return value: PKV_OK, or a negative status.  PKV_ERR_INVALID_ARG and
+ *    PKV_ERR_UNSUPPORTED are decided from the arguments alone, before any
+ *    HIP call, and nothing is launched.  PKV_ERR_LAUNCH reports a HIP error
+ *    from the launch (hipGetLastError).
+ *  - Device data contract (not checkable on the host): context_lens[b] in
+ *    [0, max_blocks_per_seq * block_size]; block_tables[b, i] in
+ *    [0, num_blocks) for i < ceil(context_lens[b] / block_size); entries past
+ *    that are never read.  The kernels guard themselves: a context length
+ *    outside the range is clamped into it, and a block id outside
+ *    [0, num_blocks) is not read and its positions do not contribute.  So a
+ *    contract violation gives wrong numbers, never an out-of-bounds access.
+ *  - Outputs must not alias inputs.  Calls that write the same memory race
+ *    unless ordered by the stream.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, ...   */
+  PKV_ERR_UNSUPPORTED = -2, /* head_dim / block_size / group not compiled  */
+  PKV_ERR_LAUNCH = -3       /* HIP reported an error for the launch        */
+};
+
+/* Static, human-readable name of a status code. */
+const char* pkv_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int pkv_version(void);
+
+/*
+ * pkv_set_launch_config -- tuning aid: choose the launch shape of an
+ * attention pass for later calls in this process.
+ *   which              0 = paged_attention_decode, 1 = the split pass.
+ *   waves_per_group    wavefronts (64 lanes) per workgroup: 1, 2, 4 or 8;
+ *                      0 restores the default.
+ *   subtiles_per_iter  16-token subtiles a wave loads per loop iteration: 1, 2
+ *                      or 4; 0 restores the default.
+ * Results do not depend on the shape beyond fp32 summation order.  Not
+ * thread-safe with respect to concurrent launches (a launch reads whichever
+ * value is current).  Returns PKV_OK or PKV_ERR_INVALID_ARG.
+ */
+int pkv_set_launch_config(int which, int waves_per_group, int subtiles_per_iter);
+
+/*
+ * kv_cache_append -- write the K and V rows of new tokens into their slots.
+ *
+ * Defined by the cache update of every decode step (Inference Engineering,
+ * Day 11 post) into the block layout of the nanoserve paged cache ("What I
+ * built").  Also serves chunked prefill: several tokens of one sequence, in
+ * any number of blocks, in one call (Inference Engineering, Day 12 post).
+ *
+ *   k_pool, v_pool  [num_blocks, block_size, num_kv_heads, head_dim] fp16,
+ *                   updated in place.
+ *   k_new, v_new    [num_tokens, num_kv_heads, head_dim] fp16.
+ *   slot_mapping    [num_tokens] int64: slot = block * block_size + offset.
+ *                   A negative slot, or one >= num_blocks * block_size, skips
+ *                   that token.  Slots must be unique within a call.
+ *
+ * The copy is bit-exact.  num_tokens == 0 is a no-op that returns PKV_OK.
+ */
+int kv_cache_append(void* k_pool, void* v_pool,
+                    const void* k_new, const void* v_new,
+                    const int64_t* slot_mapping,
+                    int32_t num_tokens, int32_t num_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t head_dim, void* stream);
+
+/*
+ * paged_attention_decode -- single-token decode attention over the paged
+ * cache, online softmax over the block table (nanoserve write-up, "What I
+ * built", fused paged-attention decode kernel):
+ *
+ *   out[b, h, :] = sum_t softmax_t(scale * q[b, h, :] . K_b[t, :]) V_b[t, :]
+ *
+ * over t < context_lens[b], with K_b, V_b the rows of KV head
+ * h / (num_q_heads / num_kv_heads) reached through block_tables[b].
+ *
+ *   out           [B, num_q_heads, head_dim] fp16 (written).
+ *   q             [B, num_q_heads, head_dim] fp16.
+ *   k_pool/v_pool [num_blocks, block_size, num_kv_heads, head_dim] fp16.
+ *   block_tables  [B, max_blocks_per_seq] int32.
+ *   context_lens  [B] int32, positions attended (including the token this
+ *                 step appended).  0 gives an all-zero output row.
+ *   scale         softmax scale (finite), applied to the fp32 dot product.
+ *
+ * All arithmetic is fp32 (fp16 products, fp32 accumulation); the output is
+ * rounded to fp16 (nearest even).  One workgroup serves one (sequence, KV
+ * head) pair, so this call fills the GPU only when B * num_kv_heads is
+ * large; the split call below spreads long contexts over the whole GPU.
+ * B == 0 is a no-op.
+ */
+int paged_attention_decode(void* out, const void* q,
+                           const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables,
+                           const int32_t* context_lens,
+                           int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, int32_t max_blocks_per_seq,
+                           float scale, void* stream);
+
+/*
+ * paged_attention_decode_split -- split-context pass of the flash-decoding
+ * style arm (nanoserve author's post thread, Day 74).  Partition p of
+ * sequence b covers logical positions [p * partition_size,
+ * min((p + 1) * partition_size, context_lens[b])).  For every partition that
+ * holds at least one position:
+ *
+ *   partial_out[b, h, p, :] = softmax-weighted sum of V over the partition
+ *                             (normalised within the partition), fp32;
+ *   partial_lse[b, h, p]    = ln(sum_t exp(scale * q . K_t)) over the
+ *                             partition, fp32.
+ *
+ * For a partition that starts at or past context_lens[b], partial_lse is set
+ * to -inf and partial_out is left untouched.
+ *
+ *   partial_out     [B, num_q_heads, max_partitions, head_dim] fp32 workspace.
+ *   partial_lse     [B, num_q_heads, max_partitions] fp32 workspace.
+ *   partition_size  a multiple of block_size.
+ *   max_partitions  with max_partitions * partition_size >=
+ *                   max_blocks_per_seq * block_size.
+ * Other arguments as for paged_attention_decode.
+ */
+int paged_attention_decode_split(float* partial_out, float* partial_lse,
+                                 const void* q,
+                                 const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables,
+                                 const int32_t* context_lens,
+                                 int32_t B, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq,
+                                 int32_t partition_size, int32_t max_partitions,
+                                 float scale, void* stream);
+
+/*
+ * split_reduce -- merge the partitions written by
+ * paged_attention_decode_split.  With n = ceil(context_lens[b] /
+ * partition_size) valid partitions of (b, h):
+ *
+ *   L          = ln(sum_{p<n} exp(partial_lse[b, h, p]))
+ *   out[b,h,:] = sum_{p<n} exp(partial_lse[b, h, p] - L) partial_out[b,h,p,:]
+ *
+ * which equals the unsplit softmax result exactly in real arithmetic (the
+ * pages name the split arm but not its merge; this log-sum-exp weighting is
+ * the exact one).  context_lens[b] == 0 gives zeros and L = -inf.
+ *
+ *   out       [B, num_q_heads, head_dim] fp16 (written).
+ *   lse_out   [B, num_q_heads] fp32 natural-log LSE of the whole context, or
+ *             NULL.
+ * Other arguments as for paged_attention_decode_split.
+ */
+int split_reduce(void* out, float* lse_out,
+                 const float* partial_out, const float* partial_lse,
+                 const int32_t* context_lens,
+                 int32_t B, int32_t num_q_heads, int32_t head_dim,
+                 int32_t partition_size, int32_t max_partitions, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

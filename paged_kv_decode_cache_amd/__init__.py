@@ -1,0 +1,15 @@
+"""Paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+
+The computation lives in libpkv.so (hand-written HIP kernels behind a C ABI,
+``include/pkv.h``); this package is its thin Python binding.
+"""
+from ._binding import (LIB_PATH, HEADER_PATH, load_library, declared_functions,
+                       status_string, set_launch_config, kv_cache_append,
+                       paged_attention_decode, paged_attention_decode_split,
+                       split_reduce, max_partitions_for,
+                       PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_LAUNCH)
+
+__all__ = ["LIB_PATH", "HEADER_PATH", "load_library", "declared_functions", "status_string",
+           "set_launch_config", "kv_cache_append", "paged_attention_decode",
+           "paged_attention_decode_split", "split_reduce", "max_partitions_for",
+           "PKV_OK", "PKV_ERR_INVALID_ARG", "PKV_ERR_UNSUPPORTED", "PKV_ERR_LAUNCH"]

@@ -1,0 +1,225 @@
+"""ctypes binding of libpkv.so.
+
+Argument marshalling only: shapes, dtypes and devices of torch tensors are
+checked, raw device pointers and the current HIP stream are handed to the C
+ABI, and its status codes become exceptions.  Every step of the computation
+runs in the library's HIP kernels; there is no other implementation to fall
+back to, so a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pkv.h")
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = -1
+PKV_ERR_UNSUPPORTED = -2
+PKV_ERR_LAUNCH = -3
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+
+_SIGNATURES = {
+    "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pkv_version": (ctypes.c_int, []),
+    "pkv_set_launch_config": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "kv_cache_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "paged_attention_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                              _I, _F, _P]),
+    "paged_attention_decode_split": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I,
+                                                    _I, _I, _I, _I, _I, _I, _F, _P]),
+    "split_reduce": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpkv.so (built in-tree) and declare its C signatures."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m paged_kv_decode_cache_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def declared_functions(header: str = HEADER_PATH):
+    """Names of the functions include/pkv.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def status_string(code: int) -> str:
+    return load_library().pkv_status_string(code).decode()
+
+
+def _raise(code: int, what: str):
+    if code == PKV_OK:
+        return
+    msg = f"{what}: {status_string(code)} (status {code})"
+    if code == PKV_ERR_INVALID_ARG:
+        raise ValueError(msg)
+    if code == PKV_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise RuntimeError(msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return ctypes.c_void_p(handle)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def set_launch_config(which: str, waves_per_group: int = 0, subtiles_per_iter: int = 0):
+    """Tuning aid: launch shape of 'decode' or 'split' (0 = library default)."""
+    idx = {"decode": 0, "split": 1}[which]
+    _raise(load_library().pkv_set_launch_config(idx, waves_per_group, subtiles_per_iter),
+           "pkv_set_launch_config")
+
+
+def kv_cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
+    """Write k_new/v_new [N, Hkv, D] into the pools at slot_mapping [N]."""
+    _need(k_pool, "k_pool", torch.float16, 4)
+    dev = k_pool.device
+    _need(v_pool, "v_pool", torch.float16, 4, dev)
+    _need(k_new, "k_new", torch.float16, 3, dev)
+    _need(v_new, "v_new", torch.float16, 3, dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+    NB, bs, Hkv, D = k_pool.shape
+    N = k_new.shape[0]
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    if k_new.shape != (N, Hkv, D) or v_new.shape != (N, Hkv, D) or slot_mapping.shape != (N,):
+        raise ValueError("k_new/v_new must be [N, Hkv, D] and slot_mapping [N]")
+    rc = load_library().kv_cache_append(_ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+                                        _ptr(slot_mapping), N, NB, bs, Hkv, D,
+                                        _stream(dev, stream))
+    _raise(rc, "kv_cache_append")
+
+
+def _attn_shapes(q, k_pool, v_pool, block_tables, context_lens):
+    _need(q, "q", torch.float16, 3)
+    dev = q.device
+    _need(k_pool, "k_pool", torch.float16, 4, dev)
+    _need(v_pool, "v_pool", torch.float16, 4, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    NB, bs, Hkv, D2 = k_pool.shape
+    if v_pool.shape != k_pool.shape or D2 != D:
+        raise ValueError("pools must be [num_blocks, block_size, Hkv, D] with q's D")
+    if block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+    return dev, B, Hq, Hkv, D, bs, NB, block_tables.shape[1]
+
+
+def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, scale,
+                           out=None, stream=None):
+    """out [B, Hq, D] fp16 = paged decode attention (one launch)."""
+    dev, B, Hq, Hkv, D, bs, NB, maxb = _attn_shapes(q, k_pool, v_pool, block_tables,
+                                                    context_lens)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    _need(out, "out", torch.float16, 3, dev)
+    if out.shape != (B, Hq, D):
+        raise ValueError("out must be [B, Hq, D]")
+    rc = load_library().paged_attention_decode(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
+        B, Hq, Hkv, D, bs, NB, maxb, float(scale), _stream(dev, stream))
+    _raise(rc, "paged_attention_decode")
+    return out
+
+
+def max_partitions_for(max_blocks_per_seq: int, block_size: int, partition_size: int) -> int:
+    return -(-max_blocks_per_seq * block_size // partition_size)
+
+
+def paged_attention_decode_split(q, k_pool, v_pool, block_tables, context_lens, scale,
+                                 partition_size, max_partitions=None, partial_out=None,
+                                 partial_lse=None, stream=None):
+    """Split pass; returns (partial_out [B,Hq,P,D] fp32, partial_lse [B,Hq,P] fp32)."""
+    dev, B, Hq, Hkv, D, bs, NB, maxb = _attn_shapes(q, k_pool, v_pool, block_tables,
+                                                    context_lens)
+    if max_partitions is None:
+        max_partitions = max_partitions_for(maxb, bs, partition_size)
+    if partial_out is None:
+        partial_out = torch.empty((B, Hq, max_partitions, D), dtype=torch.float32, device=dev)
+    if partial_lse is None:
+        partial_lse = torch.empty((B, Hq, max_partitions), dtype=torch.float32, device=dev)
+    _need(partial_out, "partial_out", torch.float32, 4, dev)
+    _need(partial_lse, "partial_lse", torch.float32, 3, dev)
+    if partial_out.shape != (B, Hq, max_partitions, D) or \
+            partial_lse.shape != (B, Hq, max_partitions):
+        raise ValueError("partial_out must be [B, Hq, P, D] and partial_lse [B, Hq, P]")
+    rc = load_library().paged_attention_decode_split(
+        _ptr(partial_out), _ptr(partial_lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, bs, NB, maxb,
+        int(partition_size), int(max_partitions), float(scale), _stream(dev, stream))
+    _raise(rc, "paged_attention_decode_split")
+    return partial_out, partial_lse
+
+
+def split_reduce(partial_out, partial_lse, context_lens, partition_size, out=None,
+                 lse_out=None, want_lse=False, stream=None):
+    """Merge partitions; returns out [B, Hq, D] fp16 (and lse [B, Hq] fp32)."""
+    _need(partial_out, "partial_out", torch.float32, 4)
+    dev = partial_out.device
+    _need(partial_lse, "partial_lse", torch.float32, 3, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, Hq, P, D = partial_out.shape
+    if partial_lse.shape != (B, Hq, P) or context_lens.shape != (B,):
+        raise ValueError("partial_lse must be [B, Hq, P] and context_lens [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    _need(out, "out", torch.float16, 3, dev)
+    if want_lse and lse_out is None:
+        lse_out = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, 2, dev)
+        if lse_out.shape != (B, Hq):
+            raise ValueError("lse_out must be [B, Hq]")
+    rc = load_library().split_reduce(_ptr(out), _ptr(lse_out), _ptr(partial_out),
+                                     _ptr(partial_lse), _ptr(context_lens), B, Hq, D,
+                                     int(partition_size), P, _stream(dev, stream))
+    _raise(rc, "split_reduce")
+    return (out, lse_out) if lse_out is not None else out

@@ -1,0 +1,275 @@
+// C ABI of libpkv.so: argument validation (before any HIP call), launch
+// configuration, and launches on the caller's stream.  No allocation, no
+// synchronisation, no device reads on the host.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "pkv.h"
+#include "pkv_kernels.hpp"
+
+namespace {
+
+using pkv::AppendParams;
+using pkv::AttnParams;
+using pkv::ReduceParams;
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+bool block_size_ok(int32_t bs) { return bs >= 16 && bs <= 256 && bs % 16 == 0; }
+
+// Launch shape (waves per workgroup, 16-token subtiles per wave iteration);
+// 0 means "library default".  Settable for tuning through
+// pkv_set_launch_config.
+std::atomic<int> g_cfg_waves[2] = {{0}, {0}};
+std::atomic<int> g_cfg_subtiles[2] = {{0}, {0}};
+
+struct Shape {
+  int waves, subtiles;
+};
+
+Shape pick_shape(int which, int head_dim) {
+  Shape s;
+  // Defaults: the split pass runs one partition per workgroup with 4 waves;
+  // the unsplit pass has one workgroup per (sequence, KV head) and uses 8.
+  s.waves = which == 0 ? 8 : 4;
+  s.subtiles = head_dim == 64 ? 4 : 2;
+  const int w = g_cfg_waves[which].load(std::memory_order_relaxed);
+  const int t = g_cfg_subtiles[which].load(std::memory_order_relaxed);
+  if (w) s.waves = w;
+  if (t) s.subtiles = t;
+  return s;
+}
+
+template <int D, int NS, int NW, bool SPLIT>
+void launch_attn_inst(const AttnParams& p, int64_t grid, hipStream_t st) {
+  hipLaunchKernelGGL((pkv::attn_kernel<D, NS, NW, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                     st, p);
+}
+
+template <int D, bool SPLIT>
+void launch_attn_ns(const AttnParams& p, int64_t grid, Shape s, hipStream_t st) {
+#define PKV_NW_CASES(NS)                                  \
+  switch (s.waves) {                                      \
+    case 1: launch_attn_inst<D, NS, 1, SPLIT>(p, grid, st); break; \
+    case 2: launch_attn_inst<D, NS, 2, SPLIT>(p, grid, st); break; \
+    case 4: launch_attn_inst<D, NS, 4, SPLIT>(p, grid, st); break; \
+    default: launch_attn_inst<D, NS, 8, SPLIT>(p, grid, st); break; \
+  }
+  switch (s.subtiles) {
+    case 1: PKV_NW_CASES(1) break;
+    case 2: PKV_NW_CASES(2) break;
+    default: PKV_NW_CASES(4) break;
+  }
+#undef PKV_NW_CASES
+}
+
+template <bool SPLIT>
+int launch_attn(const AttnParams& p, int head_dim, int64_t grid, hipStream_t st) {
+  const Shape s = pick_shape(SPLIT ? 1 : 0, head_dim);
+  if (head_dim == 64)
+    launch_attn_ns<64, SPLIT>(p, grid, s, st);
+  else
+    launch_attn_ns<128, SPLIT>(p, grid, s, st);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+// Checks shared by both attention passes.  Returns PKV_OK or an error code.
+int check_attn_common(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                      float scale) {
+  if (B < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return PKV_ERR_INVALID_ARG;
+  if (!k_pool || !v_pool || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return PKV_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PKV_ERR_UNSUPPORTED;
+  if (num_q_heads / num_kv_heads > 16) return PKV_ERR_UNSUPPORTED;
+  // positions per sequence must fit in int32
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;  // empty per-sequence arrays may be null
+  if (!q || !block_tables || !context_lens) return PKV_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PKV_ERR_INVALID_ARG;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape";
+    case PKV_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pkv_version(void) { return kVersion; }
+
+int pkv_set_launch_config(int which, int waves_per_group, int subtiles_per_iter) {
+  if (which != 0 && which != 1) return PKV_ERR_INVALID_ARG;
+  if (waves_per_group != 0 && waves_per_group != 1 && waves_per_group != 2 &&
+      waves_per_group != 4 && waves_per_group != 8)
+    return PKV_ERR_INVALID_ARG;
+  if (subtiles_per_iter != 0 && subtiles_per_iter != 1 && subtiles_per_iter != 2 &&
+      subtiles_per_iter != 4)
+    return PKV_ERR_INVALID_ARG;
+  g_cfg_waves[which].store(waves_per_group, std::memory_order_relaxed);
+  g_cfg_subtiles[which].store(subtiles_per_iter, std::memory_order_relaxed);
+  return PKV_OK;
+}
+
+int kv_cache_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                    const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                    int32_t block_size, int32_t num_kv_heads, int32_t head_dim, void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!k_pool || !v_pool || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return PKV_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;  // empty per-token arrays may be null
+  if (!k_new || !v_new || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slot_mapping, 8))
+    return PKV_ERR_INVALID_ARG;
+
+  AppendParams p;
+  p.k_pool = static_cast<pkv::f16*>(k_pool);
+  p.v_pool = static_cast<pkv::f16*>(v_pool);
+  p.k_new = static_cast<const pkv::f16*>(k_new);
+  p.v_new = static_cast<const pkv::f16*>(v_new);
+  p.slot_mapping = slot_mapping;
+  p.num_slots = (int64_t)num_blocks * block_size;
+  p.num_tokens = num_tokens;
+  p.Hkv = num_kv_heads;
+  p.D = head_dim;
+  const int64_t threads = (int64_t)num_tokens * num_kv_heads * (head_dim / 8);
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(pkv::append_kernel, dim3((unsigned)grid), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), p);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                           float scale, void* stream) {
+  int rc = check_attn_common(q, k_pool, v_pool, block_tables, context_lens, B, num_q_heads,
+                             num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                             scale);
+  if (rc != PKV_OK) return rc;
+  if (B == 0) return PKV_OK;
+  if (!out || !aligned(out, 16)) return PKV_ERR_INVALID_ARG;
+  const int64_t grid = (int64_t)B * num_kv_heads;
+  if (grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
+
+  AttnParams p = {};
+  p.q = static_cast<const pkv::f16*>(q);
+  p.k_pool = static_cast<const pkv::f16*>(k_pool);
+  p.v_pool = static_cast<const pkv::f16*>(v_pool);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = static_cast<pkv::f16*>(out);
+  p.Hq = num_q_heads;
+  p.Hkv = num_kv_heads;
+  p.G = num_q_heads / num_kv_heads;
+  p.block_size = block_size;
+  p.num_blocks = num_blocks;
+  p.max_blocks = max_blocks_per_seq;
+  p.partition_size = max_blocks_per_seq * block_size;
+  p.max_partitions = 1;
+  p.scale_log2 = scale * pkv::kLog2e;
+  return launch_attn<false>(p, head_dim, grid, static_cast<hipStream_t>(stream));
+}
+
+int paged_attention_decode_split(float* partial_out, float* partial_lse, const void* q,
+                                 const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t partition_size,
+                                 int32_t max_partitions, float scale, void* stream) {
+  int rc = check_attn_common(q, k_pool, v_pool, block_tables, context_lens, B, num_q_heads,
+                             num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                             scale);
+  if (rc != PKV_OK) return rc;
+  if (partition_size <= 0 || max_partitions <= 0 || partition_size % block_size != 0)
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_partitions * partition_size < (int64_t)max_blocks_per_seq * block_size)
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_partitions * partition_size > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  if (!partial_out || !partial_lse || !aligned(partial_out, 16) || !aligned(partial_lse, 4))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t grid = (int64_t)B * num_kv_heads * max_partitions;
+  if (grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
+
+  AttnParams p = {};
+  p.q = static_cast<const pkv::f16*>(q);
+  p.k_pool = static_cast<const pkv::f16*>(k_pool);
+  p.v_pool = static_cast<const pkv::f16*>(v_pool);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.partial_out = partial_out;
+  p.partial_lse = partial_lse;
+  p.Hq = num_q_heads;
+  p.Hkv = num_kv_heads;
+  p.G = num_q_heads / num_kv_heads;
+  p.block_size = block_size;
+  p.num_blocks = num_blocks;
+  p.max_blocks = max_blocks_per_seq;
+  p.partition_size = partition_size;
+  p.max_partitions = max_partitions;
+  p.scale_log2 = scale * pkv::kLog2e;
+  return launch_attn<true>(p, head_dim, grid, static_cast<hipStream_t>(stream));
+}
+
+int split_reduce(void* out, float* lse_out, const float* partial_out, const float* partial_lse,
+                 const int32_t* context_lens, int32_t B, int32_t num_q_heads, int32_t head_dim,
+                 int32_t partition_size, int32_t max_partitions, void* stream) {
+  if (B < 0 || num_q_heads <= 0 || partition_size <= 0 || max_partitions <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_partitions * partition_size > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (B == 0) return PKV_OK;
+  if (!out || !partial_out || !partial_lse || !context_lens) return PKV_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(partial_out, 16) || !aligned(partial_lse, 4) ||
+      !aligned(context_lens, 4) || (lse_out && !aligned(lse_out, 4)))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t grid = (int64_t)B * num_q_heads;
+  if (grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
+
+  ReduceParams p;
+  p.out = static_cast<pkv::f16*>(out);
+  p.lse_out = lse_out;
+  p.partial_out = partial_out;
+  p.partial_lse = partial_lse;
+  p.context_lens = context_lens;
+  p.Hq = num_q_heads;
+  p.partition_size = partition_size;
+  p.max_partitions = max_partitions;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (head_dim == 64)
+    hipLaunchKernelGGL(pkv::split_reduce_kernel<64>, dim3((unsigned)grid), dim3(64), 0, st, p);
+  else
+    hipLaunchKernelGGL(pkv::split_reduce_kernel<128>, dim3((unsigned)grid), dim3(64), 0, st, p);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,199 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/pkv.h declares, and rejects invalid arguments with the documented
+status before any HIP call (so nothing is launched)."""
+import ctypes
+import math
+
+import pytest
+import torch
+
+import paged_kv_decode_cache_amd as pkv
+
+# Raw-pointer validation calls must never reach a launch on a real device; they
+# are host-only checks, so they run only where no GPU is visible.
+host_only = pytest.mark.skipif(torch.cuda.is_available(),
+                               reason="raw-pointer validation checks run without a GPU")
+
+A16 = 0x10000          # fake, 16-byte aligned "device" addresses (never dereferenced)
+B16 = 0x20000
+C16 = 0x30000
+D16 = 0x40000
+E16 = 0x50000
+F16 = 0x60000
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pkv.load_library()
+    names = pkv.declared_functions()
+    for expected in ("kv_cache_append", "paged_attention_decode",
+                     "paged_attention_decode_split", "split_reduce", "pkv_status_string"):
+        assert expected in names
+    for name in names:
+        assert hasattr(lib, name), f"libpkv.so does not export {name}"
+
+
+def test_status_strings_and_version():
+    lib = pkv.load_library()
+    assert pkv.status_string(0) == "ok"
+    assert "invalid" in pkv.status_string(-1)
+    assert "unsupported" in pkv.status_string(-2)
+    assert "launch" in pkv.status_string(-3)
+    assert pkv.status_string(7) == "unknown status"
+    assert lib.pkv_version() >= 100
+
+
+def test_launch_config_validation():
+    lib = pkv.load_library()
+    assert lib.pkv_set_launch_config(2, 4, 4) == -1
+    assert lib.pkv_set_launch_config(0, 3, 4) == -1
+    assert lib.pkv_set_launch_config(1, 4, 3) == -1
+    assert lib.pkv_set_launch_config(0, 0, 0) == 0
+    assert lib.pkv_set_launch_config(1, 0, 0) == 0
+
+
+def _decode(lib, **kw):
+    a = dict(out=A16, q=B16, k=C16, v=D16, bt=E16, ctx=F16, B=2, Hq=14, Hkv=2, D=64, bs=16,
+             NB=10, maxb=4, scale=0.125)
+    a.update(kw)
+    return lib.paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["ctx"], a["B"],
+                                      a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["maxb"],
+                                      a["scale"], None)
+
+
+DECODE_BAD = [
+    ("null out", dict(out=None), -1),
+    ("null q", dict(q=None), -1),
+    ("null pool", dict(k=None), -1),
+    ("null table", dict(bt=None), -1),
+    ("misaligned q", dict(q=B16 + 2), -1),
+    ("misaligned out", dict(out=A16 + 8), -1),
+    ("misaligned table", dict(bt=E16 + 2), -1),
+    ("negative batch", dict(B=-1), -1),
+    ("zero heads", dict(Hq=0), -1),
+    ("group not integral", dict(Hq=15), -1),
+    ("zero blocks", dict(NB=0), -1),
+    ("zero table width", dict(maxb=0), -1),
+    ("nan scale", dict(scale=math.nan), -1),
+    ("inf scale", dict(scale=math.inf), -1),
+    ("head dim 96", dict(D=96), -2),
+    ("head dim 256", dict(D=256), -2),
+    ("block size 8", dict(bs=8), -2),
+    ("block size 24", dict(bs=24), -2),
+    ("block size 512", dict(bs=512), -2),
+    ("group of 32", dict(Hq=64, Hkv=2), -2),
+]
+
+
+@host_only
+@pytest.mark.parametrize("name,kw,code", DECODE_BAD, ids=[d[0] for d in DECODE_BAD])
+def test_decode_rejects(name, kw, code):
+    assert _decode(pkv.load_library(), **kw) == code
+
+
+@host_only
+def test_decode_batch0_is_noop():
+    assert _decode(pkv.load_library(), B=0) == 0
+
+
+def _split(lib, **kw):
+    a = dict(po=A16, pl=B16, q=C16, k=D16, v=E16, bt=F16, ctx=F16 + 0x1000, B=2, Hq=14, Hkv=2,
+             D=64, bs=16, NB=10, maxb=4, P=32, Pm=2, scale=0.125)
+    a.update(kw)
+    return lib.paged_attention_decode_split(a["po"], a["pl"], a["q"], a["k"], a["v"], a["bt"],
+                                            a["ctx"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                                            a["NB"], a["maxb"], a["P"], a["Pm"], a["scale"], None)
+
+
+SPLIT_BAD = [
+    ("null partial_out", dict(po=None), -1),
+    ("null partial_lse", dict(pl=None), -1),
+    ("misaligned partial_out", dict(po=A16 + 4), -1),
+    ("partition not multiple of block", dict(P=24), -1),
+    ("zero partition", dict(P=0), -1),
+    ("too few partitions", dict(Pm=1), -1),
+    ("zero partitions", dict(Pm=0), -1),
+    ("head dim 80", dict(D=80), -2),
+]
+
+
+@host_only
+@pytest.mark.parametrize("name,kw,code", SPLIT_BAD, ids=[d[0] for d in SPLIT_BAD])
+def test_split_rejects(name, kw, code):
+    assert _split(pkv.load_library(), **kw) == code
+
+
+@host_only
+def test_split_batch0_is_noop():
+    assert _split(pkv.load_library(), B=0) == 0
+
+
+def _reduce(lib, **kw):
+    a = dict(out=A16, lse=B16, po=C16, pl=D16, ctx=E16, B=2, Hq=14, D=64, P=32, Pm=2)
+    a.update(kw)
+    return lib.split_reduce(a["out"], a["lse"], a["po"], a["pl"], a["ctx"], a["B"], a["Hq"],
+                            a["D"], a["P"], a["Pm"], None)
+
+
+REDUCE_BAD = [
+    ("null out", dict(out=None), -1),
+    ("null partials", dict(po=None), -1),
+    ("null ctx", dict(ctx=None), -1),
+    ("misaligned lse_out", dict(lse=B16 + 2), -1),
+    ("zero partition", dict(P=0), -1),
+    ("negative batch", dict(B=-3), -1),
+    ("head dim 32", dict(D=32), -2),
+]
+
+
+@host_only
+@pytest.mark.parametrize("name,kw,code", REDUCE_BAD, ids=[d[0] for d in REDUCE_BAD])
+def test_reduce_rejects(name, kw, code):
+    assert _reduce(pkv.load_library(), **kw) == code
+
+
+def _append(lib, **kw):
+    a = dict(k=A16, v=B16, kn=C16, vn=D16, slots=E16, N=3, NB=10, bs=16, Hkv=2, D=64)
+    a.update(kw)
+    return lib.kv_cache_append(a["k"], a["v"], a["kn"], a["vn"], a["slots"], a["N"], a["NB"],
+                               a["bs"], a["Hkv"], a["D"], None)
+
+
+APPEND_BAD = [
+    ("null pool", dict(k=None), -1),
+    ("null slots", dict(slots=None), -1),
+    ("misaligned k_new", dict(kn=C16 + 2), -1),
+    ("misaligned slots", dict(slots=E16 + 4), -1),
+    ("negative tokens", dict(N=-1), -1),
+    ("zero heads", dict(Hkv=0), -1),
+    ("head dim 48", dict(D=48), -2),
+    ("block size 20", dict(bs=20), -2),
+]
+
+
+@host_only
+@pytest.mark.parametrize("name,kw,code", APPEND_BAD, ids=[d[0] for d in APPEND_BAD])
+def test_append_rejects(name, kw, code):
+    assert _append(pkv.load_library(), **kw) == code
+
+
+@host_only
+def test_append_zero_tokens_is_noop():
+    assert _append(pkv.load_library(), N=0) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    q = torch.zeros((1, 2, 64), dtype=torch.float16)
+    kp = torch.zeros((2, 16, 1, 64), dtype=torch.float16)
+    bt = torch.zeros((1, 1), dtype=torch.int32)
+    ctx = torch.ones(1, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pkv.paged_attention_decode(q, kp, kp, bt, ctx, 0.125)
+
+
+def test_binding_rejects_wrong_dtype():
+    q = torch.zeros((1, 2, 64), dtype=torch.float32)
+    kp = torch.zeros((2, 16, 1, 64), dtype=torch.float16)
+    bt = torch.zeros((1, 1), dtype=torch.int32)
+    ctx = torch.ones(1, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        pkv.paged_attention_decode(q, kp, kp, bt, ctx, 0.125)

@@ -1,0 +1,134 @@
+"""paged_attention_decode_split + split_reduce on the GPU against the oracle
+(partials and merged output), and against the unsplit kernel."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_decode_cache_amd as pkv
+import workloads
+from oracle import paged_ref as ref
+from gpu_common import (PARTIAL_ATOL, case, check_fp16, host64, needs_gpu, oracle_decode,
+                        sample_rows, say, to_gpu)
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _split_reduce(g, c, P, Pm=None):
+    po, pl = pkv.paged_attention_decode_split(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale,
+                                              P, max_partitions=Pm)
+    out, lse = pkv.split_reduce(po, pl, g.ctx, P, want_lse=True)
+    return po, pl, out, lse
+
+
+def _check_lse(got, want, label, rows=None):
+    g = host64(got)
+    w = np.asarray(want, dtype=np.float64)
+    if rows is not None:
+        g, w = g[rows], w[rows]
+    fin = np.isfinite(w)
+    assert np.array_equal(np.isneginf(g), np.isneginf(w)), f"{label}: -inf pattern differs"
+    if fin.any():
+        err = float(np.abs(g[fin] - w[fin]).max())
+        assert err <= PARTIAL_ATOL, f"{label}: lse err {err:.3e}"
+
+
+LONG = [f"long:{B}:{ctx}" for B, ctx in workloads.LONG_POINTS]
+
+
+@pytest.mark.parametrize("name", LONG)
+def test_long_context_split_matches_oracle_and_unsplit(name):
+    c = case(name)
+    P = 512
+    say(f"split {name}: P={P}")
+    g = to_gpu(c)
+    po, pl, out, lse = _split_reduce(g, c, P)
+    unsplit = pkv.paged_attention_decode(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale)
+    torch.cuda.synchronize()
+    want, want_lse = oracle_decode(c)
+    check_fp16(out, want, name + " split")
+    _check_lse(lse, want_lse, name)
+    d = (out.float() - unsplit.float()).abs().max().item()
+    assert d <= 2e-3, f"split vs unsplit differ by {d}"
+
+
+@pytest.mark.parametrize("name,P", [("tiny", 16), ("qwen", 512), ("qwen", 64),
+                                    ("sweep:32:4096", 256), ("sweep:1:128", 512),
+                                    ("sweep:8:1024", 16)])
+def test_split_partials_match_oracle(name, P):
+    c = case(name)
+    say(f"split partials {name}: P={P}")
+    g = to_gpu(c)
+    Pm = c.max_partitions(P)
+    po, pl, out, lse = _split_reduce(g, c, P, Pm)
+    torch.cuda.synchronize()
+    wpo, wpl = ref.paged_attention_decode_split(c.q, c.k_pool, c.v_pool, c.block_tables,
+                                                c.context_lens, c.scale, P, Pm)
+    gpl = host64(pl)
+    gpo = host64(po)
+    assert np.array_equal(np.isneginf(gpl), np.isneginf(wpl))
+    valid = np.isfinite(wpl)
+    assert float(np.abs(gpl[valid] - wpl[valid]).max()) <= PARTIAL_ATOL
+    assert float(np.abs(gpo[valid] - wpo[valid]).max()) <= PARTIAL_ATOL
+    want, want_lse = oracle_decode(c)
+    check_fp16(out, want, f"{name} P={P}")
+    _check_lse(lse, want_lse, name)
+
+
+def test_skewed_split_sampled():
+    c = case("skewed")
+    P = 512
+    rows = sample_rows(c, k=16)
+    say(f"split skewed P={P} rows {rows}")
+    g = to_gpu(c)
+    po, pl, out, lse = _split_reduce(g, c, P)
+    torch.cuda.synchronize()
+    want, want_lse = oracle_decode(c, seqs=rows)
+    check_fp16(out, want, "skewed split", rows=rows)
+    _check_lse(lse, want_lse, "skewed", rows=rows)
+
+
+def test_partition_larger_than_context_and_spare_partitions():
+    c = workloads.custom_case("spare", B=4, Hq=14, Hkv=2, D=64, block_size=32,
+                              lens=[1, 31, 32, 600], seed=98, q_mult=4.0)
+    g = to_gpu(c)
+    for P, extra in ((1024, 0), (1024, 3), (32, 5), (64, 1)):
+        Pm = c.max_partitions(P) + extra
+        po, pl, out, lse = _split_reduce(g, c, P, Pm)
+        torch.cuda.synchronize()
+        want, want_lse = oracle_decode(c)
+        check_fp16(out, want, f"spare P={P}+{extra}")
+        _check_lse(lse, want_lse, f"spare P={P}")
+        gpl = host64(pl)
+        for b, n in enumerate(c.context_lens):
+            used = -(-int(n) // P)
+            assert np.all(np.isfinite(gpl[b, :, :used]))
+            assert np.all(np.isneginf(gpl[b, :, used:]))
+
+
+def test_split_ctx0():
+    c = workloads.custom_case("sctx0", B=2, Hq=4, Hkv=1, D=128, block_size=16, lens=[0, 40],
+                              seed=99)
+    g = to_gpu(c)
+    po, pl, out, lse = _split_reduce(g, c, 32)
+    torch.cuda.synchronize()
+    assert int((out[0] != 0).sum()) == 0
+    assert torch.isneginf(lse[0]).all()
+    want, want_lse = oracle_decode(c)
+    check_fp16(out, want, "split ctx0")
+    _check_lse(lse, want_lse, "split ctx0")
+
+
+@pytest.mark.parametrize("waves", [1, 2, 4, 8])
+@pytest.mark.parametrize("subtiles", [1, 2, 4])
+def test_split_every_launch_shape(waves, subtiles):
+    try:
+        pkv.set_launch_config("split", waves, subtiles)
+        c = case("qwen")
+        g = to_gpu(c)
+        po, pl, out, lse = _split_reduce(g, c, 256)
+        torch.cuda.synchronize()
+        want, want_lse = oracle_decode(c)
+        check_fp16(out, want, f"split NW={waves} NS={subtiles}")
+        _check_lse(lse, want_lse, "split shapes")
+    finally:
+        pkv.set_launch_config("split", 0, 0)

@@ -7,8 +7,13 @@ attention arithmetic; the oracle and the HIP path both consume what it returns.
 Recipe ("Input recipe"):
 * ``numpy.random.default_rng(seed)`` (PCG64).  Draw order: lengths, block
   tables, K pool, V pool, q, k_new, v_new.
-* Values: ``standard_normal(float32)`` rounded to fp16 (round to nearest
-  even); q of the long-context workload is then multiplied by 4 (exact).
+* Values are N(0,1) in fp16, drawn by inverse-CDF sampling: each raw 64-bit
+  PCG64 word gives four 16-bit indices i, and i maps to the standard normal
+  quantile at probability (i + 1/2) / 65536, rounded to fp16 (nearest even).
+  (Drawing fp32 normals and converting them is ~20x slower on the host and
+  the 1 GB pools of the skewed workload made that the bottleneck of the
+  tests.)  The tails are cut at |x| = 4.33, which changes nothing the tests
+  rely on.  q of the long-context workload is then multiplied by 4 (exact).
 * Block tables: ``rng.permutation(num_blocks)``; each sequence in turn takes
   the next ceil(ctx / block_size) ids; unused table entries are -1.
 * Pool slots that no sequence attends (the tail of each last block, and
@@ -20,6 +25,7 @@ Recipe ("Input recipe"):
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -71,13 +77,43 @@ class DecodeCase:
         return self.B * self.Hq * self.D * 2 * 2
 
 
-def _normal16(rng: np.random.Generator, shape, chunk: int = 1 << 26) -> np.ndarray:
-    """N(0,1) drawn in float32 and rounded to fp16, in bounded chunks."""
+_QUANTILES16 = None
+
+
+def _quantile_table() -> np.ndarray:
+    global _QUANTILES16
+    if _QUANTILES16 is None:
+        import scipy.special
+        probs = (np.arange(65536, dtype=np.float64) + 0.5) / 65536.0
+        _QUANTILES16 = scipy.special.ndtri(probs).astype(np.float16)
+    return _QUANTILES16
+
+
+_POOL = None
+
+
+def _normal16(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
+    """N(0,1) fp16 values by inverse-CDF lookup of raw 16-bit draws.  The raw
+    words are drawn in order from the one stream; the lookups of large arrays
+    run on a few threads (the result does not depend on the thread count)."""
+    global _POOL
     n = int(np.prod(shape))
+    table = _quantile_table()
     out = np.empty(n, dtype=np.float16)
+    if n <= chunk:
+        idx = rng.bit_generator.random_raw((n + 3) // 4).view(np.uint16)[:n]
+        out[:] = table[idx]
+        return out.reshape(shape)
+    if _POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max(1, min(8, len(os.sched_getaffinity(0)))))
+    futs = []
     for lo in range(0, n, chunk):
         hi = min(n, lo + chunk)
-        out[lo:hi] = rng.standard_normal(hi - lo, dtype=np.float32).astype(np.float16)
+        idx = rng.bit_generator.random_raw((hi - lo + 3) // 4).view(np.uint16)[: hi - lo]
+        futs.append(_POOL.submit(np.take, table, idx, 0, out[lo:hi]))
+    for f in futs:
+        f.result()
     return out.reshape(shape)
 
 
