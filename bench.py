@@ -1,0 +1,472 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache decode path on one MI355X.
+
+One step is the whole hot path over one batch: kv_cache_append of the batch's
+new tokens, the split-context attention pass (paged_attention_decode_split),
+and the LSE merge (split_reduce).  The default workload is the batch x context
+sweep point B=32, ctx=4096 (Hq=14, Hkv=2, D=64, block_size=16, fp16).
+
+Timing protocol
+  * R rotation sets: disjoint block ranges of one large pool, each with its own
+    block tables and new tokens, R chosen so the K/V bytes of all sets exceed
+    4x the 256 MB Infinity Cache; step i uses set i % R, so every call reads
+    its K/V from HBM.
+  * W untimed warm-up steps and at least 200 ms of warm-up (clock ramp).
+  * R consecutive steps (one per set) are captured in one HIP graph and
+    replayed until K steps have run; HIP events on the replay stream bracket
+    the timed replays (after torch.cuda.synchronize()).  The split pass alone
+    is timed the same way (R back-to-back launches per replay) for the
+    roofline figure.  Eager (per-call Python) timings are reported beside.
+  * A streaming-read probe over the same bytes per launch gives the
+    achievable read bandwidth.
+  * The fp64 oracle runs on a bounded sample of the same workload on the host
+    (one thread) for the CPU baseline.
+
+Prints one JSON line.  --sweep writes per-point lines for the whole
+batch x context sweep (unsplit and split) to a file instead.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and µs/call vs B×ctx"
+PEAK_GBS = 8000.0
+LLC_BYTES = 256 * 2**20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--batch", type=int, default=32)
+    ap.add_argument("--ctx", type=int, default=4096)
+    ap.add_argument("--partition", type=int, default=512, help="split partition size (tokens)")
+    ap.add_argument("--waves", type=int, default=0, help="split pass waves/workgroup (0=default)")
+    ap.add_argument("--subtiles", type=int, default=0, help="split pass subtiles/iter (0=default)")
+    ap.add_argument("--sets", type=int, default=0, help="rotation sets (0 = auto, >= 4x LLC)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--sweep", default="", help="write the full sweep as JSON lines to this file")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run 20 plain device copies of MIB MiB (a known-size "
+                         "reference for HBM traffic counters)")
+    return ap.parse_args()
+
+
+def alg_bytes(B, ctx_sum, Hq, Hkv, D):
+    """K and V of the attended positions + q read + out written (fp16)."""
+    return ctx_sum * Hkv * D * 2 * 2 + B * Hq * D * 2 * 2
+
+
+def split_kernel_bytes(B, ctx_sum, Hq, Hkv, D):
+    """Algorithmic bytes of the split pass alone: K/V of the attended
+    positions and q (its partials are workspace, not counted)."""
+    return ctx_sum * Hkv * D * 2 * 2 + B * Hq * D * 2
+
+
+def append_bytes(N, Hkv, D):
+    return 2 * (2 * N * Hkv * D * 2) + 8 * N
+
+
+class Rotation:
+    """R disjoint copies of one generated batch inside one large pool."""
+
+    def __init__(self, case, R, device):
+        import torch
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        NB = case.num_blocks
+        self.R = R
+        shape = (R * NB,) + case.k_pool.shape[1:]
+        self.k_pool = torch.empty(shape, dtype=torch.float16, device=device)
+        self.v_pool = torch.empty(shape, dtype=torch.float16, device=device)
+        k0, v0 = t(case.k_pool), t(case.v_pool)
+        for r in range(R):
+            self.k_pool[r * NB:(r + 1) * NB].copy_(k0)
+            self.v_pool[r * NB:(r + 1) * NB].copy_(v0)
+        del k0, v0
+        bt0 = case.block_tables.astype(np.int64)
+        self.bt = [t(np.where(bt0 >= 0, bt0 + r * NB, -1).astype(np.int32)) for r in range(R)]
+        s0 = case.slot_mapping
+        self.slots = [t(np.where(s0 >= 0, s0 + r * NB * case.block_size, -1)) for r in range(R)]
+        self.q = t(case.q)
+        self.ctx = t(case.context_lens)
+        self.k_new = t(case.k_new)
+        self.v_new = t(case.v_new)
+
+
+def time_cpu_oracle(case, seconds):
+    """fp64 oracle on a bounded sample of the batch; returns (GB/s, sample)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import paged_ref as ref
+    nseq = max(1, min(case.B, 4))
+    seqs = list(range(nseq))
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            ref.paged_attention_decode(case.q, case.k_pool, case.v_pool, case.block_tables,
+                                       case.context_lens, case.scale, seqs=seqs)
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    dt = time.perf_counter() - t0
+    ctx_sample = int(case.context_lens[:nseq].astype(np.int64).sum())
+    sample_bytes = alg_bytes(nseq, ctx_sample, case.Hq, case.Hkv, case.D)
+    gbs = sample_bytes * done / dt / 1e9
+    sample = (f"oracle paged_attention_decode on {nseq} of {case.B} sequences "
+              f"({ctx_sample} positions, all {case.Hkv} KV heads) x {done} repeats in "
+              f"{dt:.1f} s, fp64, one thread; rate scaled by algorithmic bytes")
+    return gbs, sample
+
+
+def capture(fns):
+    """One HIP graph holding the launches of fns, in order."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, per_replay, K):
+    """Average µs per captured unit over >= K units of graph replays."""
+    import torch
+    reps = max(3, math.ceil(K / per_replay))
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * per_replay)
+
+
+def probe_read_gbs(rot, nbytes, R, K):
+    """Streaming-read probe over the same byte count per launch, rotating
+    through the K/V pool (so reads are cold like the kernel's); best grid."""
+    import ctypes
+    import torch
+    lib_path = os.path.join(ROOT, "paged_kv_decode_cache_amd", "libpkv_probe.so")
+    if not os.path.exists(lib_path):
+        return None
+    lib = ctypes.CDLL(lib_path)
+    lib.pkv_probe_stream_read.restype = ctypes.c_int
+    lib.pkv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_void_p]
+    flat = rot.k_pool.view(-1)
+    total = flat.numel() * 2
+    per = (min(nbytes, total) // 16) * 16     # never past the end of the pool
+    sink = torch.zeros(4, dtype=torch.int32, device=flat.device)
+    best = 0.0
+    for grid in (1024, 2048, 4096, 8192):
+        def launch(r, grid=grid):
+            off = (r * per) % (total - per) if total > per else 0
+            off -= off % 16
+            assert off + per <= total
+            st = torch.cuda.current_stream().cuda_stream
+            rc = lib.pkv_probe_stream_read(ctypes.c_void_p(flat.data_ptr() + off), per,
+                                           ctypes.c_void_p(sink.data_ptr()), grid,
+                                           ctypes.c_void_p(st))
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed: {rc}")
+        g = capture([lambda r=r: launch(r) for r in range(R)])
+        us = time_graph(g, R, K)
+        best = max(best, per / (us * 1e-6) / 1e9)
+    return best
+
+
+KERNEL_SOURCES = ("paged_kv_decode_cache_amd/csrc/pkv_kernels.hpp",
+                  "paged_kv_decode_cache_amd/csrc/pkv_api.hip")
+TRAFFIC_PROFILE = "profiles/hbm_traffic_attn_split__sweep_B32_ctx4096.md"
+
+
+def profiled_traffic(kernel_name):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources for this kernel; else None."""
+    import hashlib
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith(("|", "#", "-", "`")):
+            k, v = line.strip().split("=", 1)
+            kv[k] = v
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    if kv.get("kernel_sources_sha256") != h.hexdigest() or kv.get("kernel") != kernel_name:
+        return None
+    return int(kv["traffic_bytes"])
+
+
+def run_headline(args):
+    import torch
+    import paged_kv_decode_cache_amd as pkv
+    import workloads
+
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=device).random_()
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    B, ctx = args.batch, args.ctx
+    if B in workloads.SWEEP_B and ctx in workloads.SWEEP_CTX:
+        case = workloads.sweep_case(B, ctx)
+    else:
+        case = workloads.sweep_case(B, ctx, seed=3999)
+    P = args.partition
+    kv_set = case.kv_bytes()
+    R = args.sets or max(2, math.ceil(4 * LLC_BYTES / kv_set))
+    rot = Rotation(case, R, device)
+    Pm = case.max_partitions(P)
+    po = torch.empty((B, case.Hq, Pm, case.D), dtype=torch.float32, device=device)
+    pl = torch.empty((B, case.Hq, Pm), dtype=torch.float32, device=device)
+    out = torch.empty((B, case.Hq, case.D), dtype=torch.float16, device=device)
+    if args.waves or args.subtiles:
+        pkv.set_launch_config("split", args.waves, args.subtiles)
+    stream = torch.cuda.current_stream(device)
+
+    def step(i, ev=None):
+        r = i % R
+        pkv.kv_cache_append(rot.k_pool, rot.v_pool, rot.k_new, rot.v_new, rot.slots[r])
+        if ev is not None:
+            ev[0].record(stream)
+        split_pass(i)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.split_reduce(po, pl, rot.ctx, P, out=out)
+
+    def split_pass(i):
+        pkv.paged_attention_decode_split(rot.q, rot.k_pool, rot.v_pool, rot.bt[i % R], rot.ctx,
+                                         case.scale, P, Pm, po, pl)
+
+    # warm-up: W steps and at least 200 ms
+    t0 = time.perf_counter()
+    i = 0
+    while i < args.warmup or time.perf_counter() - t0 < 0.2:
+        step(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    K = args.steps
+
+    # Graph-launched steps: R consecutive steps (one per rotation set) are
+    # captured once and replayed; HIP events on the replay stream bracket the
+    # timed replays.  This is the timing of record (no host launch overhead).
+    g_step = capture([lambda r=r: step(r) for r in range(R)])
+    step_us = time_graph(g_step, R, K)
+    g_kern = capture([lambda r=r: split_pass(r) for r in range(R)])
+    kern_us = time_graph(g_kern, R, K)
+
+    # Eager launches (Python binding per call), for context.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    eager_step_us = (time.perf_counter() - t0) * 1e6 / K
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    eager_kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
+
+    # Unsplit decode on the same rotation, graph-launched.
+    g_uns = capture([lambda r=r: pkv.paged_attention_decode(
+        rot.q, rot.k_pool, rot.v_pool, rot.bt[r], rot.ctx, case.scale, out=out)
+        for r in range(R)])
+    unsplit_us = time_graph(g_uns, R, K)
+    if args.waves or args.subtiles:
+        pkv.set_launch_config("split", 0, 0)
+    probe = probe_read_gbs(rot, case.kv_bytes(), R, K)
+    ms_per_step = step_us * 1e-3
+
+    ctx_sum = int(case.context_lens.astype(np.int64).sum())
+    step_bytes = alg_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
+    kbytes = split_kernel_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
+    ns = args.subtiles or (2 if case.D == 64 else 1)
+    nw = args.waves or 4
+    dual = "true" if case.Hq // case.Hkv <= 8 else "false"
+    kname = f"void pkv::attn_kernel<{case.D}, {ns}, {nw}, true, {dual}>(pkv::AttnParams)"
+    traffic = profiled_traffic(kname) if (B, ctx, P) == (32, 4096, 512) else None
+    achieved = kbytes / (kern_us * 1e-6) / 1e9
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    kern_p = np.percentile(eager_kern_ms * 1e3, [10, 50, 90])
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"batch x context sweep point B={B} ctx={ctx} (Hq={case.Hq}, "
+                        f"Hkv={case.Hkv}, D={case.D}, block_size={case.block_size})",
+            "B": B, "ctx": ctx, "Hq": case.Hq, "Hkv": case.Hkv, "D": case.D,
+            "block_size": case.block_size, "partition_size": P, "max_partitions": Pm,
+            "step": "kv_cache_append + paged_attention_decode_split + split_reduce",
+            "rotation_sets": R, "kv_bytes_all_sets": kv_set * R,
+            "launch": "HIP graph of R consecutive steps, replayed",
+            "algorithmic_bytes_per_step": step_bytes,
+            "append_bytes_per_step": append_bytes(B, case.Hkv, case.D),
+            "accumulate": "fp32",
+        },
+        "pct_of_peak": round(100 * value / PEAK_GBS, 2),
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kname,
+            "achieved": round(achieved, 1),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBS, 4),
+            "traffic": traffic,
+            "traffic_source": TRAFFIC_PROFILE if traffic else None,
+            "kernel_us": round(kern_us, 3),
+            "kernel_timing": "HIP events around graph replays of R back-to-back launches",
+            "eager_kernel_us_p10_p50_p90": [round(float(x), 3) for x in kern_p],
+            "algorithmic_bytes_per_launch": kbytes,
+            "probe_read_gbs": round(probe, 1),
+            "frac_of_probe": round(achieved / probe, 4) if probe else None,
+        },
+        "eager_us_per_step": round(eager_step_us, 3),
+        "unsplit_decode_us": round(unsplit_us, 3),
+        "unsplit_decode_gbs": round(step_bytes / (unsplit_us * 1e-6) / 1e9, 1),
+    }
+    if not args.no_cpu:
+        gbs, sample = time_cpu_oracle(case, args.cpu_seconds)
+        res["cpu_baseline"] = {"value": round(gbs, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "sample": sample}
+    return res
+
+
+def run_sweep(args):
+    """Every batch x context point plus the other workloads: unsplit and split
+    timings (rotated over >= 4x LLC of K/V), one JSON line per point."""
+    import torch
+    import paged_kv_decode_cache_amd as pkv
+    import workloads
+
+    device = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(device)
+    points = [("sweep", B, c) for B in workloads.SWEEP_B for c in workloads.SWEEP_CTX]
+    points += [("qwen", 8, 0), ("skewed", 256, 0)]
+    points += [("long", B, c) for B, c in workloads.LONG_POINTS]
+    lines = []
+    for kind, B, c in points:
+        case = (workloads.sweep_case(B, c) if kind == "sweep" else workloads.qwen_case()
+                if kind == "qwen" else workloads.skewed_case() if kind == "skewed"
+                else workloads.long_case(B, c))
+        kv = case.kv_bytes()
+        R = max(2, math.ceil(4 * LLC_BYTES / kv))
+        if kv * R > 24e9:
+            R = max(1, int(24e9 // kv))
+        rot = Rotation(case, R, device)
+        ctx_sum = int(case.context_lens.astype(np.int64).sum())
+        nbytes = alg_bytes(case.B, ctx_sum, case.Hq, case.Hkv, case.D)
+        K = int(min(2000, max(20, 2e9 / nbytes)))
+        out = torch.empty((case.B, case.Hq, case.D), dtype=torch.float16, device=device)
+
+        def time_it(fn):
+            for i in range(max(10, K // 10)):
+                fn(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(K):
+                fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / K
+
+        us_unsplit = time_it(lambda i: pkv.paged_attention_decode(
+            rot.q, rot.k_pool, rot.v_pool, rot.bt[i % R], rot.ctx, case.scale, out=out))
+        best = None
+        for P in (128, 256, 512, 1024, 2048):
+            if P % case.block_size:
+                continue
+            Pm = case.max_partitions(P)
+            po = torch.empty((case.B, case.Hq, Pm, case.D), dtype=torch.float32, device=device)
+            pl = torch.empty((case.B, case.Hq, Pm), dtype=torch.float32, device=device)
+
+            def split(i):
+                pkv.paged_attention_decode_split(rot.q, rot.k_pool, rot.v_pool, rot.bt[i % R],
+                                                 rot.ctx, case.scale, P, Pm, po, pl)
+                pkv.split_reduce(po, pl, rot.ctx, P, out=out)
+            us = time_it(split)
+            if best is None or us < best[1]:
+                best = (P, us)
+            del po, pl
+        line = {"point": case.name, "B": case.B, "sum_ctx": ctx_sum,
+                "alg_bytes": nbytes, "rotation_sets": R,
+                "unsplit_us": round(us_unsplit, 3),
+                "unsplit_gbs": round(nbytes / us_unsplit / 1e3, 1),
+                "split_best_partition": best[0], "split_us": round(best[1], 3),
+                "split_gbs": round(nbytes / best[1] / 1e3, 1)}
+        print(json.dumps(line), flush=True)
+        lines.append(line)
+        del rot
+        torch.cuda.empty_cache()
+    with open(args.sweep, "w") as f:
+        for ln in lines:
+            f.write(json.dumps(ln) + "\n")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path "
+                                   "needs no collective, see DESIGN.md for how it would shard",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    if args.sweep:
+        run_sweep(args)
+        return
+    print(json.dumps(run_headline(args)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,7 +51,8 @@
  *  - Device data contract (not checkable on the host): context_lens[b] in
  *    [0, max_blocks_per_seq * block_size]; block_tables[b, i] in
  *    [0, num_blocks) for i < ceil(context_lens[b] / block_size); entries past
- *    that are never read.  The kernels guard themselves: a context length
+ *    that may be read (the whole [B, max_blocks_per_seq] array must be
+ *    readable) but their values are never used.  The kernels guard themselves: a context length
  *    outside the range is clamped into it, and a block id outside
  *    [0, num_blocks) is not read and its positions do not contribute.  So a
  *    contract violation gives wrong numbers, never an out-of-bounds access.
@@ -88,7 +89,8 @@ int pkv_version(void);
  *   waves_per_group    wavefronts (64 lanes) per workgroup: 1, 2, 4 or 8;
  *                      0 restores the default.
  *   subtiles_per_iter  16-token subtiles a wave loads per loop iteration: 1, 2
- *                      or 4; 0 restores the default.
+ *                      or 4 (head_dim 128 uses at most 2); 0 restores the
+ *                      default.
  * Results do not depend on the shape beyond fp32 summation order.  Not
  * thread-safe with respect to concurrent launches (a launch reads whichever
  * value is current).  Returns PKV_OK or PKV_ERR_INVALID_ARG.

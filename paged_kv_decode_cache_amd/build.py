@@ -13,6 +13,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
 SOURCES = [os.path.join(CSRC, "pkv_api.hip")]
 DEPS = SOURCES + [os.path.join(CSRC, "pkv_kernels.hpp"), os.path.join(INCLUDE, "pkv.h")]
+# Measurement aid used by bench.py only (streaming-read bandwidth probe).
+PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "probe_read.hip")]
 
 
 def hipcc() -> str:
@@ -22,17 +25,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpkv.so)")
 
 
-def command(out: str = LIB, extra=()) -> list:
+def command(out: str = LIB, extra=(), sources=None) -> list:
     return [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unused-function",
-            "-I", INCLUDE, "-I", CSRC, *extra, *SOURCES, "-o", out]
+            "-I", INCLUDE, "-I", CSRC, *extra, *(sources or SOURCES), "-o", out]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libpkv.so next to this file (always)."""
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def _compile(out: str, sources, verbose: bool) -> str:
+    tmp = out + ".tmp"
+    cmd = command(tmp, sources=sources)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,8 +44,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source (libpkv.so and the bench probe library) next
+    to this file, always."""
+    _compile(PROBE_LIB, PROBE_SOURCES, verbose)
+    return _compile(LIB, SOURCES, verbose)
 
 
 def is_stale() -> bool:

@@ -39,18 +39,34 @@ Shape pick_shape(int which, int head_dim) {
   // Defaults: the split pass runs one partition per workgroup with 4 waves;
   // the unsplit pass has one workgroup per (sequence, KV head) and uses 8.
   s.waves = which == 0 ? 8 : 4;
-  s.subtiles = head_dim == 64 ? 4 : 2;
+  s.subtiles = head_dim == 64 ? 2 : 1;
   const int w = g_cfg_waves[which].load(std::memory_order_relaxed);
   const int t = g_cfg_subtiles[which].load(std::memory_order_relaxed);
   if (w) s.waves = w;
   if (t) s.subtiles = t;
+  // head_dim 128 keeps two tiles of K/V in registers only up to 2 subtiles
+  if (head_dim == 128 && s.subtiles > 2) s.subtiles = 2;
   return s;
 }
 
 template <int D, int NS, int NW, bool SPLIT>
 void launch_attn_inst(const AttnParams& p, int64_t grid, hipStream_t st) {
-  hipLaunchKernelGGL((pkv::attn_kernel<D, NS, NW, SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     st, p);
+  // Groups of up to 8 query heads put the fp16 remainder of P in the spare
+  // MFMA columns (one PV MFMA per 16 dims instead of two).
+  if (p.G <= 8)
+    hipLaunchKernelGGL((pkv::attn_kernel<D, NS, NW, SPLIT, true>), dim3((unsigned)grid),
+                       dim3(NW * 64), 0, st, p);
+  else
+    hipLaunchKernelGGL((pkv::attn_kernel<D, NS, NW, SPLIT, false>), dim3((unsigned)grid),
+                       dim3(NW * 64), 0, st, p);
+}
+
+int spb_shift_of(int32_t block_size) {
+  const int spb = block_size / 16;
+  if (spb & (spb - 1)) return -1;
+  int sh = 0;
+  while ((1 << sh) < spb) ++sh;
+  return sh;
 }
 
 template <int D, bool SPLIT>
@@ -65,7 +81,13 @@ void launch_attn_ns(const AttnParams& p, int64_t grid, Shape s, hipStream_t st) 
   switch (s.subtiles) {
     case 1: PKV_NW_CASES(1) break;
     case 2: PKV_NW_CASES(2) break;
-    default: PKV_NW_CASES(4) break;
+    default:
+      if constexpr (D == 64) {
+        PKV_NW_CASES(4)
+      } else {
+        PKV_NW_CASES(2)
+      }
+      break;
   }
 #undef PKV_NW_CASES
 }
@@ -194,6 +216,7 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
   p.max_blocks = max_blocks_per_seq;
   p.partition_size = max_blocks_per_seq * block_size;
   p.max_partitions = 1;
+  p.spb_shift = spb_shift_of(block_size);
   p.scale_log2 = scale * pkv::kLog2e;
   return launch_attn<false>(p, head_dim, grid, static_cast<hipStream_t>(stream));
 }
@@ -236,6 +259,7 @@ int paged_attention_decode_split(float* partial_out, float* partial_lse, const v
   p.max_blocks = max_blocks_per_seq;
   p.partition_size = partition_size;
   p.max_partitions = max_partitions;
+  p.spb_shift = spb_shift_of(block_size);
   p.scale_log2 = scale * pkv::kLog2e;
   return launch_attn<true>(p, head_dim, grid, static_cast<hipStream_t>(stream));
 }
@@ -266,9 +290,9 @@ int split_reduce(void* out, float* lse_out, const float* partial_out, const floa
   p.max_partitions = max_partitions;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (head_dim == 64)
-    hipLaunchKernelGGL(pkv::split_reduce_kernel<64>, dim3((unsigned)grid), dim3(64), 0, st, p);
+    hipLaunchKernelGGL(pkv::split_reduce_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL(pkv::split_reduce_kernel<128>, dim3((unsigned)grid), dim3(64), 0, st, p);
+    hipLaunchKernelGGL(pkv::split_reduce_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, p);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

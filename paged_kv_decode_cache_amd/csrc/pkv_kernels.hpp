@@ -27,7 +27,7 @@
 //     must be the transposed A operand (row = dim, k = token), so each
 //     subtile of V goes through LDS: written row-major as loaded (masked
 //     positions written as zeros, so a NaN in an unused slot never meets a
-//     zero weight), read back one 16-bit element per lane and k-slot.
+//     zero weight), read back with gfx950's transposing LDS read.
 //   * Partial results of the NW waves merge through LDS at the end.
 //
 // All accumulation is fp32.  Positions past the context, or in a block whose
@@ -60,6 +60,7 @@ struct AttnParams {
   int32_t Hq, Hkv, G;
   int32_t block_size, num_blocks, max_blocks;
   int32_t partition_size, max_partitions;
+  int32_t spb_shift;    // log2(block_size / 16) when a power of two, else -1
   float scale_log2;     // softmax scale * log2(e)
 };
 
@@ -110,18 +111,213 @@ struct AttnSmem {
       (kStageHalves * 2 > kMergeFloats * 4 ? kStageHalves * 2 : kMergeFloats * 4);
 };
 
-template <int D, int NS, int NW, bool SPLIT>
+// The running maximum used as the softmax reference moves only when a tile's
+// maximum exceeds it by more than this (log2 units), so probabilities stay
+// <= 2^8 and the accumulators are rescaled only a few times per sequence.
+constexpr float kRescaleLog2 = 8.0f;
+
+// K and V registers of one tile (NS subtiles of 16 tokens) of one wave.
+template <int D, int NS>
+struct KVTile {
+  f16x8 k[NS][D / 32];
+  f16x8 v[NS][D / 32];
+  int okmask;  // bit j: subtile j was loaded (valid block id, inside the range)
+  int s0;
+  bool full;   // every position of the tile is attended: no masking needed
+};
+
+// Physical block ids of the NS subtiles starting at subtile s0, one per lane
+// (lanes 0..NS-1; -1 at or past subtile `limit`).  One vector load per wave.
+template <int NS>
+__device__ __forceinline__ int load_block_ids(const int32_t* bt_row, int s0, int limit,
+                                              int spb, int spb_shift, int lane) {
+  const int s = s0 + (lane & (NS - 1));
+  int id = -1;
+  if (lane < NS && s < limit) id = bt_row[spb_shift >= 0 ? (s >> spb_shift) : (s / spb)];
+  return id;
+}
+
+// Issue the K/V loads of one tile.  `ids` comes from load_block_ids; a block
+// id outside [0, num_blocks) is not read and its subtile is masked out.  All
+// address arithmetic is wave-uniform except the lane's fixed offset.
+template <int D, int NS>
+__device__ __forceinline__ void load_kv_tile(KVTile<D, NS>& T, const AttnParams& a, int ids,
+                                             int s0, int sub_end, int t_end, int spb,
+                                             int spb_shift, int64_t tok_stride, int kvh,
+                                             int lane_off) {
+  constexpr int KC = D / 32;
+  T.s0 = s0;
+  int okm = 0;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int phys = __builtin_amdgcn_readlane(ids, j);
+    const bool ok = s0 + j < sub_end && phys >= 0 && phys < a.num_blocks;
+    okm |= (ok ? 1 : 0) << j;
+    const int s = s0 + j;
+    const int sib = spb_shift >= 0 ? (s & (spb - 1)) : (s % spb);
+    const int64_t blk_off =
+        ((int64_t)(ok ? phys : 0) * a.block_size + sib * 16) * tok_stride + (int64_t)kvh * D;
+    if (ok) {
+      const f16* kp = a.k_pool + blk_off + lane_off;
+      const f16* vp = a.v_pool + blk_off + lane_off;
+#pragma unroll
+      for (int m = 0; m < KC; ++m) {
+        T.k[j][m] = *reinterpret_cast<const f16x8*>(kp + 32 * m);
+        T.v[j][m] = *reinterpret_cast<const f16x8*>(vp + 32 * m);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < KC; ++m) {
+        T.k[j][m] = zero8();
+        T.v[j][m] = zero8();
+      }
+    }
+  }
+  T.okmask = okm;
+  T.full = okm == (1 << NS) - 1 && ((s0 + NS) << 4) <= t_end;
+}
+
+// Online-softmax state of one wave: reference maximum (log2 domain) per head
+// column, the lane's partial weight sum, and the O^T accumulators.
+template <int D>
+struct SoftmaxState {
+  f32x4 o[D / 16];
+  float m;
+  float l;
+};
+
+// QK^T, online-softmax update and PV for one loaded tile.
+//   DUAL (G <= 8): MFMA columns 0..7 carry the query heads with P rounded to
+//   fp16, columns 8..15 the same heads with the fp16 remainder P - fp16(P),
+//   so one PV MFMA per 16 dims takes both parts; the two column halves are
+//   summed once at the end.  Otherwise (G <= 16) each part has its own MFMA.
+//   FULL: every position of the tile is attended, so no masking.
+template <int D, int NS, bool DUAL, bool FULL>
+__device__ __forceinline__ void consume_tile(const KVTile<D, NS>& T, SoftmaxState<D>& st,
+                                             const f16x8 (&qb)[D / 32], f16* stage,
+                                             float scale_log2, int t_end, int lane) {
+  constexpr int KC = D / 32;
+  constexpr int NDB = D / 16;
+  constexpr int ROW = D + 4;
+  const int g = lane & 15;
+  const int quad = lane >> 4;
+
+  f32x4 sc[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    f32x4 acc = zero4f();
+#pragma unroll
+    for (int m = 0; m < KC; ++m)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(T.k[j][m], qb[m], acc, 0, 0, 0);
+    sc[j] = acc;
+  }
+
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float x = sc[j][v] * scale_log2;
+      if (!FULL) {
+        const int tok = ((T.s0 + j) << 4) + 4 * quad + v;
+        x = (((T.okmask >> j) & 1) && tok < t_end) ? x : -INFINITY;
+      }
+      sc[j][v] = x;
+      tmax = fmaxf(tmax, x);
+    }
+  }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const bool grow = tmax > st.m + kRescaleLog2;
+  if (__any(grow)) {
+    const float m_new = grow ? tmax : st.m;
+    const float alpha = fast_exp2(st.m - m_new);  // 1 where unchanged, 0 from -inf
+    st.m = m_new;
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) st.o[i] *= alpha;
+  }
+  const float m_use = (st.m == -INFINITY) ? 0.0f : st.m;
+
+  f16x4 ph[NS], pl[NS];
+  const bool lo_col = DUAL && g >= 8;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float pv = fast_exp2(sc[j][v] - m_use);
+      st.l += pv;
+      const f16 hi = (f16)pv;
+      if (DUAL) {
+        ph[j][v] = (f16)(lo_col ? pv - (float)hi : pv);
+      } else {
+        ph[j][v] = hi;
+        pl[j][v] = (f16)(pv - (float)hi);
+      }
+    }
+  }
+
+  // V subtiles -> LDS, row-major [token][dim]; masked rows as zeros.
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    bool keep = true;
+    if (!FULL) {
+      const int tok = ((T.s0 + j) << 4) + (lane & 15);
+      keep = ((T.okmask >> j) & 1) && tok < t_end;
+    }
+    f16* row = stage + (j * 16 + (lane & 15)) * ROW + 8 * quad;
+#pragma unroll
+    for (int m = 0; m < KC; ++m) {
+      const f16x8 v = keep ? T.v[j][m] : zero8();
+      *reinterpret_cast<f16x4*>(row + 32 * m) = v.lo;
+      *reinterpret_cast<f16x4*>(row + 32 * m + 4) = v.hi;
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+  // V^T operand by transposing LDS reads: within each 16-lane group, lane i
+  // of ds_read_b64_tr_b16 receives element (i % 4) of the 8-byte chunks that
+  // lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4 point at.  Lane j of quad q points
+  // at V[4q + j/4][16 db + 4 (j%4) ..], so lane (q, i) receives
+  // V[4q + k][16 db + i] for k = 0..3: the A operand of the 16x16x16 MFMA.
+  const f16* tr = stage + (4 * quad + (g >> 2)) * ROW + 4 * (g & 3);
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(tr + j * 16 * ROW + 16 * db));
+      const f16x4 va = __builtin_bit_cast(f16x4, raw);
+      st.o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph[j], st.o[db], 0, 0, 0);
+      if (!DUAL) st.o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pl[j], st.o[db], 0, 0, 0);
+    }
+  }
+  asm volatile("" ::: "memory");  // next tile's LDS writes stay after these reads
+}
+
+template <int D, int NS, bool DUAL>
+__device__ __forceinline__ void consume(const KVTile<D, NS>& T, SoftmaxState<D>& st,
+                                        const f16x8 (&qb)[D / 32], f16* stage,
+                                        float scale_log2, int t_end, int lane) {
+  if (T.full)
+    consume_tile<D, NS, DUAL, true>(T, st, qb, stage, scale_log2, t_end, lane);
+  else
+    consume_tile<D, NS, DUAL, false>(T, st, qb, stage, scale_log2, t_end, lane);
+}
+
+template <int D, int NS, int NW, bool SPLIT, bool DUAL>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
   constexpr int KC = D / 32;   // QK MFMAs (16x16x32) per subtile
   constexpr int NDB = D / 16;  // PV MFMA column blocks (16 dims each)
   using SM = AttnSmem<D, NS>;
-  constexpr int ROW = SM::kRow;
   __shared__ __attribute__((aligned(16))) unsigned char smem[NW * SM::kWaveBytes];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int g = lane & 15;     // MFMA column: query head within the group
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane & 15;     // MFMA column
   const int quad = lane >> 4;  // 0..3
+  const int head_col = DUAL ? (g & 7) : g;  // query head (within the group) of this column
 
   const int Hkv = a.Hkv;
   const int kvh = blockIdx.x % Hkv;
@@ -134,12 +330,28 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
     b = rest;
   }
 
+  const int spb = a.block_size >> 4;  // subtiles per block
+  const int spb_shift = a.spb_shift;
+  const int64_t tok_stride = (int64_t)Hkv * D;
+  const int lane_off = (lane & 15) * Hkv * D + 8 * quad;
+  const int32_t* bt_row = a.block_tables + (size_t)b * a.max_blocks;
+  constexpr int STEP = NW * NS;  // subtiles between a wave's consecutive tiles
+
+  // The block ids of the wave's first two tiles are requested together with
+  // the context length (not after it): any entry of the table row is a valid
+  // read, and ids past the context are masked once the length is known.
+  const int t_begin = SPLIT ? p * a.partition_size : 0;
+  const int sub_begin = t_begin >> 4;
+  const int s_first = sub_begin + wave * NS;
+  const int sub_cap = a.max_blocks * spb;  // subtiles the table row covers
+  int ids0 = load_block_ids<NS>(bt_row, s_first, sub_cap, spb, spb_shift, lane);
+  int ids1 = load_block_ids<NS>(bt_row, s_first + STEP, sub_cap, spb, spb_shift, lane);
+
   const int cap = a.max_blocks * a.block_size;
   int ctx = a.context_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
-  int t_begin = 0, t_end = ctx;
+  int t_end = ctx;
   if (SPLIT) {
-    t_begin = p * a.partition_size;
     if (t_begin >= ctx) {
       if (threadIdx.x < a.G)
         a.partial_lse[((size_t)b * a.Hq + kvh * a.G + threadIdx.x) * a.max_partitions + p] =
@@ -148,12 +360,15 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
     }
     t_end = min(ctx, t_begin + a.partition_size);
   }
+  const int sub_end = (t_end + 15) >> 4;
 
-  // Query group as the B operand: lane l holds q[head l%16][8*(l/16) + 32m ..].
+  // The query group as the B operand (lane l holds q[head of column l%16]
+  // [8*(l/16) + 32m ..]).
   f16x8 qb[KC];
   {
-    const bool hv = g < a.G;
-    const f16* qrow = a.q + ((size_t)b * a.Hq + kvh * a.G + (hv ? g : 0)) * D + 8 * quad;
+    const bool hv = head_col < a.G;
+    const f16* qrow =
+        a.q + ((size_t)b * a.Hq + kvh * a.G + (hv ? head_col : 0)) * D + 8 * quad;
 #pragma unroll
     for (int m = 0; m < KC; ++m) {
       const f16x8 v = *reinterpret_cast<const f16x8*>(qrow + 32 * m);
@@ -161,142 +376,58 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
     }
   }
 
-  const int sub_begin = t_begin >> 4;
-  const int sub_end = (t_end + 15) >> 4;
-  const int spb = a.block_size >> 4;  // subtiles per block
-  const int64_t tok_stride = (int64_t)Hkv * D;
-  const int lane_off = (lane & 15) * Hkv * D + 8 * quad;
-  const int32_t* bt_row = a.block_tables + (size_t)b * a.max_blocks;
-
-  f32x4 o[NDB];
+  SoftmaxState<D> st;
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) o[i] = zero4f();
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
+  for (int i = 0; i < NDB; ++i) st.o[i] = zero4f();
+  st.m = -INFINITY;
+  st.l = 0.0f;
   f16* stage = reinterpret_cast<f16*>(smem + wave * SM::kWaveBytes);
 
-  for (int s0 = sub_begin + wave * NS; s0 < sub_end; s0 += NW * NS) {
-    bool ok[NS];
-    int64_t base[NS];
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int s = s0 + j;
-      const int blk = s / spb;
-      bool v = s < sub_end;
-      const int phys = v ? bt_row[blk] : 0;
-      v = v && phys >= 0 && phys < a.num_blocks;
-      ok[j] = v;
-      base[j] = ((int64_t)(v ? phys : 0) * a.block_size + (s - blk * spb) * 16) * tok_stride +
-                (int64_t)kvh * D;
-    }
-
-    f16x8 kr[NS][KC], vr[NS][KC];
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      if (ok[j]) {
-        const f16* kp = a.k_pool + base[j] + lane_off;
-        const f16* vp = a.v_pool + base[j] + lane_off;
-#pragma unroll
-        for (int m = 0; m < KC; ++m) {
-          kr[j][m] = *reinterpret_cast<const f16x8*>(kp + 32 * m);
-          vr[j][m] = *reinterpret_cast<const f16x8*>(vp + 32 * m);
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < KC; ++m) {
-          kr[j][m] = zero8();
-          vr[j][m] = zero8();
-        }
+  // Two-deep software pipeline over the wave's tiles: while tile t is
+  // consumed, the K/V of tile t+1 and the block ids of tile t+2 are in flight.
+  // Block ids are always requested before the K/V loads they run ahead of, so
+  // waiting for them never waits for K/V.
+  KVTile<D, NS> A, Bt;
+  int s0 = s_first;
+  if (s0 < sub_end) {
+    load_kv_tile<D, NS>(A, a, ids0, s0, sub_end, t_end, spb, spb_shift, tok_stride, kvh, lane_off);
+    while (true) {
+      const int s1 = s0 + STEP;
+      if (s1 < sub_end) {
+        const int ids2 = load_block_ids<NS>(bt_row, s1 + STEP, sub_end, spb, spb_shift, lane);
+        load_kv_tile<D, NS>(Bt, a, ids1, s1, sub_end, t_end, spb, spb_shift, tok_stride, kvh, lane_off);
+        ids1 = ids2;
       }
-    }
-
-    // S^T[token][head] for each subtile.
-    f32x4 sc[NS];
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      f32x4 acc = zero4f();
-#pragma unroll
-      for (int m = 0; m < KC; ++m)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[j][m], qb[m], acc, 0, 0, 0);
-      sc[j] = acc;
-    }
-
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tok = ((s0 + j) << 4) + 4 * quad + v;
-        float x = sc[j][v] * a.scale_log2;
-        x = (ok[j] && tok < t_end) ? x : -INFINITY;
-        sc[j][v] = x;
-        tmax = fmaxf(tmax, x);
+      consume<D, NS, DUAL>(A, st, qb, stage, a.scale_log2, t_end, lane);
+      if (s1 >= sub_end) break;
+      const int s2 = s1 + STEP;
+      if (s2 < sub_end) {
+        const int ids3 = load_block_ids<NS>(bt_row, s2 + STEP, sub_end, spb, spb_shift, lane);
+        load_kv_tile<D, NS>(A, a, ids1, s2, sub_end, t_end, spb, spb_shift, tok_stride, kvh, lane_off);
+        ids1 = ids3;
       }
+      consume<D, NS, DUAL>(Bt, st, qb, stage, a.scale_log2, t_end, lane);
+      if (s2 >= sub_end) break;
+      s0 = s2;
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) o[i] *= alpha;
-
-    f16x4 ph[NS], pl[NS];
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float pv = fast_exp2(sc[j][v] - m_use);
-        l_run += pv;
-        const f16 hi = (f16)pv;
-        ph[j][v] = hi;
-        pl[j][v] = (f16)(pv - (float)hi);
-      }
-    }
-
-    // V subtiles -> LDS, row-major [token][dim], masked rows as zeros.
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int tok = ((s0 + j) << 4) + (lane & 15);
-      const bool keep = ok[j] && tok < t_end;
-      f16* row = stage + (j * 16 + (lane & 15)) * ROW + 8 * quad;
-#pragma unroll
-      for (int m = 0; m < KC; ++m) {
-        const f16x8 v = keep ? vr[j][m] : zero8();
-        *reinterpret_cast<f16x4*>(row + 32 * m) = v.lo;
-        *reinterpret_cast<f16x4*>(row + 32 * m + 4) = v.hi;
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const f16* col = stage + (j * 16 + 4 * quad) * ROW + g;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        f16x4 va;
-        va[0] = col[16 * db];
-        va[1] = col[16 * db + ROW];
-        va[2] = col[16 * db + 2 * ROW];
-        va[3] = col[16 * db + 3 * ROW];
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph[j], o[db], 0, 0, 0);
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pl[j], o[db], 0, 0, 0);
-      }
-    }
-    asm volatile("" ::: "memory");
   }
 
+  // DUAL: fold the remainder columns (8..15) into the head columns (0..7).
+  if (DUAL) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) st.o[db][v] += __shfl_xor(st.o[db][v], 8);
+  }
   // Sum of the wave's weights per head: lanes of one head differ in quad.
-  float l_tot = l_run + __shfl_xor(l_run, 16);
+  float l_tot = st.l + __shfl_xor(st.l, 16);
   l_tot += __shfl_xor(l_tot, 32);
 
-  // Final value for column block db of this lane's head: o_sum / l_sum with
-  // the running maximum m_max (log2 domain).
+  // Final value for column block db of this lane's head.
+  const bool emits = (DUAL ? g < 8 : true) && head_col < a.G;
   auto emit = [&](int db, f32x4 acc, float L, float M) {
-    if (g >= a.G) return;
-    const int h = kvh * a.G + g;
+    if (!emits) return;
+    const int h = kvh * a.G + head_col;
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     const int d0 = 16 * db + 4 * quad;
     if (SPLIT) {
@@ -318,7 +449,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
 
   if (NW == 1) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) emit(db, o[db], l_tot, m_run);
+    for (int db = 0; db < NDB; ++db) emit(db, st.o[db], l_tot, st.m);
     return;
   }
 
@@ -327,9 +458,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) mine[(db * 4 + v) * 64 + lane] = o[db][v];
+    for (int v = 0; v < 4; ++v) mine[(db * 4 + v) * 64 + lane] = st.o[db][v];
   if (quad == 0) {
-    mine[NDB * 4 * 64 + g] = m_run;
+    mine[NDB * 4 * 64 + g] = st.m;
     mine[NDB * 4 * 64 + 16 + g] = l_tot;
   }
   __syncthreads();
@@ -356,51 +487,93 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
   }
 }
 
-// LSE-weighted merge of the valid partitions of one (sequence, query head);
-// one wave per pair, lane = dim (D = 64) or dim pair (D = 128).
+// LSE-weighted merge of the valid partitions of one (sequence, query head).
+// One 256-thread workgroup per pair: the partition weights exp(lse_p - max)
+// are computed once into LDS, then thread (row r, column c) accumulates
+// partitions r, r + ROWS, ... of its 4 dims with 16-byte loads, so ROWS
+// partitions are in flight at a time; rows are summed through LDS at the end.
+// The first 256 log-sum-exps and the first ROWS partition rows are requested
+// together with the context length (every index below max_partitions is a
+// valid read), so a call with few partitions costs one memory round trip.
 template <int D>
-__global__ __launch_bounds__(64) void split_reduce_kernel(const ReduceParams a) {
-  constexpr int PER = D / 64;
+__global__ __launch_bounds__(256) void split_reduce_kernel(const ReduceParams a) {
+  constexpr int TPR = D / 4;         // threads per partition row (4 dims each)
+  constexpr int ROWS = 256 / TPR;    // partitions in flight (16 for D=64)
+  constexpr int CHUNK = 2048;        // weights staged per pass
+  __shared__ float w[CHUNK];
+  __shared__ f32x4 red[ROWS][TPR];
+  __shared__ float wave_part[4];
+
   const int bh = blockIdx.x;
   const int b = bh / a.Hq;
-  const int lane = threadIdx.x;
-  const int cap = a.max_partitions * a.partition_size;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int r = t / TPR;
+  const int c = t % TPR;
+  const int Pm = a.max_partitions;
+  const float* lse = a.partial_lse + (size_t)bh * Pm;
+  const float* po = a.partial_out + (size_t)bh * Pm * D + 4 * c;
+
+  const float lse_t = t < Pm ? lse[t] : -INFINITY;
+  const f32x4 x_r = r < Pm ? *reinterpret_cast<const f32x4*>(po + (size_t)r * D) : zero4f();
+  const int cap = Pm * a.partition_size;
   int ctx = a.context_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
   const int np = (ctx + a.partition_size - 1) / a.partition_size;
-  const float* lse = a.partial_lse + (size_t)bh * a.max_partitions;
-  const float* po = a.partial_out + (size_t)bh * a.max_partitions * D;
 
-  float M = -INFINITY;
-  for (int i = lane; i < np; i += 64) M = fmaxf(M, lse[i]);
+  float M = t < np ? lse_t : -INFINITY;
+  for (int i = t + 256; i < np; i += 256) M = fmaxf(M, lse[i]);
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh));
+  if (lane == 0) wave_part[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(wave_part[0], wave_part[1]), fmaxf(wave_part[2], wave_part[3]));
 
-  float acc[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
+  f32x4 acc = zero4f();
   float L = 0.0f;
   if (M != -INFINITY) {
     const float M2 = M * kLog2e;
-    for (int i = 0; i < np; ++i) {
-      const float e = fast_exp2(fmaf(lse[i], kLog2e, -M2));
-      L += e;
-      const float* row = po + (size_t)i * D + PER * lane;
-      if (PER == 1) {
-        acc[0] = fmaf(e, row[0], acc[0]);
-      } else {
-        const float2 x = *reinterpret_cast<const float2*>(row);
-        acc[0] = fmaf(e, x.x, acc[0]);
-        acc[1] = fmaf(e, x.y, acc[1]);
+    for (int base = 0; base < np; base += CHUNK) {
+      const int n = min(CHUNK, np - base);
+      __syncthreads();  // previous chunk's weights are consumed
+      for (int i = t; i < n; i += 256) {
+        const float li = (base == 0 && i == t) ? lse_t : lse[base + i];
+        const float e = fast_exp2(fmaf(li, kLog2e, -M2));
+        w[i] = e;
+        L += e;
+      }
+      __syncthreads();
+      int i = r;
+      if (base == 0) {
+        if (r < n) acc += w[r] * x_r;
+        i = r + ROWS;
+      }
+#pragma unroll 4
+      for (; i < n; i += ROWS) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(po + (size_t)(base + i) * D);
+        acc += w[i] * x;
       }
     }
   }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  f16* dst = a.out + (size_t)bh * D + PER * lane;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) dst[k] = (f16)(acc[k] * inv);
-  if (a.lse_out != nullptr && lane == 0)
-    a.lse_out[bh] = L > 0.0f ? M + logf(L) : -INFINITY;
+  for (int sh = 32; sh >= 1; sh >>= 1) L += __shfl_xor(L, sh);
+  __syncthreads();
+  if (lane == 0) wave_part[wave] = L;
+  red[r][c] = acc;
+  __syncthreads();
+  if (t < TPR) {
+    L = wave_part[0] + wave_part[1] + wave_part[2] + wave_part[3];
+    f32x4 sum = zero4f();
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) sum += red[i][t];
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    f16x4 o;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) o[v] = (f16)(sum[v] * inv);
+    *reinterpret_cast<f16x4*>(a.out + (size_t)bh * D + 4 * t) = o;
+    if (a.lse_out != nullptr && t == 0) a.lse_out[bh] = L > 0.0f ? M + logf(L) : -INFINITY;
+  }
 }
 
 // Bit-exact scatter of new K/V rows: one thread per 16-byte chunk of one
@@ -414,12 +587,15 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams a) {
   const int64_t rest = idx / chunks;
   const int h = (int)(rest % a.Hkv);
   const int64_t n = rest / a.Hkv;
+  // The new rows are read together with their slot (not after it).
+  const int64_t src = (n * a.Hkv + h) * a.D + 8 * c;
+  const uint4 kx = *reinterpret_cast<const uint4*>(a.k_new + src);
+  const uint4 vx = *reinterpret_cast<const uint4*>(a.v_new + src);
   const int64_t slot = a.slot_mapping[n];
   if (slot < 0 || slot >= a.num_slots) return;
   const int64_t dst = (slot * a.Hkv + h) * a.D + 8 * c;
-  const int64_t src = (n * a.Hkv + h) * a.D + 8 * c;
-  *reinterpret_cast<uint4*>(a.k_pool + dst) = *reinterpret_cast<const uint4*>(a.k_new + src);
-  *reinterpret_cast<uint4*>(a.v_pool + dst) = *reinterpret_cast<const uint4*>(a.v_new + src);
+  *reinterpret_cast<uint4*>(a.k_pool + dst) = kx;
+  *reinterpret_cast<uint4*>(a.v_pool + dst) = vx;
 }
 
 }  // namespace pkv

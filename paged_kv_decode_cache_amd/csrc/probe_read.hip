@@ -1,0 +1,92 @@
+// Streaming-read probe: reads a buffer once with 16-byte loads and writes
+// nothing (unless an XOR of everything it read hits one fixed pattern), so its
+// time measures the achievable HBM read bandwidth for a given byte count.  A
+// measurement aid for the benchmark, not part of the decode path.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* src, int64_t n16,
+                                                          uint4* sink) {
+  uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc.x ^= a.x ^ b.x ^ c.x ^ d.x;
+    acc.y ^= a.y ^ b.y ^ c.y ^ d.y;
+    acc.z ^= a.z ^ b.z ^ c.z ^ d.z;
+    acc.w ^= a.w ^ b.w ^ c.w ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    acc.x ^= a.x;
+    acc.y ^= a.y;
+    acc.z ^= a.z;
+    acc.w ^= a.w;
+  }
+  if (acc.x == 0x9E3779B9u && acc.y == 0x7F4A7C15u && acc.z == 0x85EBCA6Bu &&
+      acc.w == 0xC2B2AE35u)
+    sink[0] = acc;
+}
+
+// Paged-pattern read: the buffer is a pool of 128-byte head rows with two
+// heads interleaved (row r of head h at (2r + h) * 128 B), read in 16-row
+// subtiles of one head, one subtile per wave per step.  mode 1: lane l reads
+// row l % 16, bytes 16*(l/16) + 64m (the MFMA A-operand layout); mode 2: lane l
+// reads row l / 8 + 8m, bytes 16*(l%8) (each 128-byte row by 8 adjacent lanes).
+__global__ __launch_bounds__(256) void paged_read_kernel(const unsigned char* src,
+                                                         int64_t n_subtiles, int mode,
+                                                         uint4* sink) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+  for (int64_t s = wave; s < n_subtiles; s += nwaves) {
+    const int64_t h = s & 1;
+    const int64_t row0 = (s >> 1) * 16;
+    uint4 x[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      int64_t row, col;
+      if (mode == 1) {
+        row = row0 + (lane & 15);
+        col = 16 * (lane >> 4) + 64 * m;
+      } else {
+        row = row0 + (lane >> 3) + 8 * m;
+        col = 16 * (lane & 7);
+      }
+      x[m] = *reinterpret_cast<const uint4*>(src + (2 * row + h) * 128 + col);
+    }
+    acc.x ^= x[0].x ^ x[1].x;
+    acc.y ^= x[0].y ^ x[1].y;
+    acc.z ^= x[0].z ^ x[1].z;
+    acc.w ^= x[0].w ^ x[1].w;
+  }
+  if (acc.x == 0x9E3779B9u && acc.y == 0x7F4A7C15u && acc.z == 0x85EBCA6Bu &&
+      acc.w == 0xC2B2AE35u)
+    sink[0] = acc;
+}
+
+}  // namespace
+
+// Reads `bytes` (a multiple of 4096) of src in the paged pattern `mode`.
+extern "C" int pkv_probe_paged_read(const void* src, int64_t bytes, void* sink, int grid,
+                                    int mode, void* stream) {
+  if (!src || !sink || bytes <= 0 || bytes % 4096 != 0 || grid <= 0 || (mode != 1 && mode != 2))
+    return -1;
+  hipLaunchKernelGGL(paged_read_kernel, dim3(grid), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const unsigned char*>(src),
+                     bytes / 2048, mode, static_cast<uint4*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+extern "C" int pkv_probe_stream_read(const void* src, int64_t bytes, void* sink, int grid,
+                                     void* stream) {
+  if (!src || !sink || bytes <= 0 || bytes % 16 != 0 || grid <= 0) return -1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(src), bytes / 16,
+                     static_cast<uint4*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
