@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the paged KV-cache decode path on one MI355X.
 
-One step is the whole hot path over one batch: kv_cache_append of the batch's
-new tokens, the split-context attention pass (paged_attention_decode_split),
-and the LSE merge (split_reduce).  The default workload is the batch x context
+One step is the whole hot path over one batch: the cache write of the batch's
+new tokens, the split-context attention pass and the LSE merge.  By default
+the step is paged_decode_step, which fuses the three into one launch; the
+three-launch form (kv_cache_append + paged_attention_decode_split +
+split_reduce) is timed beside it.  The default workload is the batch x context
 sweep point B=32, ctx=4096 (Hq=14, Hkv=2, D=64, block_size=16, fp16).
 
 Timing protocol
@@ -54,11 +56,14 @@ def parse():
     ap.add_argument("--ctx", type=int, default=4096)
     ap.add_argument("--partition", type=int, default=512, help="split partition size (tokens)")
     ap.add_argument("--waves", type=int, default=0, help="split pass waves/workgroup (0=default)")
-    ap.add_argument("--subtiles", type=int, default=0, help="split pass subtiles/iter (0=default)")
+    ap.add_argument("--subtiles", type=int, default=0, help="split pass subtiles/tile (0=default)")
+    ap.add_argument("--depth", type=int, default=0, help="split pass tiles in flight (0=default)")
     ap.add_argument("--sets", type=int, default=0, help="rotation sets (0 = auto, >= 4x LLC)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", default="", help="write the full sweep as JSON lines to this file")
+    ap.add_argument("--path", choices=("step", "split"), default="step",
+                    help="step: fused paged_decode_step; split: append + split pass + merge")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 20 plain device copies of MIB MiB (a known-size "
                          "reference for HBM traffic counters)")
@@ -202,14 +207,15 @@ def probe_read_gbs(rot, nbytes, R, K):
 
 KERNEL_SOURCES = ("paged_kv_decode_cache_amd/csrc/pkv_kernels.hpp",
                   "paged_kv_decode_cache_amd/csrc/pkv_api.hip")
-TRAFFIC_PROFILE = "profiles/hbm_traffic_attn_split__sweep_B32_ctx4096.md"
+TRAFFIC_PROFILES = {"step": "profiles/hbm_traffic_decode_step__sweep_B32_ctx4096.md",
+                    "split": "profiles/hbm_traffic_attn_split__sweep_B32_ctx4096.md"}
 
 
-def profiled_traffic(kernel_name):
+def profiled_traffic(kernel_name, profile):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel sources for this kernel; else None."""
     import hashlib
-    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    path = os.path.join(ROOT, profile)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -250,14 +256,24 @@ def run_headline(args):
     R = args.sets or max(2, math.ceil(4 * LLC_BYTES / kv_set))
     rot = Rotation(case, R, device)
     Pm = case.max_partitions(P)
-    po = torch.empty((B, case.Hq, Pm, case.D), dtype=torch.float32, device=device)
-    pl = torch.empty((B, case.Hq, Pm), dtype=torch.float32, device=device)
+    ws = pkv.StepWorkspace(B, case.Hq, case.Hkv, case.D, Pm, device)
+    po, pl = ws.partial_out, ws.partial_lse
     out = torch.empty((B, case.Hq, case.D), dtype=torch.float16, device=device)
-    if args.waves or args.subtiles:
-        pkv.set_launch_config("split", args.waves, args.subtiles)
+    if args.waves or args.subtiles or args.depth:
+        pkv.set_launch_config("split", args.waves, args.subtiles, args.depth)
     stream = torch.cuda.current_stream(device)
 
-    def step(i, ev=None):
+    def fused_step(i):
+        r = i % R
+        pkv.paged_decode_step(rot.q, rot.k_pool, rot.v_pool, rot.bt[r], rot.ctx, case.scale, P,
+                              k_new=rot.k_new, v_new=rot.v_new, slot_mapping=rot.slots[r],
+                              workspace=ws, out=out)
+
+    def split_pass(i):
+        pkv.paged_attention_decode_split(rot.q, rot.k_pool, rot.v_pool, rot.bt[i % R], rot.ctx,
+                                         case.scale, P, Pm, po, pl)
+
+    def three_launch_step(i, ev=None):
         r = i % R
         pkv.kv_cache_append(rot.k_pool, rot.v_pool, rot.k_new, rot.v_new, rot.slots[r])
         if ev is not None:
@@ -267,15 +283,15 @@ def run_headline(args):
             ev[1].record(stream)
         pkv.split_reduce(po, pl, rot.ctx, P, out=out)
 
-    def split_pass(i):
-        pkv.paged_attention_decode_split(rot.q, rot.k_pool, rot.v_pool, rot.bt[i % R], rot.ctx,
-                                         case.scale, P, Pm, po, pl)
+    fused = args.path == "step"
+    step = fused_step if fused else three_launch_step
 
-    # warm-up: W steps and at least 200 ms
+    # warm-up: W steps of each path and at least 200 ms
     t0 = time.perf_counter()
     i = 0
     while i < args.warmup or time.perf_counter() - t0 < 0.2:
-        step(i)
+        fused_step(i)
+        three_launch_step(i)
         i += 1
         if i % 64 == 0:
             torch.cuda.synchronize()
@@ -285,10 +301,9 @@ def run_headline(args):
     # Graph-launched steps: R consecutive steps (one per rotation set) are
     # captured once and replayed; HIP events on the replay stream bracket the
     # timed replays.  This is the timing of record (no host launch overhead).
-    g_step = capture([lambda r=r: step(r) for r in range(R)])
-    step_us = time_graph(g_step, R, K)
-    g_kern = capture([lambda r=r: split_pass(r) for r in range(R)])
-    kern_us = time_graph(g_kern, R, K)
+    fused_us = time_graph(capture([lambda r=r: fused_step(r) for r in range(R)]), R, K)
+    three_us = time_graph(capture([lambda r=r: three_launch_step(r) for r in range(R)]), R, K)
+    split_us = time_graph(capture([lambda r=r: split_pass(r) for r in range(R)]), R, K)
 
     # Eager launches (Python binding per call), for context.
     torch.cuda.synchronize()
@@ -297,34 +312,39 @@ def run_headline(args):
         step(i)
     torch.cuda.synchronize()
     eager_step_us = (time.perf_counter() - t0) * 1e6 / K
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
-    for i in range(K):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    eager_kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
 
     # Unsplit decode on the same rotation, graph-launched.
     g_uns = capture([lambda r=r: pkv.paged_attention_decode(
         rot.q, rot.k_pool, rot.v_pool, rot.bt[r], rot.ctx, case.scale, out=out)
         for r in range(R)])
     unsplit_us = time_graph(g_uns, R, K)
-    if args.waves or args.subtiles:
-        pkv.set_launch_config("split", 0, 0)
+    if args.waves or args.subtiles or args.depth:
+        pkv.set_launch_config("split", 0, 0, 0)
     probe = probe_read_gbs(rot, case.kv_bytes(), R, K)
-    ms_per_step = step_us * 1e-3
 
     ctx_sum = int(case.context_lens.astype(np.int64).sum())
     step_bytes = alg_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
-    kbytes = split_kernel_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
+    app_bytes = append_bytes(B, case.Hkv, case.D)
     ns = args.subtiles or (2 if case.D == 64 else 1)
     nw = args.waves or 4
+    depth = args.depth or 2
     dual = "true" if case.Hq // case.Hkv <= 8 else "false"
-    kname = f"void pkv::attn_kernel<{case.D}, {ns}, {nw}, true, {dual}>(pkv::AttnParams)"
-    traffic = profiled_traffic(kname) if (B, ctx, P) == (32, 4096, 512) else None
+    if fused:
+        ms_per_step = fused_us * 1e-3
+        kern_us = fused_us
+        kbytes = step_bytes + app_bytes
+        kname = f"void pkv::attn_kernel<{case.D}, {ns}, {nw}, {depth}, 2, {dual}>(pkv::AttnParams)"
+        step_desc = "paged_decode_step (append + split pass + merge in one launch)"
+    else:
+        ms_per_step = three_us * 1e-3
+        kern_us = split_us
+        kbytes = split_kernel_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
+        kname = f"void pkv::attn_kernel<{case.D}, {ns}, {nw}, {depth}, 1, {dual}>(pkv::AttnParams)"
+        step_desc = "kv_cache_append + paged_attention_decode_split + split_reduce"
+    tprof = TRAFFIC_PROFILES[args.path]
+    traffic = profiled_traffic(kname, tprof) if (B, ctx, P) == (32, 4096, 512) else None
     achieved = kbytes / (kern_us * 1e-6) / 1e9
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    kern_p = np.percentile(eager_kern_ms * 1e3, [10, 50, 90])
+    value = (step_bytes + app_bytes) / (ms_per_step * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -343,11 +363,12 @@ def run_headline(args):
                         f"Hkv={case.Hkv}, D={case.D}, block_size={case.block_size})",
             "B": B, "ctx": ctx, "Hq": case.Hq, "Hkv": case.Hkv, "D": case.D,
             "block_size": case.block_size, "partition_size": P, "max_partitions": Pm,
-            "step": "kv_cache_append + paged_attention_decode_split + split_reduce",
+            "step": step_desc,
             "rotation_sets": R, "kv_bytes_all_sets": kv_set * R,
             "launch": "HIP graph of R consecutive steps, replayed",
-            "algorithmic_bytes_per_step": step_bytes,
-            "append_bytes_per_step": append_bytes(B, case.Hkv, case.D),
+            "algorithmic_bytes_per_step": step_bytes + app_bytes,
+            "attention_bytes_per_step": step_bytes,
+            "append_bytes_per_step": app_bytes,
             "accumulate": "fp32",
         },
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
@@ -360,15 +381,19 @@ def run_headline(args):
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4),
             "traffic": traffic,
-            "traffic_source": TRAFFIC_PROFILE if traffic else None,
+            "traffic_source": tprof if traffic else None,
             "kernel_us": round(kern_us, 3),
             "kernel_timing": "HIP events around graph replays of R back-to-back launches",
-            "eager_kernel_us_p10_p50_p90": [round(float(x), 3) for x in kern_p],
             "algorithmic_bytes_per_launch": kbytes,
             "probe_read_gbs": round(probe, 1),
             "frac_of_probe": round(achieved / probe, 4) if probe else None,
         },
         "eager_us_per_step": round(eager_step_us, 3),
+        "three_launch_step_us": round(three_us, 3),
+        "split_pass_us": round(split_us, 3),
+        "split_pass_gbs": round(split_kernel_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
+                                / (split_us * 1e-6) / 1e9, 1),
+        "fused_step_us": round(fused_us, 3),
         "unsplit_decode_us": round(unsplit_us, 3),
         "unsplit_decode_gbs": round(step_bytes / (unsplit_us * 1e-6) / 1e9, 1),
     }
@@ -400,48 +425,51 @@ def run_sweep(args):
         R = max(2, math.ceil(4 * LLC_BYTES / kv))
         if kv * R > 24e9:
             R = max(1, int(24e9 // kv))
+        R = min(R, 64)
         rot = Rotation(case, R, device)
         ctx_sum = int(case.context_lens.astype(np.int64).sum())
         nbytes = alg_bytes(case.B, ctx_sum, case.Hq, case.Hkv, case.D)
-        K = int(min(2000, max(20, 2e9 / nbytes)))
+        K = int(min(400, max(20, 2e9 / nbytes)))
         out = torch.empty((case.B, case.Hq, case.D), dtype=torch.float16, device=device)
 
         def time_it(fn):
-            for i in range(max(10, K // 10)):
-                fn(i)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(K):
-                fn(i)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) * 1e3 / K
+            n = min(R, 16)
+            return time_graph(capture([lambda r=r: fn(r) for r in range(n)]), n, K)
 
         us_unsplit = time_it(lambda i: pkv.paged_attention_decode(
             rot.q, rot.k_pool, rot.v_pool, rot.bt[i % R], rot.ctx, case.scale, out=out))
         best = None
+        best_step = None
         for P in (128, 256, 512, 1024, 2048):
             if P % case.block_size:
                 continue
             Pm = case.max_partitions(P)
-            po = torch.empty((case.B, case.Hq, Pm, case.D), dtype=torch.float32, device=device)
-            pl = torch.empty((case.B, case.Hq, Pm), dtype=torch.float32, device=device)
+            ws = pkv.StepWorkspace(case.B, case.Hq, case.Hkv, case.D, Pm, device)
+            po, pl = ws.partial_out, ws.partial_lse
 
             def split(i):
                 pkv.paged_attention_decode_split(rot.q, rot.k_pool, rot.v_pool, rot.bt[i % R],
                                                  rot.ctx, case.scale, P, Pm, po, pl)
                 pkv.split_reduce(po, pl, rot.ctx, P, out=out)
+
+            def fused(i):
+                pkv.paged_decode_step(rot.q, rot.k_pool, rot.v_pool, rot.bt[i % R], rot.ctx,
+                                      case.scale, P, workspace=ws, out=out)
             us = time_it(split)
             if best is None or us < best[1]:
                 best = (P, us)
-            del po, pl
+            us = time_it(fused)
+            if best_step is None or us < best_step[1]:
+                best_step = (P, us)
+            del po, pl, ws
         line = {"point": case.name, "B": case.B, "sum_ctx": ctx_sum,
                 "alg_bytes": nbytes, "rotation_sets": R,
                 "unsplit_us": round(us_unsplit, 3),
                 "unsplit_gbs": round(nbytes / us_unsplit / 1e3, 1),
                 "split_best_partition": best[0], "split_us": round(best[1], 3),
-                "split_gbs": round(nbytes / best[1] / 1e3, 1)}
+                "split_gbs": round(nbytes / best[1] / 1e3, 1),
+                "fused_best_partition": best_step[0], "fused_us": round(best_step[1], 3),
+                "fused_gbs": round(nbytes / best_step[1] / 1e3, 1)}
         print(json.dumps(line), flush=True)
         lines.append(line)
         del rot

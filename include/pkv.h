@@ -12,6 +12,7 @@
  *                                 sequence's context ("flash-decoding" style
  *                                 split), writing per-partition results
  *   split_reduce                  log-sum-exp weighted merge of the partitions
+ *   paged_decode_step             append + split pass + merge in one launch
  *
  * Sources (the pages describing the method):
  *   - nanoserve project write-up, section "What I built": a paged KV cache
@@ -86,16 +87,18 @@ int pkv_version(void);
  * pkv_set_launch_config -- tuning aid: choose the launch shape of an
  * attention pass for later calls in this process.
  *   which              0 = paged_attention_decode, 1 = the split pass.
- *   waves_per_group    wavefronts (64 lanes) per workgroup: 1, 2, 4 or 8;
- *                      0 restores the default.
- *   subtiles_per_iter  16-token subtiles a wave loads per loop iteration: 1, 2
- *                      or 4 (head_dim 128 uses at most 2); 0 restores the
- *                      default.
- * Results do not depend on the shape beyond fp32 summation order.  Not
- * thread-safe with respect to concurrent launches (a launch reads whichever
- * value is current).  Returns PKV_OK or PKV_ERR_INVALID_ARG.
+ *   waves_per_group    wavefronts (64 lanes) per workgroup: 1, 2, 4 or 8.
+ *   subtiles_per_tile  16-token subtiles a wave loads per tile: 1, 2 or 4.
+ *   tiles_in_flight    tiles of K/V a wave keeps in flight: 2 or 4.
+ * 0 in any of the last three restores its default.  Shapes beyond the
+ * register budget (more than 8 subtiles in flight at head_dim 64, 4 at
+ * head_dim 128) are reduced to fit.  Results do not depend on the shape
+ * beyond fp32 summation order.  Not synchronised with concurrent launches (a
+ * launch uses whichever value is current).  Returns PKV_OK or
+ * PKV_ERR_INVALID_ARG.
  */
-int pkv_set_launch_config(int which, int waves_per_group, int subtiles_per_iter);
+int pkv_set_launch_config(int which, int waves_per_group, int subtiles_per_tile,
+                          int tiles_in_flight);
 
 /*
  * kv_cache_append -- write the K and V rows of new tokens into their slots.
@@ -186,6 +189,50 @@ int paged_attention_decode_split(float* partial_out, float* partial_lse,
                                  int32_t max_blocks_per_seq,
                                  int32_t partition_size, int32_t max_partitions,
                                  float scale, void* stream);
+
+/*
+ * paged_decode_step -- one whole decode step in a single launch: the cache
+ * write of kv_cache_append, the split pass of paged_attention_decode_split
+ * and the merge of split_reduce, fused.  This is the launch-overhead remedy
+ * the pages point to (nanoserve write-up, "Results": decode time is mostly
+ * launch overhead; the author's post thread, Day 74: a CUDA-graphed arm).
+ *
+ *   out, lse_out      as split_reduce (lse_out may be NULL).
+ *   k_pool, v_pool    the pools, updated in place by the append.
+ *   q                 [B, num_q_heads, head_dim] fp16.
+ *   k_new, v_new      [B, num_kv_heads, head_dim] fp16: one new token per
+ *                     sequence.
+ *   slot_mapping      [B] int64, the new token's slot, or NULL for no append
+ *                     (then k_new/v_new may be NULL).  A negative slot, or one
+ *                     past the pool, skips that sequence's append.  The slot
+ *                     must be the one of position context_lens[b] - 1 in the
+ *                     sequence's block table (the decode step's new token); the
+ *                     step then attends over it exactly as append followed by
+ *                     decode would.  Any other slot is still written, but
+ *                     whether this step's attention sees the new value there
+ *                     is undefined.
+ *   partial_out, partial_lse  workspace as for paged_attention_decode_split.
+ *   counters          [B, num_kv_heads] int32 workspace: must be zero before
+ *                     the first call; every call leaves it zero.  Calls that
+ *                     share a counter workspace must be ordered by a stream.
+ * Other arguments as for paged_attention_decode_split.
+ *
+ * Each (sequence, KV head) with more than one non-empty partition is merged
+ * by the workgroup that finishes its last partition (an atomic counter with
+ * release/acquire ordering; nothing waits on another workgroup).  A sequence
+ * that fits one partition is written directly.  Results equal append +
+ * split pass + split_reduce up to fp32 summation order.
+ */
+int paged_decode_step(void* out, float* lse_out,
+                      void* k_pool, void* v_pool,
+                      const void* q, const void* k_new, const void* v_new,
+                      const int64_t* slot_mapping,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      float* partial_out, float* partial_lse, int32_t* counters,
+                      int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                      int32_t max_blocks_per_seq, int32_t partition_size,
+                      int32_t max_partitions, float scale, void* stream);
 
 /*
  * split_reduce -- merge the partitions written by

@@ -6,10 +6,11 @@ The computation lives in libpkv.so (hand-written HIP kernels behind a C ABI,
 from ._binding import (LIB_PATH, HEADER_PATH, load_library, declared_functions,
                        status_string, set_launch_config, kv_cache_append,
                        paged_attention_decode, paged_attention_decode_split,
-                       split_reduce, max_partitions_for,
+                       split_reduce, max_partitions_for, paged_decode_step, StepWorkspace,
                        PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_LAUNCH)
 
 __all__ = ["LIB_PATH", "HEADER_PATH", "load_library", "declared_functions", "status_string",
            "set_launch_config", "kv_cache_append", "paged_attention_decode",
            "paged_attention_decode_split", "split_reduce", "max_partitions_for",
+           "paged_decode_step", "StepWorkspace",
            "PKV_OK", "PKV_ERR_INVALID_ARG", "PKV_ERR_UNSUPPORTED", "PKV_ERR_LAUNCH"]

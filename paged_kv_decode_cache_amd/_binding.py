@@ -31,13 +31,16 @@ _F = ctypes.c_float
 _SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_version": (ctypes.c_int, []),
-    "pkv_set_launch_config": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "pkv_set_launch_config": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int]),
     "kv_cache_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "paged_attention_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                               _I, _F, _P]),
     "paged_attention_decode_split": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I,
                                                     _I, _I, _I, _I, _I, _I, _F, _P]),
     "split_reduce": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "paged_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                         _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
 }
 
 _lib = None
@@ -110,11 +113,12 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, device=None
         raise ValueError(f"{name} must be contiguous")
 
 
-def set_launch_config(which: str, waves_per_group: int = 0, subtiles_per_iter: int = 0):
+def set_launch_config(which: str, waves_per_group: int = 0, subtiles_per_tile: int = 0,
+                      tiles_in_flight: int = 0):
     """Tuning aid: launch shape of 'decode' or 'split' (0 = library default)."""
     idx = {"decode": 0, "split": 1}[which]
-    _raise(load_library().pkv_set_launch_config(idx, waves_per_group, subtiles_per_iter),
-           "pkv_set_launch_config")
+    _raise(load_library().pkv_set_launch_config(idx, waves_per_group, subtiles_per_tile,
+                                                tiles_in_flight), "pkv_set_launch_config")
 
 
 def kv_cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
@@ -222,4 +226,61 @@ def split_reduce(partial_out, partial_lse, context_lens, partition_size, out=Non
                                      _ptr(partial_lse), _ptr(context_lens), B, Hq, D,
                                      int(partition_size), P, _stream(dev, stream))
     _raise(rc, "split_reduce")
+    return (out, lse_out) if lse_out is not None else out
+
+
+class StepWorkspace:
+    """Device workspace of paged_decode_step: split partials and the
+    per-(sequence, KV head) counters (zeroed here once; every call leaves them
+    zero).  Allocated with torch by the caller's code, never by the library."""
+
+    def __init__(self, B, num_q_heads, num_kv_heads, head_dim, max_partitions, device):
+        self.partial_out = torch.empty((B, num_q_heads, max_partitions, head_dim),
+                                       dtype=torch.float32, device=device)
+        self.partial_lse = torch.empty((B, num_q_heads, max_partitions), dtype=torch.float32,
+                                       device=device)
+        self.counters = torch.zeros((B, num_kv_heads), dtype=torch.int32, device=device)
+        self.max_partitions = max_partitions
+
+
+def paged_decode_step(q, k_pool, v_pool, block_tables, context_lens, scale, partition_size,
+                      k_new=None, v_new=None, slot_mapping=None, workspace=None, out=None,
+                      lse_out=None, want_lse=False, stream=None):
+    """Fused decode step: append (if slot_mapping is given) + split pass +
+    merge in one launch.  Returns out [B, Hq, D] fp16 (and lse [B, Hq])."""
+    dev, B, Hq, Hkv, D, bs, NB, maxb = _attn_shapes(q, k_pool, v_pool, block_tables,
+                                                    context_lens)
+    Pm = max_partitions_for(maxb, bs, partition_size)
+    if workspace is None:
+        workspace = StepWorkspace(B, Hq, Hkv, D, Pm, dev)
+    ws = workspace
+    _need(ws.partial_out, "partial_out", torch.float32, 4, dev)
+    _need(ws.partial_lse, "partial_lse", torch.float32, 3, dev)
+    _need(ws.counters, "counters", torch.int32, 2, dev)
+    Pm = ws.max_partitions
+    if ws.partial_out.shape != (B, Hq, Pm, D) or ws.partial_lse.shape != (B, Hq, Pm) or \
+            ws.counters.shape != (B, Hkv):
+        raise ValueError("workspace shapes do not match the call")
+    if slot_mapping is not None:
+        _need(k_new, "k_new", torch.float16, 3, dev)
+        _need(v_new, "v_new", torch.float16, 3, dev)
+        _need(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+        if k_new.shape != (B, Hkv, D) or v_new.shape != (B, Hkv, D) or \
+                slot_mapping.shape != (B,):
+            raise ValueError("k_new/v_new must be [B, Hkv, D] and slot_mapping [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    _need(out, "out", torch.float16, 3, dev)
+    if want_lse and lse_out is None:
+        lse_out = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, 2, dev)
+    rc = load_library().paged_decode_step(
+        _ptr(out), _ptr(lse_out), _ptr(k_pool), _ptr(v_pool), _ptr(q),
+        _ptr(k_new) if slot_mapping is not None else None,
+        _ptr(v_new) if slot_mapping is not None else None, _ptr(slot_mapping),
+        _ptr(block_tables), _ptr(context_lens), _ptr(ws.partial_out), _ptr(ws.partial_lse),
+        _ptr(ws.counters), B, Hq, Hkv, D, bs, NB, maxb, int(partition_size), Pm, float(scale),
+        _stream(dev, stream))
+    _raise(rc, "paged_decode_step")
     return (out, lse_out) if lse_out is not None else out

@@ -28,6 +28,9 @@ def hipcc() -> str:
 def command(out: str = LIB, extra=(), sources=None) -> list:
     return [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in VGPRs: the softmax rescale touches them
+            # with VALU ops, which AGPRs would need copies for.
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wall", "-Wno-unused-function",
             "-I", INCLUDE, "-I", CSRC, *extra, *(sources or SOURCES), "-o", out]
 

@@ -24,41 +24,76 @@ bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
 
 bool block_size_ok(int32_t bs) { return bs >= 16 && bs <= 256 && bs % 16 == 0; }
 
-// Launch shape (waves per workgroup, 16-token subtiles per wave iteration);
-// 0 means "library default".  Settable for tuning through
+// Launch shape: waves per workgroup, 16-token subtiles per tile, tiles in
+// flight per wave; 0 means "library default".  Settable for tuning through
 // pkv_set_launch_config.
 std::atomic<int> g_cfg_waves[2] = {{0}, {0}};
 std::atomic<int> g_cfg_subtiles[2] = {{0}, {0}};
+std::atomic<int> g_cfg_depth[2] = {{0}, {0}};
 
 struct Shape {
-  int waves, subtiles;
+  int waves, subtiles, depth;
 };
 
 Shape pick_shape(int which, int head_dim) {
   Shape s;
-  // Defaults: the split pass runs one partition per workgroup with 4 waves;
-  // the unsplit pass has one workgroup per (sequence, KV head) and uses 8.
+  // Defaults (measured on MI355X): the split pass runs one partition per
+  // workgroup with 4 waves; the unsplit pass has one workgroup per
+  // (sequence, KV head) and uses 8.
   s.waves = which == 0 ? 8 : 4;
   s.subtiles = head_dim == 64 ? 2 : 1;
+  s.depth = 2;
   const int w = g_cfg_waves[which].load(std::memory_order_relaxed);
   const int t = g_cfg_subtiles[which].load(std::memory_order_relaxed);
+  const int d = g_cfg_depth[which].load(std::memory_order_relaxed);
   if (w) s.waves = w;
   if (t) s.subtiles = t;
-  // head_dim 128 keeps two tiles of K/V in registers only up to 2 subtiles
+  if (d) s.depth = d;
+  // register budget: at most 8 subtiles of K/V in flight per wave at
+  // head_dim 64 and 4 at head_dim 128
+  const int max_inflight = head_dim == 64 ? 8 : 4;
   if (head_dim == 128 && s.subtiles > 2) s.subtiles = 2;
+  if (s.subtiles * s.depth > max_inflight) s.depth = 2;
+  if (s.subtiles * s.depth > max_inflight) s.subtiles = max_inflight / 2;
   return s;
 }
 
-template <int D, int NS, int NW, bool SPLIT>
+// MODE: 0 unsplit decode, 1 split pass, 2 fused decode step.
+template <int D, int NS, int NW, int DEPTH, int MODE>
 void launch_attn_inst(const AttnParams& p, int64_t grid, hipStream_t st) {
   // Groups of up to 8 query heads put the fp16 remainder of P in the spare
   // MFMA columns (one PV MFMA per 16 dims instead of two).
   if (p.G <= 8)
-    hipLaunchKernelGGL((pkv::attn_kernel<D, NS, NW, SPLIT, true>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((pkv::attn_kernel<D, NS, NW, DEPTH, MODE, true>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, st, p);
   else
-    hipLaunchKernelGGL((pkv::attn_kernel<D, NS, NW, SPLIT, false>), dim3((unsigned)grid),
-                       dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((pkv::attn_kernel<D, NS, NW, DEPTH, MODE, false>),
+                       dim3((unsigned)grid), dim3(NW * 64), 0, st, p);
+}
+
+template <int D, int NS, int DEPTH, int MODE>
+void launch_attn_nw(const AttnParams& p, int64_t grid, int waves, hipStream_t st) {
+  switch (waves) {
+    case 1: launch_attn_inst<D, NS, 1, DEPTH, MODE>(p, grid, st); break;
+    case 2: launch_attn_inst<D, NS, 2, DEPTH, MODE>(p, grid, st); break;
+    case 4: launch_attn_inst<D, NS, 4, DEPTH, MODE>(p, grid, st); break;
+    default: launch_attn_inst<D, NS, 8, DEPTH, MODE>(p, grid, st); break;
+  }
+}
+
+template <int D, int MODE>
+void launch_attn_shape(const AttnParams& p, int64_t grid, Shape s, hipStream_t st) {
+  const int w = s.waves;
+  if (s.depth == 4) {
+    if (s.subtiles == 1) launch_attn_nw<D, 1, 4, MODE>(p, grid, w, st);
+    else if constexpr (D == 64) launch_attn_nw<D, 2, 4, MODE>(p, grid, w, st);
+    else launch_attn_nw<D, 1, 4, MODE>(p, grid, w, st);
+  } else {
+    if (s.subtiles == 1) launch_attn_nw<D, 1, 2, MODE>(p, grid, w, st);
+    else if (s.subtiles == 2) launch_attn_nw<D, 2, 2, MODE>(p, grid, w, st);
+    else if constexpr (D == 64) launch_attn_nw<D, 4, 2, MODE>(p, grid, w, st);
+    else launch_attn_nw<D, 2, 2, MODE>(p, grid, w, st);
+  }
 }
 
 int spb_shift_of(int32_t block_size) {
@@ -69,36 +104,13 @@ int spb_shift_of(int32_t block_size) {
   return sh;
 }
 
-template <int D, bool SPLIT>
-void launch_attn_ns(const AttnParams& p, int64_t grid, Shape s, hipStream_t st) {
-#define PKV_NW_CASES(NS)                                  \
-  switch (s.waves) {                                      \
-    case 1: launch_attn_inst<D, NS, 1, SPLIT>(p, grid, st); break; \
-    case 2: launch_attn_inst<D, NS, 2, SPLIT>(p, grid, st); break; \
-    case 4: launch_attn_inst<D, NS, 4, SPLIT>(p, grid, st); break; \
-    default: launch_attn_inst<D, NS, 8, SPLIT>(p, grid, st); break; \
-  }
-  switch (s.subtiles) {
-    case 1: PKV_NW_CASES(1) break;
-    case 2: PKV_NW_CASES(2) break;
-    default:
-      if constexpr (D == 64) {
-        PKV_NW_CASES(4)
-      } else {
-        PKV_NW_CASES(2)
-      }
-      break;
-  }
-#undef PKV_NW_CASES
-}
-
-template <bool SPLIT>
+template <int MODE>
 int launch_attn(const AttnParams& p, int head_dim, int64_t grid, hipStream_t st) {
-  const Shape s = pick_shape(SPLIT ? 1 : 0, head_dim);
+  const Shape s = pick_shape(MODE == 0 ? 0 : 1, head_dim);
   if (head_dim == 64)
-    launch_attn_ns<64, SPLIT>(p, grid, s, st);
+    launch_attn_shape<64, MODE>(p, grid, s, st);
   else
-    launch_attn_ns<128, SPLIT>(p, grid, s, st);
+    launch_attn_shape<128, MODE>(p, grid, s, st);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
@@ -142,16 +154,20 @@ const char* pkv_status_string(int status) {
 
 int pkv_version(void) { return kVersion; }
 
-int pkv_set_launch_config(int which, int waves_per_group, int subtiles_per_iter) {
+int pkv_set_launch_config(int which, int waves_per_group, int subtiles_per_tile,
+                          int tiles_in_flight) {
   if (which != 0 && which != 1) return PKV_ERR_INVALID_ARG;
   if (waves_per_group != 0 && waves_per_group != 1 && waves_per_group != 2 &&
       waves_per_group != 4 && waves_per_group != 8)
     return PKV_ERR_INVALID_ARG;
-  if (subtiles_per_iter != 0 && subtiles_per_iter != 1 && subtiles_per_iter != 2 &&
-      subtiles_per_iter != 4)
+  if (subtiles_per_tile != 0 && subtiles_per_tile != 1 && subtiles_per_tile != 2 &&
+      subtiles_per_tile != 4)
+    return PKV_ERR_INVALID_ARG;
+  if (tiles_in_flight != 0 && tiles_in_flight != 2 && tiles_in_flight != 4)
     return PKV_ERR_INVALID_ARG;
   g_cfg_waves[which].store(waves_per_group, std::memory_order_relaxed);
-  g_cfg_subtiles[which].store(subtiles_per_iter, std::memory_order_relaxed);
+  g_cfg_subtiles[which].store(subtiles_per_tile, std::memory_order_relaxed);
+  g_cfg_depth[which].store(tiles_in_flight, std::memory_order_relaxed);
   return PKV_OK;
 }
 
@@ -218,7 +234,7 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
   p.max_partitions = 1;
   p.spb_shift = spb_shift_of(block_size);
   p.scale_log2 = scale * pkv::kLog2e;
-  return launch_attn<false>(p, head_dim, grid, static_cast<hipStream_t>(stream));
+  return launch_attn<0>(p, head_dim, grid, static_cast<hipStream_t>(stream));
 }
 
 int paged_attention_decode_split(float* partial_out, float* partial_lse, const void* q,
@@ -261,7 +277,66 @@ int paged_attention_decode_split(float* partial_out, float* partial_lse, const v
   p.max_partitions = max_partitions;
   p.spb_shift = spb_shift_of(block_size);
   p.scale_log2 = scale * pkv::kLog2e;
-  return launch_attn<true>(p, head_dim, grid, static_cast<hipStream_t>(stream));
+  return launch_attn<1>(p, head_dim, grid, static_cast<hipStream_t>(stream));
+}
+
+int paged_decode_step(void* out, float* lse_out, void* k_pool, void* v_pool, const void* q,
+                      const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      float* partial_out, float* partial_lse, int32_t* counters, int32_t B,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                      int32_t partition_size, int32_t max_partitions, float scale,
+                      void* stream) {
+  int rc = check_attn_common(q, k_pool, v_pool, block_tables, context_lens, B, num_q_heads,
+                             num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                             scale);
+  if (rc != PKV_OK) return rc;
+  if (partition_size <= 0 || max_partitions <= 0 || partition_size % block_size != 0)
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_partitions * partition_size < (int64_t)max_blocks_per_seq * block_size)
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_partitions * partition_size > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  if (!out || !partial_out || !partial_lse || !counters) return PKV_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(partial_out, 16) || !aligned(partial_lse, 4) ||
+      !aligned(counters, 4) || (lse_out && !aligned(lse_out, 4)))
+    return PKV_ERR_INVALID_ARG;
+  if (slot_mapping) {
+    if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+        !aligned(slot_mapping, 8))
+      return PKV_ERR_INVALID_ARG;
+  }
+  const int64_t grid = (int64_t)B * num_kv_heads * max_partitions;
+  if (grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
+
+  AttnParams p = {};
+  p.q = static_cast<const pkv::f16*>(q);
+  p.k_pool = static_cast<const pkv::f16*>(k_pool);
+  p.v_pool = static_cast<const pkv::f16*>(v_pool);
+  p.k_pool_w = static_cast<pkv::f16*>(k_pool);
+  p.v_pool_w = static_cast<pkv::f16*>(v_pool);
+  p.k_new = static_cast<const pkv::f16*>(k_new);
+  p.v_new = static_cast<const pkv::f16*>(v_new);
+  p.slot_mapping = slot_mapping;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = static_cast<pkv::f16*>(out);
+  p.lse_out = lse_out;
+  p.partial_out = partial_out;
+  p.partial_lse = partial_lse;
+  p.counters = counters;
+  p.Hq = num_q_heads;
+  p.Hkv = num_kv_heads;
+  p.G = num_q_heads / num_kv_heads;
+  p.block_size = block_size;
+  p.num_blocks = num_blocks;
+  p.max_blocks = max_blocks_per_seq;
+  p.partition_size = partition_size;
+  p.max_partitions = max_partitions;
+  p.spb_shift = spb_shift_of(block_size);
+  p.scale_log2 = scale * pkv::kLog2e;
+  return launch_attn<2>(p, head_dim, grid, static_cast<hipStream_t>(stream));
 }
 
 int split_reduce(void* out, float* lse_out, const float* partial_out, const float* partial_lse,

@@ -8,7 +8,8 @@
 //   (nanoserve write-up, "What I built": one fused kernel walking the block
 //   table with an online softmax).  Inside the workgroup the context is cut
 //   into 16-token subtiles (one subtile never straddles a block, since block
-//   sizes are multiples of 16); wave w takes tiles of NS subtiles round-robin.
+//   sizes are multiples of 16); wave w takes tiles of NS subtiles round-robin
+//   and keeps up to DEPTH of them in flight.
 //
 // Per subtile, per wave
 //   * K rows: lane l loads 16 contiguous bytes of token (l % 16), dims
@@ -62,6 +63,14 @@ struct AttnParams {
   int32_t partition_size, max_partitions;
   int32_t spb_shift;    // log2(block_size / 16) when a power of two, else -1
   float scale_log2;     // softmax scale * log2(e)
+  // fused decode step only
+  f16* k_pool_w;        // the pools, writable (the step's append)
+  f16* v_pool_w;
+  const f16* k_new;     // [B, Hkv, D] the step's new token per sequence
+  const f16* v_new;
+  const int64_t* slot_mapping;  // [B] or null (no append)
+  int32_t* counters;    // [B, Hkv] finished-partition counters, zero between calls
+  float* lse_out;       // [B, Hq] or null
 };
 
 struct ReduceParams {
@@ -178,30 +187,68 @@ __device__ __forceinline__ void load_kv_tile(KVTile<D, NS>& T, const AttnParams&
 }
 
 // Online-softmax state of one wave: reference maximum (log2 domain) per head
-// column, the lane's partial weight sum, and the O^T accumulators.
+// column, and the O^T and weight-sum accumulators (MFMA layout: lane
+// (quad, g) holds rows 4*quad + v of column g).
 template <int D>
 struct SoftmaxState {
   f32x4 o[D / 16];
+  f32x4 lsum;  // row 0 of column g = sum of the column's weights
   float m;
-  float l;
 };
+
+// Maximum over the two lanes l and l^16, then over l^32 (gfx950 row swaps).
+__device__ __forceinline__ float max_across_quads(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 // QK^T, online-softmax update and PV for one loaded tile.
 //   DUAL (G <= 8): MFMA columns 0..7 carry the query heads with P rounded to
 //   fp16, columns 8..15 the same heads with the fp16 remainder P - fp16(P),
 //   so one PV MFMA per 16 dims takes both parts; the two column halves are
 //   summed once at the end.  Otherwise (G <= 16) each part has its own MFMA.
-//   FULL: every position of the tile is attended, so no masking.
-template <int D, int NS, bool DUAL, bool FULL>
-__device__ __forceinline__ void consume_tile(const KVTile<D, NS>& T, SoftmaxState<D>& st,
-                                             const f16x8 (&qb)[D / 32], f16* stage,
-                                             float scale_log2, int t_end, int lane) {
+//   Tiles where every position is attended skip all masking.
+//   c = |scale| * log2(e) > 0 (a negative scale is folded into q; a zero
+//   scale is raised to the smallest normal float, which keeps masked logits
+//   at -inf and rounds every weight of a uniform softmax to exactly 1).
+//   ones: the A operand with row 0 all ones, so one more MFMA per part sums
+//   the weights of every column (no per-value VALU adds).
+//   rem_mul: -1 in DUAL remainder columns, else 0 (selects P or P - fp16(P)
+//   with one exact fused multiply-add).
+//   SUB: position (s_new, tok_new) takes K/V from kn/vn (the fused step's new
+//   token, which this launch also writes to the pool) when its slot is the
+//   position's slot: new_phys * block_size + new_off.
+template <int D, int NS, bool DUAL, bool SUB>
+__device__ __forceinline__ void consume_tile(KVTile<D, NS>& T, SoftmaxState<D>& st,
+                                             const f16x8 (&qb)[D / 32], f16* stage, float c,
+                                             int t_end, int lane, f16x4 ones, float rem_mul,
+                                             int s_new, int tok_new, int64_t slot, int new_phys,
+                                             int new_off, int block_size,
+                                             const f16x8 (&kn)[D / 32],
+                                             const f16x8 (&vn)[D / 32]) {
   constexpr int KC = D / 32;
   constexpr int NDB = D / 16;
   constexpr int ROW = D + 4;
   const int g = lane & 15;
   const int quad = lane >> 4;
+  if (SUB && s_new >= T.s0 && s_new < T.s0 + NS &&
+      (int64_t)new_phys * block_size + new_off == slot) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const bool mine = T.s0 + j == s_new && (lane & 15) == tok_new;
+#pragma unroll
+      for (int m = 0; m < KC; ++m) {
+        T.k[j][m] = mine ? kn[m] : T.k[j][m];
+        T.v[j][m] = mine ? vn[m] : T.v[j][m];
+      }
+    }
+  }
 
+  // raw logits S^T[token][column]
   f32x4 sc[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
@@ -211,48 +258,53 @@ __device__ __forceinline__ void consume_tile(const KVTile<D, NS>& T, SoftmaxStat
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(T.k[j][m], qb[m], acc, 0, 0, 0);
     sc[j] = acc;
   }
-
-  float tmax = -INFINITY;
+  if (!T.full) {
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
+    for (int j = 0; j < NS; ++j) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float x = sc[j][v] * scale_log2;
-      if (!FULL) {
+      for (int v = 0; v < 4; ++v) {
         const int tok = ((T.s0 + j) << 4) + 4 * quad + v;
-        x = (((T.okmask >> j) & 1) && tok < t_end) ? x : -INFINITY;
+        sc[j][v] = (((T.okmask >> j) & 1) && tok < t_end) ? sc[j][v] : -INFINITY;
       }
-      sc[j][v] = x;
-      tmax = fmaxf(tmax, x);
     }
   }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  const bool grow = tmax > st.m + kRescaleLog2;
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) tmax = fmaxf(tmax, sc[j][v]);
+  tmax = max_across_quads(tmax);
+  const float tmax_s = tmax * c;  // c > 0: -inf stays -inf
+  const bool grow = tmax_s > st.m + kRescaleLog2;
   if (__any(grow)) {
-    const float m_new = grow ? tmax : st.m;
+    const float m_new = grow ? tmax_s : st.m;
     const float alpha = fast_exp2(st.m - m_new);  // 1 where unchanged, 0 from -inf
     st.m = m_new;
-    st.l *= alpha;
+    st.lsum *= alpha;
 #pragma unroll
     for (int i = 0; i < NDB; ++i) st.o[i] *= alpha;
   }
-  const float m_use = (st.m == -INFINITY) ? 0.0f : st.m;
+  const float neg_m = (st.m == -INFINITY) ? 0.0f : -st.m;
 
   f16x4 ph[NS], pl[NS];
-  const bool lo_col = DUAL && g >= 8;
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
+    float pv[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float pv = fast_exp2(sc[j][v] - m_use);
-      st.l += pv;
-      const f16 hi = (f16)pv;
+      pv[v] = fast_exp2(fmaf(sc[j][v], c, neg_m));  // masked: exp2(-inf) = 0
+    }
+#pragma unroll
+    for (int v = 0; v < 4; v += 2) {
+      const f16 h0 = (f16)pv[v], h1 = (f16)pv[v + 1];
       if (DUAL) {
-        ph[j][v] = (f16)(lo_col ? pv - (float)hi : pv);
+        ph[j][v] = (f16)fmaf((float)h0, rem_mul, pv[v]);
+        ph[j][v + 1] = (f16)fmaf((float)h1, rem_mul, pv[v + 1]);
       } else {
-        ph[j][v] = hi;
-        pl[j][v] = (f16)(pv - (float)hi);
+        ph[j][v] = h0;
+        ph[j][v + 1] = h1;
+        pl[j][v] = (f16)fmaf((float)h0, -1.0f, pv[v]);
+        pl[j][v + 1] = (f16)fmaf((float)h1, -1.0f, pv[v + 1]);
       }
     }
   }
@@ -260,17 +312,22 @@ __device__ __forceinline__ void consume_tile(const KVTile<D, NS>& T, SoftmaxStat
   // V subtiles -> LDS, row-major [token][dim]; masked rows as zeros.
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    bool keep = true;
-    if (!FULL) {
-      const int tok = ((T.s0 + j) << 4) + (lane & 15);
-      keep = ((T.okmask >> j) & 1) && tok < t_end;
-    }
     f16* row = stage + (j * 16 + (lane & 15)) * ROW + 8 * quad;
+    if (T.full) {
 #pragma unroll
-    for (int m = 0; m < KC; ++m) {
-      const f16x8 v = keep ? T.v[j][m] : zero8();
-      *reinterpret_cast<f16x4*>(row + 32 * m) = v.lo;
-      *reinterpret_cast<f16x4*>(row + 32 * m + 4) = v.hi;
+      for (int m = 0; m < KC; ++m) {
+        *reinterpret_cast<f16x4*>(row + 32 * m) = T.v[j][m].lo;
+        *reinterpret_cast<f16x4*>(row + 32 * m + 4) = T.v[j][m].hi;
+      }
+    } else {
+      const int tok = ((T.s0 + j) << 4) + (lane & 15);
+      const bool keep = ((T.okmask >> j) & 1) && tok < t_end;
+#pragma unroll
+      for (int m = 0; m < KC; ++m) {
+        const f16x8 v = keep ? T.v[j][m] : zero8();
+        *reinterpret_cast<f16x4*>(row + 32 * m) = v.lo;
+        *reinterpret_cast<f16x4*>(row + 32 * m + 4) = v.hi;
+      }
     }
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -283,6 +340,8 @@ __device__ __forceinline__ void consume_tile(const KVTile<D, NS>& T, SoftmaxStat
   const f16* tr = stage + (4 * quad + (g >> 2)) * ROW + 4 * (g & 3);
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
+    st.lsum = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, ph[j], st.lsum, 0, 0, 0);
+    if (!DUAL) st.lsum = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pl[j], st.lsum, 0, 0, 0);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -296,20 +355,137 @@ __device__ __forceinline__ void consume_tile(const KVTile<D, NS>& T, SoftmaxStat
   asm volatile("" ::: "memory");  // next tile's LDS writes stay after these reads
 }
 
-template <int D, int NS, bool DUAL>
-__device__ __forceinline__ void consume(const KVTile<D, NS>& T, SoftmaxState<D>& st,
-                                        const f16x8 (&qb)[D / 32], f16* stage,
-                                        float scale_log2, int t_end, int lane) {
-  if (T.full)
-    consume_tile<D, NS, DUAL, true>(T, st, qb, stage, scale_log2, t_end, lane);
-  else
-    consume_tile<D, NS, DUAL, false>(T, st, qb, stage, scale_log2, t_end, lane);
+// Merge of the NW waves' partial results through LDS; calls emit(db, acc, L,
+// M) for the column blocks this wave finalises.
+template <int D, int NW, typename Emit>
+__device__ __forceinline__ void merge_waves_impl(const SoftmaxState<D>& st, float l_tot,
+                                                 unsigned char* smem, int wave_bytes, int wave,
+                                                 int lane, Emit& emit) {
+  constexpr int NDB = D / 16;
+  const int g = lane & 15;
+  const int quad = lane >> 4;
+  __syncthreads();  // every wave is done with its staging area
+  float* mine = reinterpret_cast<float*>(smem + wave * wave_bytes);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) mine[(db * 4 + v) * 64 + lane] = st.o[db][v];
+  if (quad == 0) {
+    mine[NDB * 4 * 64 + g] = st.m;
+    mine[NDB * 4 * 64 + 16 + g] = l_tot;
+  }
+  __syncthreads();
+
+  for (int db = wave; db < NDB; db += NW) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float* theirs = reinterpret_cast<const float*>(smem + w * wave_bytes);
+      M = fmaxf(M, theirs[NDB * 4 * 64 + g]);
+    }
+    const float mu = (M == -INFINITY) ? 0.0f : M;
+    float L = 0.0f;
+    f32x4 acc = zero4f();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float* theirs = reinterpret_cast<const float*>(smem + w * wave_bytes);
+      const float e = fast_exp2(theirs[NDB * 4 * 64 + g] - mu);
+      L += e * theirs[NDB * 4 * 64 + 16 + g];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] += e * theirs[(db * 4 + v) * 64 + lane];
+    }
+    emit(db, acc, L, M);
+  }
 }
 
-template <int D, int NS, int NW, bool SPLIT, bool DUAL>
+// Cross-workgroup merge of the fused step, run by the workgroup that finished
+// the last partition of (b, kvh): threads cover (head, 4 dims) x partition
+// groups with a streaming LSE merge, and the groups combine through LDS.
+constexpr int kMergeSlots = 512;  // >= 16 heads x 128/4 dims
+
+template <int D, int NW>
+__device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int np,
+                                      float* msm /* 6 * kMergeSlots floats */) {
+  constexpr int NT = NW * 64;
+  constexpr int TPR = D / 4;
+  const int t = threadIdx.x;
+  const int per_group = a.G * TPR;
+  const int ngroups = per_group <= NT ? NT / per_group : 1;
+  const int nslots = per_group * ngroups;
+  for (int slot = t; slot < nslots; slot += NT) {
+    const int grp = slot / per_group;
+    const int hc = slot % per_group;
+    const int h = kvh * a.G + hc / TPR;
+    const int cc = hc % TPR;
+    const float* lse = a.partial_lse + ((size_t)b * a.Hq + h) * a.max_partitions;
+    const float* po = a.partial_out + ((size_t)b * a.Hq + h) * a.max_partitions * D + 4 * cc;
+    float M = -INFINITY, L = 0.0f;
+    f32x4 acc = zero4f();
+#pragma unroll 4
+    for (int q = grp; q < np; q += ngroups) {
+      const float l = __hip_atomic_load(lse + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      f32x4 x;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        x[v] = __hip_atomic_load(po + (size_t)q * D + v, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      if (l > M) {
+        const float sc = fast_exp2((M - l) * kLog2e);  // 0 from -inf
+        acc *= sc;
+        L *= sc;
+        M = l;
+      }
+      const float w = fast_exp2((l - M) * kLog2e);
+      acc += w * x;
+      L += w;
+    }
+    float* r = msm + 6 * slot;
+    r[0] = M;
+    r[1] = L;
+    r[2] = acc[0];
+    r[3] = acc[1];
+    r[4] = acc[2];
+    r[5] = acc[3];
+  }
+  __syncthreads();
+  for (int hc = t; hc < per_group; hc += NT) {
+    float M = -INFINITY;
+    for (int gi = 0; gi < ngroups; ++gi) M = fmaxf(M, msm[6 * (gi * per_group + hc)]);
+    const float mu = M == -INFINITY ? 0.0f : M;
+    float L = 0.0f;
+    f32x4 acc = zero4f();
+    for (int gi = 0; gi < ngroups; ++gi) {
+      const float* r = msm + 6 * (gi * per_group + hc);
+      const float e = fast_exp2((r[0] - mu) * kLog2e);
+      L += e * r[1];
+      acc[0] += e * r[2];
+      acc[1] += e * r[3];
+      acc[2] += e * r[4];
+      acc[3] += e * r[5];
+    }
+    const int h = kvh * a.G + hc / TPR;
+    const int cc = hc % TPR;
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    f16x4 o;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) o[v] = (f16)(acc[v] * inv);
+    *reinterpret_cast<f16x4*>(a.out + ((size_t)b * a.Hq + h) * D + 4 * cc) = o;
+    if (a.lse_out != nullptr && cc == 0)
+      a.lse_out[(size_t)b * a.Hq + h] = L > 0.0f ? M + logf(L) : -INFINITY;
+  }
+}
+
+// MODE 0: unsplit decode (one workgroup per (sequence, KV head), fp16 out).
+// MODE 1: split pass (one workgroup per partition, fp32 partials + lse).
+// MODE 2: fused decode step: the split pass plus, in the same launch, the
+//         step's cache write and the LSE merge by the last workgroup to
+//         finish a (sequence, KV head).
+template <int D, int NS, int NW, int DEPTH, int MODE, bool DUAL>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
   constexpr int KC = D / 32;   // QK MFMAs (16x16x32) per subtile
   constexpr int NDB = D / 16;  // PV MFMA column blocks (16 dims each)
+  constexpr bool SPLIT = MODE >= 1;
+  constexpr bool STEP = MODE == 2;
   using SM = AttnSmem<D, NS>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[NW * SM::kWaveBytes];
 
@@ -335,25 +511,28 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
   const int64_t tok_stride = (int64_t)Hkv * D;
   const int lane_off = (lane & 15) * Hkv * D + 8 * quad;
   const int32_t* bt_row = a.block_tables + (size_t)b * a.max_blocks;
-  constexpr int STEP = NW * NS;  // subtiles between a wave's consecutive tiles
+  constexpr int TSTEP = NW * NS;  // subtiles between a wave's consecutive tiles
 
-  // The block ids of the wave's first two tiles are requested together with
+  // The block ids of the wave's first DEPTH tiles are requested together with
   // the context length (not after it): any entry of the table row is a valid
   // read, and ids past the context are masked once the length is known.
   const int t_begin = SPLIT ? p * a.partition_size : 0;
   const int sub_begin = t_begin >> 4;
   const int s_first = sub_begin + wave * NS;
   const int sub_cap = a.max_blocks * spb;  // subtiles the table row covers
-  int ids0 = load_block_ids<NS>(bt_row, s_first, sub_cap, spb, spb_shift, lane);
-  int ids1 = load_block_ids<NS>(bt_row, s_first + STEP, sub_cap, spb, spb_shift, lane);
+  int ids[DEPTH];
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i)
+    ids[i] = load_block_ids<NS>(bt_row, s_first + i * TSTEP, sub_cap, spb, spb_shift, lane);
 
   const int cap = a.max_blocks * a.block_size;
   int ctx = a.context_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
   int t_end = ctx;
   if (SPLIT) {
-    if (t_begin >= ctx) {
-      if (threadIdx.x < a.G)
+    // the fused step's partition 0 of an empty sequence still writes zeros
+    if (t_begin >= ctx && !(STEP && ctx == 0 && p == 0)) {
+      if (!STEP && threadIdx.x < a.G)
         a.partial_lse[((size_t)b * a.Hq + kvh * a.G + threadIdx.x) * a.max_partitions + p] =
             -INFINITY;
       return;
@@ -361,9 +540,50 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
     t_end = min(ctx, t_begin + a.partition_size);
   }
   const int sub_end = (t_end + 15) >> 4;
+  const int n_parts = STEP ? (ctx + a.partition_size - 1) / a.partition_size : 1;
+
+  // Fused step: the workgroup owning position ctx-1 (partition 0 if ctx = 0)
+  // writes the new token's K/V row of its head into the pool (at the end of
+  // the kernel), and takes that position's K/V from k_new/v_new instead of
+  // the pool when the slot is the position's slot in the block table (so the
+  // launch never reads its own write).  Everything it needs is requested here
+  // and waited for only where it is used.
+  const bool owns_new =
+      STEP && a.slot_mapping != nullptr && p == (ctx > 0 ? (ctx - 1) / a.partition_size : 0);
+  int64_t slot = -1;
+  int new_phys = -1;
+  int s_new = -1, tok_new = -1, new_off = 0;
+  f16x8 kn[KC], vn[KC];
+  const size_t new_row = ((size_t)b * Hkv + kvh) * D;
+  if (owns_new) {
+    slot = a.slot_mapping[b];
+    if (ctx > 0) {
+      const int pos = ctx - 1;
+      const int blk = pos / a.block_size;
+      new_phys = bt_row[blk];
+      new_off = pos - blk * a.block_size;
+      s_new = pos >> 4;
+      tok_new = pos & 15;
+    }
+#pragma unroll
+    for (int m = 0; m < KC; ++m) {
+      kn[m] = *reinterpret_cast<const f16x8*>(a.k_new + new_row + 8 * quad + 32 * m);
+      vn[m] = *reinterpret_cast<const f16x8*>(a.v_new + new_row + 8 * quad + 32 * m);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < KC; ++m) {
+      kn[m] = zero8();
+      vn[m] = zero8();
+    }
+  }
 
   // The query group as the B operand (lane l holds q[head of column l%16]
   // [8*(l/16) + 32m ..]).
+  // A negative scale is folded into q (negating fp16 is exact), so the
+  // kernel works with c = |scale| * log2(e).
+  const bool neg_scale = a.scale_log2 < 0.0f;
+  const float c = fmaxf(neg_scale ? -a.scale_log2 : a.scale_log2, 1.17549435e-38f);
   f16x8 qb[KC];
   {
     const bool hv = head_col < a.G;
@@ -372,43 +592,64 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
 #pragma unroll
     for (int m = 0; m < KC; ++m) {
       const f16x8 v = *reinterpret_cast<const f16x8*>(qrow + 32 * m);
-      qb[m] = hv ? v : zero8();
+      qb[m] = hv ? (neg_scale ? -v : v) : zero8();
     }
   }
+  f16x4 ones;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ones[i] = (f16)(g == 0 ? 1.0f : 0.0f);
+  const float rem_mul = (DUAL && g >= 8) ? -1.0f : 0.0f;
 
   SoftmaxState<D> st;
 #pragma unroll
   for (int i = 0; i < NDB; ++i) st.o[i] = zero4f();
+  st.lsum = zero4f();
   st.m = -INFINITY;
-  st.l = 0.0f;
   f16* stage = reinterpret_cast<f16*>(smem + wave * SM::kWaveBytes);
 
-  // Two-deep software pipeline over the wave's tiles: while tile t is
-  // consumed, the K/V of tile t+1 and the block ids of tile t+2 are in flight.
-  // Block ids are always requested before the K/V loads they run ahead of, so
-  // waiting for them never waits for K/V.
-  KVTile<D, NS> A, Bt;
-  int s0 = s_first;
-  if (s0 < sub_end) {
-    load_kv_tile<D, NS>(A, a, ids0, s0, sub_end, t_end, spb, spb_shift, tok_stride, kvh, lane_off);
-    while (true) {
-      const int s1 = s0 + STEP;
-      if (s1 < sub_end) {
-        const int ids2 = load_block_ids<NS>(bt_row, s1 + STEP, sub_end, spb, spb_shift, lane);
-        load_kv_tile<D, NS>(Bt, a, ids1, s1, sub_end, t_end, spb, spb_shift, tok_stride, kvh, lane_off);
-        ids1 = ids2;
+  // DEPTH-slot software pipeline over the wave's tiles: up to DEPTH tiles of
+  // K/V are in flight while one is consumed.  The block ids of tile u+DEPTH
+  // are requested right after the K/V of tile u, so the in-order wait for
+  // them only ever waits for tiles already consumed.
+  const int n_tiles = s_first < sub_end ? (sub_end - s_first + TSTEP - 1) / TSTEP : 0;
+  KVTile<D, NS> buf[DEPTH];
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i) {
+    if (i < n_tiles) {
+      load_kv_tile<D, NS>(buf[i], a, ids[i], s_first + i * TSTEP, sub_end, t_end, spb, spb_shift,
+                          tok_stride, kvh, lane_off);
+      ids[i] = load_block_ids<NS>(bt_row, s_first + (i + DEPTH) * TSTEP, sub_end, spb,
+                                  spb_shift, lane);
+    }
+  }
+  for (int u0 = 0; u0 < n_tiles; u0 += DEPTH) {
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) {
+      const int u = u0 + i;
+      if (u < n_tiles) {
+        consume_tile<D, NS, DUAL, STEP>(buf[i], st, qb, stage, c, t_end, lane, ones, rem_mul,
+                                        s_new, tok_new, slot, new_phys, new_off,
+                                        a.block_size, kn, vn);
+        if (u + DEPTH < n_tiles) {
+          load_kv_tile<D, NS>(buf[i], a, ids[i], s_first + (u + DEPTH) * TSTEP, sub_end, t_end,
+                              spb, spb_shift, tok_stride, kvh, lane_off);
+          ids[i] = load_block_ids<NS>(bt_row, s_first + (u + 2 * DEPTH) * TSTEP, sub_end, spb,
+                                      spb_shift, lane);
+        }
       }
-      consume<D, NS, DUAL>(A, st, qb, stage, a.scale_log2, t_end, lane);
-      if (s1 >= sub_end) break;
-      const int s2 = s1 + STEP;
-      if (s2 < sub_end) {
-        const int ids3 = load_block_ids<NS>(bt_row, s2 + STEP, sub_end, spb, spb_shift, lane);
-        load_kv_tile<D, NS>(A, a, ids1, s2, sub_end, t_end, spb, spb_shift, tok_stride, kvh, lane_off);
-        ids1 = ids3;
+    }
+  }
+
+  // Fused step: the append of the new token's row of this head.
+  if (owns_new && slot >= 0 && slot < (int64_t)a.num_blocks * a.block_size) {
+    f16* kd = a.k_pool_w + (slot * Hkv + kvh) * D + 8 * quad;
+    f16* vd = a.v_pool_w + (slot * Hkv + kvh) * D + 8 * quad;
+    if (wave == 0 && g == 0) {
+#pragma unroll
+      for (int m = 0; m < KC; ++m) {
+        *reinterpret_cast<f16x8*>(kd + 32 * m) = kn[m];
+        *reinterpret_cast<f16x8*>(vd + 32 * m) = vn[m];
       }
-      consume<D, NS, DUAL>(Bt, st, qb, stage, a.scale_log2, t_end, lane);
-      if (s2 >= sub_end) break;
-      s0 = s2;
     }
   }
 
@@ -418,10 +659,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int v = 0; v < 4; ++v) st.o[db][v] += __shfl_xor(st.o[db][v], 8);
+    st.lsum[0] += __shfl_xor(st.lsum[0], 8);
   }
-  // Sum of the wave's weights per head: lanes of one head differ in quad.
-  float l_tot = st.l + __shfl_xor(st.l, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  // Weight sum of this lane's column: row 0, held by the quad-0 lane.
+  const float l_tot = __shfl(st.lsum[0], g);
 
   // Final value for column block db of this lane's head.
   const bool emits = (DUAL ? g < 8 : true) && head_col < a.G;
@@ -430,61 +671,64 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
     const int h = kvh * a.G + head_col;
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     const int d0 = 16 * db + 4 * quad;
-    if (SPLIT) {
+    if (SPLIT && !(STEP && n_parts <= 1)) {
       f32x4 r;
 #pragma unroll
       for (int v = 0; v < 4; ++v) r[v] = acc[v] * inv;
       float* dst = a.partial_out + (((size_t)b * a.Hq + h) * a.max_partitions + p) * D + d0;
-      *reinterpret_cast<f32x4*>(dst) = r;
-      if (db == 0 && quad == 0)
-        a.partial_lse[((size_t)b * a.Hq + h) * a.max_partitions + p] =
-            L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+      float* lse_dst = a.partial_lse + ((size_t)b * a.Hq + h) * a.max_partitions + p;
+      const float lse_v = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+      if (STEP) {
+        // device-coherent stores: the merging workgroup may run on another XCD
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          __hip_atomic_store(dst + v, r[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (db == 0 && quad == 0)
+          __hip_atomic_store(lse_dst, lse_v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        *reinterpret_cast<f32x4*>(dst) = r;
+        if (db == 0 && quad == 0) *lse_dst = lse_v;
+      }
     } else {
       f16x4 r;
 #pragma unroll
       for (int v = 0; v < 4; ++v) r[v] = (f16)(acc[v] * inv);
       *reinterpret_cast<f16x4*>(a.out + ((size_t)b * a.Hq + h) * D + d0) = r;
+      if (STEP && a.lse_out != nullptr && db == 0 && quad == 0)
+        a.lse_out[(size_t)b * a.Hq + h] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
     }
   };
 
   if (NW == 1) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) emit(db, st.o[db], l_tot, st.m);
-    return;
+  } else {
+    merge_waves_impl<D, NW>(st, l_tot, smem, SM::kWaveBytes, wave, lane, emit);
   }
+  if (!STEP || n_parts <= 1) return;
 
-  __syncthreads();  // every wave is done with its staging area
-  float* mine = reinterpret_cast<float*>(smem + wave * SM::kWaveBytes);
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) mine[(db * 4 + v) * 64 + lane] = st.o[db][v];
-  if (quad == 0) {
-    mine[NDB * 4 * 64 + g] = st.m;
-    mine[NDB * 4 * 64 + 16 + g] = l_tot;
+  // Fused step: count finished partitions of (b, kvh); the last one merges.
+  // Message passing through device-coherent accesses only: the partials were
+  // written with device-scope atomic stores, which are complete (s_waitcnt)
+  // on every wave before the barrier and the count's increment; the merging
+  // workgroup reads them with device-scope atomic loads.  No cache-wide
+  // write-back or invalidate (an acquire/release fence on gfx950 writes back
+  // and invalidates the whole L2 of the XCD, which costs more than the merge
+  // saves while other workgroups stream K/V through that L2).
+  __shared__ int s_last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int* ctr = a.counters + (size_t)b * Hkv + kvh;
+    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == n_parts - 1;
+    if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
   }
   __syncthreads();
-
-  for (int db = wave; db < NDB; db += NW) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float* theirs = reinterpret_cast<const float*>(smem + w * SM::kWaveBytes);
-      M = fmaxf(M, theirs[NDB * 4 * 64 + g]);
-    }
-    const float mu = (M == -INFINITY) ? 0.0f : M;
-    float L = 0.0f;
-    f32x4 acc = zero4f();
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float* theirs = reinterpret_cast<const float*>(smem + w * SM::kWaveBytes);
-      const float e = fast_exp2(theirs[NDB * 4 * 64 + g] - mu);
-      L += e * theirs[NDB * 4 * 64 + 16 + g];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] += e * theirs[(db * 4 + v) * 64 + lane];
-    }
-    emit(db, acc, L, M);
-  }
+  if (!s_last) return;
+  __shared__ float msm[6 * kMergeSlots];
+  merge_step_partitions<D, NW>(a, b, kvh, n_parts, msm);
 }
 
 // LSE-weighted merge of the valid partitions of one (sequence, query head).

@@ -33,31 +33,60 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* src, int6
 
 // Paged-pattern read: the buffer is a pool of 128-byte head rows with two
 // heads interleaved (row r of head h at (2r + h) * 128 B), read in 16-row
-// subtiles of one head, one subtile per wave per step.  mode 1: lane l reads
-// row l % 16, bytes 16*(l/16) + 64m (the MFMA A-operand layout); mode 2: lane l
-// reads row l / 8 + 8m, bytes 16*(l%8) (each 128-byte row by 8 adjacent lanes).
+// subtiles of one head.
+//   mode 1: lane l reads row l % 16, bytes 16*(l/16) + 64m (the MFMA
+//           A-operand layout); adjacent waves of a workgroup read the two
+//           heads of the same rows.
+//   mode 2: as 1 but lane l reads row l / 8 + 8m, bytes 16*(l%8) (each
+//           128-byte row by 8 adjacent lanes).
+//   mode 3: as 1 but the two heads of a row go to adjacent workgroups (which
+//           the dispatcher places on different XCDs), like one workgroup per
+//           (sequence, KV head).
+//   mode +4: the same with non-temporal loads.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const unsigned char* p) {
+  if (NT) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+template <bool NT>
 __global__ __launch_bounds__(256) void paged_read_kernel(const unsigned char* src,
                                                          int64_t n_subtiles, int mode,
                                                          uint4* sink) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
   uint4 acc = make_uint4(0u, 0u, 0u, 0u);
-  for (int64_t s = wave; s < n_subtiles; s += nwaves) {
-    const int64_t h = s & 1;
-    const int64_t row0 = (s >> 1) * 16;
+  int64_t wave, nwaves;
+  if (mode == 3) {
+    // workgroup pair (2k, 2k+1) reads rows of pair k, one head each
+    const int64_t pair = blockIdx.x >> 1;
+    const int64_t npairs = gridDim.x >> 1;
+    wave = pair * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    nwaves = npairs * (blockDim.x >> 6);
+  } else {
+    wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  }
+  const int64_t n_groups = n_subtiles >> 1;  // 16-row groups, both heads
+  for (int64_t s = wave; s < (mode == 3 ? n_groups : n_subtiles); s += nwaves) {
+    const int64_t h = mode == 3 ? (int64_t)(blockIdx.x & 1) : (s & 1);
+    const int64_t row0 = (mode == 3 ? s : (s >> 1)) * 16;
     uint4 x[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       int64_t row, col;
-      if (mode == 1) {
-        row = row0 + (lane & 15);
-        col = 16 * (lane >> 4) + 64 * m;
-      } else {
+      if (mode == 2) {
         row = row0 + (lane >> 3) + 8 * m;
         col = 16 * (lane & 7);
+      } else {
+        row = row0 + (lane & 15);
+        col = 16 * (lane >> 4) + 64 * m;
       }
-      x[m] = *reinterpret_cast<const uint4*>(src + (2 * row + h) * 128 + col);
+      x[m] = ld16<NT>(src + (2 * row + h) * 128 + col);
     }
     acc.x ^= x[0].x ^ x[1].x;
     acc.y ^= x[0].y ^ x[1].y;
@@ -74,11 +103,18 @@ __global__ __launch_bounds__(256) void paged_read_kernel(const unsigned char* sr
 // Reads `bytes` (a multiple of 4096) of src in the paged pattern `mode`.
 extern "C" int pkv_probe_paged_read(const void* src, int64_t bytes, void* sink, int grid,
                                     int mode, void* stream) {
-  if (!src || !sink || bytes <= 0 || bytes % 4096 != 0 || grid <= 0 || (mode != 1 && mode != 2))
+  const int base_mode = mode & 3;
+  if (!src || !sink || bytes <= 0 || bytes % 4096 != 0 || grid <= 0 || grid % 2 != 0 ||
+      base_mode == 0 || mode > 7)
     return -1;
-  hipLaunchKernelGGL(paged_read_kernel, dim3(grid), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const unsigned char*>(src),
-                     bytes / 2048, mode, static_cast<uint4*>(sink));
+  if (mode & 4)
+    hipLaunchKernelGGL(paged_read_kernel<true>, dim3(grid), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const unsigned char*>(src),
+                       bytes / 2048, base_mode, static_cast<uint4*>(sink));
+  else
+    hipLaunchKernelGGL(paged_read_kernel<false>, dim3(grid), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const unsigned char*>(src),
+                       bytes / 2048, base_mode, static_cast<uint4*>(sink));
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -44,11 +44,12 @@ def test_status_strings_and_version():
 
 def test_launch_config_validation():
     lib = pkv.load_library()
-    assert lib.pkv_set_launch_config(2, 4, 4) == -1
-    assert lib.pkv_set_launch_config(0, 3, 4) == -1
-    assert lib.pkv_set_launch_config(1, 4, 3) == -1
-    assert lib.pkv_set_launch_config(0, 0, 0) == 0
-    assert lib.pkv_set_launch_config(1, 0, 0) == 0
+    assert lib.pkv_set_launch_config(2, 4, 4, 2) == -1
+    assert lib.pkv_set_launch_config(0, 3, 4, 2) == -1
+    assert lib.pkv_set_launch_config(1, 4, 3, 2) == -1
+    assert lib.pkv_set_launch_config(1, 4, 2, 3) == -1
+    assert lib.pkv_set_launch_config(0, 0, 0, 0) == 0
+    assert lib.pkv_set_launch_config(1, 0, 0, 0) == 0
 
 
 def _decode(lib, **kw):

@@ -182,9 +182,10 @@ def test_peaked_softmax_large_outputs():
 
 @pytest.mark.parametrize("waves", [1, 2, 4, 8])
 @pytest.mark.parametrize("subtiles", [1, 2, 4])
-def test_decode_every_launch_shape(waves, subtiles):
+@pytest.mark.parametrize("depth", [2, 4])
+def test_decode_every_launch_shape(waves, subtiles, depth):
     try:
-        pkv.set_launch_config("decode", waves, subtiles)
+        pkv.set_launch_config("decode", waves, subtiles, depth)
         for name, D in (("qwen", 64), ("d128", 128)):
             if name == "qwen":
                 c = case("qwen")
@@ -195,9 +196,9 @@ def test_decode_every_launch_shape(waves, subtiles):
             out = _decode(g, c)
             torch.cuda.synchronize()
             want, _ = oracle_decode(c)
-            check_fp16(out, want, f"{name} NW={waves} NS={subtiles}")
+            check_fp16(out, want, f"{name} NW={waves} NS={subtiles} DEPTH={depth}")
     finally:
-        pkv.set_launch_config("decode", 0, 0)
+        pkv.set_launch_config("decode", 0, 0, 0)
 
 
 def test_out_of_range_block_ids_are_ignored():
@@ -221,3 +222,20 @@ def test_out_of_range_block_ids_are_ignored():
     w1 = ref.paged_attention_decode(c.q[1:2], kp, vp, np.array([[0, 1]], np.int32),
                                     np.array([32], np.int32), c.scale)
     check_fp16(out[1:2], w1, "badids seq1")
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 2.0e-3])
+def test_decode_scale_sign_and_zero(scale):
+    """A negative scale is folded into q; a zero scale gives the plain mean of
+    V (uniform weights); a tiny scale stays close to it."""
+    c = workloads.custom_case("scales", B=3, Hq=14, Hkv=2, D=64, block_size=16,
+                              lens=[1, 45, 700], seed=101, scale=scale)
+    g = to_gpu(c)
+    out = _decode(g, c)
+    po, pl = pkv.paged_attention_decode_split(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale,
+                                              64)
+    out_s = pkv.split_reduce(po, pl, g.ctx, 64)
+    torch.cuda.synchronize()
+    want, _ = oracle_decode(c)
+    check_fp16(out, want, f"scale {scale}")
+    check_fp16(out_s, want, f"split scale {scale}")

@@ -120,15 +120,24 @@ def test_split_ctx0():
 
 @pytest.mark.parametrize("waves", [1, 2, 4, 8])
 @pytest.mark.parametrize("subtiles", [1, 2, 4])
-def test_split_every_launch_shape(waves, subtiles):
+@pytest.mark.parametrize("depth", [2, 4])
+def test_split_every_launch_shape(waves, subtiles, depth):
     try:
-        pkv.set_launch_config("split", waves, subtiles)
+        pkv.set_launch_config("split", waves, subtiles, depth)
         c = case("qwen")
         g = to_gpu(c)
         po, pl, out, lse = _split_reduce(g, c, 256)
         torch.cuda.synchronize()
         want, want_lse = oracle_decode(c)
-        check_fp16(out, want, f"split NW={waves} NS={subtiles}")
+        check_fp16(out, want, f"split NW={waves} NS={subtiles} DEPTH={depth}")
         _check_lse(lse, want_lse, "split shapes")
+        # head_dim 128, group 16 (separate hi/lo MFMAs), block size 32
+        c2 = workloads.custom_case("split_d128_g16", B=3, Hq=16, Hkv=1, D=128, block_size=32,
+                                   lens=[33, 700, 1500], seed=100)
+        g2 = to_gpu(c2)
+        po, pl, out2, lse2 = _split_reduce(g2, c2, 256)
+        torch.cuda.synchronize()
+        want2, want_lse2 = oracle_decode(c2)
+        check_fp16(out2, want2, f"split d128 g16 NW={waves} NS={subtiles} DEPTH={depth}")
     finally:
-        pkv.set_launch_config("split", 0, 0)
+        pkv.set_launch_config("split", 0, 0, 0)

@@ -1,0 +1,204 @@
+"""paged_decode_step (append + split pass + merge in one launch) on the GPU
+against the oracle's append followed by its decode."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_decode_cache_amd as pkv
+import workloads
+from oracle import paged_ref as ref
+from gpu_common import (PARTIAL_ATOL, case, check_fp16, host64, needs_gpu, oracle_decode,
+                        sample_rows, say, to_gpu)
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _step(g, c, P, ws=None, append=True, want_lse=True):
+    kw = dict(k_new=g.k_new, v_new=g.v_new, slot_mapping=g.slots) if append else {}
+    return pkv.paged_decode_step(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale, P, workspace=ws,
+                                 want_lse=want_lse, **kw)
+
+
+def _oracle_step(c, seqs=None):
+    kp, vp = ref.kv_cache_append(c.k_pool, c.v_pool, c.k_new, c.v_new, c.slot_mapping)
+    out, lse = ref.paged_attention_decode(c.q, kp, vp, c.block_tables, c.context_lens, c.scale,
+                                          return_lse=True, seqs=seqs)
+    return out, lse, kp, vp
+
+
+def _check_lse(got, want, rows=None):
+    g = host64(got)
+    w = np.asarray(want)
+    if rows is not None:
+        g, w = g[rows], w[rows]
+    assert np.array_equal(np.isneginf(g), np.isneginf(w))
+    fin = np.isfinite(w)
+    if fin.any():
+        assert float(np.abs(g[fin] - w[fin]).max()) <= PARTIAL_ATOL
+
+
+@pytest.mark.parametrize("name,P", [("tiny", 16), ("tiny", 64), ("qwen", 512), ("qwen", 128),
+                                    ("sweep:32:4096", 512), ("sweep:1:128", 512),
+                                    ("sweep:8:2048", 256), ("long:1:32768", 512),
+                                    ("long:4:32768", 2048)])
+def test_step_matches_append_then_decode(name, P):
+    c = case(name)
+    say(f"step {name} P={P}")
+    g = to_gpu(c)
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    out, lse = _step(g, c, P, ws)
+    torch.cuda.synchronize()
+    want, want_lse, kp, vp = _oracle_step(c)
+    check_fp16(out, want, f"step {name}")
+    _check_lse(lse, want_lse)
+    assert np.array_equal(g.k_pool.cpu().numpy().view(np.uint16), kp.view(np.uint16))
+    assert np.array_equal(g.v_pool.cpu().numpy().view(np.uint16), vp.view(np.uint16))
+    assert int(ws.counters.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("name", ["skewed", "long:4:131072"])
+def test_step_full_size_sampled(name):
+    c = case(name)
+    P = 512
+    rows = sample_rows(c, k=16 if name == "skewed" else 4)
+    say(f"step {name} sampled {rows}")
+    g = to_gpu(c)
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    out, lse = _step(g, c, P, ws)
+    torch.cuda.synchronize()
+    want, want_lse, _, _ = _oracle_step(c, seqs=rows)
+    check_fp16(out, want, f"step {name}", rows=rows)
+    _check_lse(lse, want_lse, rows=rows)
+    assert int(ws.counters.abs().sum()) == 0
+
+
+def test_step_repeated_calls_reuse_counters():
+    """Three steps in a row on one workspace (counters reset each time), the
+    second and third with other queries and shorter contexts."""
+    c = case("qwen")
+    P = 256
+    g = to_gpu(c)
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    out1 = _step(g, c, P, ws, want_lse=False).clone()
+    torch.cuda.synchronize()
+    want, _, _, _ = _oracle_step(c)
+    check_fp16(out1, want, "step call 1")
+    rng = np.random.default_rng(7)
+    for k in (2, 3):
+        q2 = (rng.standard_normal(c.q.shape) * 0.5).astype(np.float16)
+        ctx2 = np.maximum(c.context_lens - 100 * k, 1).astype(np.int32)
+        g.q = torch.from_numpy(q2).to(g.q.device)
+        g.ctx = torch.from_numpy(ctx2).to(g.q.device)
+        out2 = _step(g, c, P, ws, append=False, want_lse=False)
+        torch.cuda.synchronize()
+        kp, vp = ref.kv_cache_append(c.k_pool, c.v_pool, c.k_new, c.v_new, c.slot_mapping)
+        want2 = ref.paged_attention_decode(q2, kp, vp, c.block_tables, ctx2, c.scale)
+        check_fp16(out2, want2, f"step call {k}")
+        assert int(ws.counters.abs().sum()) == 0
+
+
+def test_step_without_append_equals_decode():
+    c = case("sweep:8:1024")
+    g = to_gpu(c)
+    out = _step(g, c, 256, append=False, want_lse=False)
+    torch.cuda.synchronize()
+    want, _ = oracle_decode(c)
+    check_fp16(out, want, "step no append")
+
+
+def test_step_edge_lengths_and_single_partition():
+    c = workloads.custom_case("step_edges", B=6, Hq=14, Hkv=2, D=64, block_size=16,
+                              lens=[0, 1, 16, 17, 511, 1300], seed=110, q_mult=4.0)
+    g = to_gpu(c)
+    for P in (16, 512, 2048):
+        g2 = to_gpu(c)
+        out, lse = _step(g2, c, P)
+        torch.cuda.synchronize()
+        want, want_lse, kp, _ = _oracle_step(c)
+        check_fp16(out, want, f"edges P={P}")
+        _check_lse(lse, want_lse)
+        assert int((out[0] != 0).sum()) == 0
+        assert np.array_equal(g2.k_pool.cpu().numpy().view(np.uint16), kp.view(np.uint16))
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,bs", [(16, 1, 128, 32), (32, 8, 128, 16), (4, 4, 64, 64)])
+def test_step_other_shapes(Hq, Hkv, D, bs):
+    c = workloads.custom_case("step_shapes", B=4, Hq=Hq, Hkv=Hkv, D=D, block_size=bs,
+                              lens=[3, 200, 1000, 2500], seed=111)
+    g = to_gpu(c)
+    out, lse = _step(g, c, 256)
+    torch.cuda.synchronize()
+    want, want_lse, _, _ = _oracle_step(c)
+    check_fp16(out, want, f"step shapes {Hq}/{Hkv}/{D}/{bs}")
+    _check_lse(lse, want_lse)
+
+
+def test_step_in_hip_graph_replays():
+    """The step is capture-safe: replays of a captured step, with eager work
+    and synchronisation between them, all equal the eager result."""
+    c = case("sweep:32:1024")
+    P = 256
+    g = to_gpu(c)
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    out = torch.empty((c.B, c.Hq, c.D), dtype=torch.float16, device=g.q.device)
+    eager = _step(g, c, P, ws, want_lse=False).clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pkv.paged_decode_step(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale, P, k_new=g.k_new,
+                              v_new=g.v_new, slot_mapping=g.slots, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pkv.paged_decode_step(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale, P, k_new=g.k_new,
+                              v_new=g.v_new, slot_mapping=g.slots, workspace=ws, out=out)
+    for rep in range(4):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        assert int(ws.counters.abs().sum()) == 0
+        junk = torch.randn(1024, device=g.q.device).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        del junk
+
+
+@pytest.mark.parametrize("waves,subtiles,depth", [(1, 1, 2), (2, 2, 4), (4, 2, 2), (8, 4, 2),
+                                                  (4, 1, 4)])
+def test_step_launch_shapes(waves, subtiles, depth):
+    try:
+        pkv.set_launch_config("split", waves, subtiles, depth)
+        for name in ("qwen", "tiny"):
+            c = case(name)
+            g = to_gpu(c)
+            out = _step(g, c, 64 if name == "tiny" else 256, want_lse=False)
+            torch.cuda.synchronize()
+            want, _, _, _ = _oracle_step(c)
+            check_fp16(out, want, f"step {name} NW={waves} NS={subtiles} DEPTH={depth}")
+    finally:
+        pkv.set_launch_config("split", 0, 0, 0)
+
+
+def test_step_merge_stress_against_three_launch_path():
+    """40 fused steps with new queries each time; each must match the
+    append + split pass + split_reduce path (which has no cross-workgroup
+    hand-off) within fp16 tolerance.  A merge that read a stale partial would
+    be off by O(1)."""
+    c = case("sweep:32:1024")
+    P = 128
+    g = to_gpu(c)
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    gen = torch.Generator(device=g.q.device).manual_seed(5)
+    worst = 0.0
+    for it in range(40):
+        g.q = torch.randn(g.q.shape, generator=gen, device=g.q.device).to(torch.float16)
+        fused = _step(g, c, P, ws, want_lse=False)
+        po, pl = pkv.paged_attention_decode_split(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale,
+                                                  P)
+        ref3 = pkv.split_reduce(po, pl, g.ctx, P)
+        torch.cuda.synchronize()
+        worst = max(worst, (fused.float() - ref3.float()).abs().max().item())
+        assert int(ws.counters.abs().sum()) == 0
+    assert worst <= 2e-3, worst
