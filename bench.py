@@ -257,7 +257,10 @@ def run_headline(args):
     rot = Rotation(case, R, device)
     Pm = case.max_partitions(P)
     ws = pkv.StepWorkspace(B, case.Hq, case.Hkv, case.D, Pm, device)
-    po, pl = ws.partial_out, ws.partial_lse
+    # the three-launch path has its own partials (the step's workspace must
+    # keep its "not written" state between calls)
+    po = torch.empty_like(ws.partial_out)
+    pl = torch.empty_like(ws.partial_lse)
     out = torch.empty((B, case.Hq, case.D), dtype=torch.float16, device=device)
     if args.waves or args.subtiles or args.depth:
         pkv.set_launch_config("split", args.waves, args.subtiles, args.depth)
@@ -416,10 +419,12 @@ def run_sweep(args):
     points = [("sweep", B, c) for B in workloads.SWEEP_B for c in workloads.SWEEP_CTX]
     points += [("qwen", 8, 0), ("skewed", 256, 0)]
     points += [("long", B, c) for B, c in workloads.LONG_POINTS]
+    points += [("extra", B, c) for B, c in workloads.EXTRA_POINTS]
     lines = []
     for kind, B, c in points:
         case = (workloads.sweep_case(B, c) if kind == "sweep" else workloads.qwen_case()
                 if kind == "qwen" else workloads.skewed_case() if kind == "skewed"
+                else workloads.extra_case(B, c) if kind == "extra"
                 else workloads.long_case(B, c))
         kv = case.kv_bytes()
         R = max(2, math.ceil(4 * LLC_BYTES / kv))
@@ -445,7 +450,8 @@ def run_sweep(args):
                 continue
             Pm = case.max_partitions(P)
             ws = pkv.StepWorkspace(case.B, case.Hq, case.Hkv, case.D, Pm, device)
-            po, pl = ws.partial_out, ws.partial_lse
+            po = torch.empty_like(ws.partial_out)
+            pl = torch.empty_like(ws.partial_lse)
 
             def split(i):
                 pkv.paged_attention_decode_split(rot.q, rot.k_pool, rot.v_pool, rot.bt[i % R],
@@ -462,7 +468,7 @@ def run_sweep(args):
             if best_step is None or us < best_step[1]:
                 best_step = (P, us)
             del po, pl, ws
-        line = {"point": case.name, "B": case.B, "sum_ctx": ctx_sum,
+        line = {"point": case.name, "kind": kind, "B": case.B, "sum_ctx": ctx_sum,
                 "alg_bytes": nbytes, "rotation_sets": R,
                 "unsplit_us": round(us_unsplit, 3),
                 "unsplit_gbs": round(nbytes / us_unsplit / 1e3, 1),

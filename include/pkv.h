@@ -211,17 +211,27 @@ int paged_attention_decode_split(float* partial_out, float* partial_lse,
  *                     decode would.  Any other slot is still written, but
  *                     whether this step's attention sees the new value there
  *                     is undefined.
- *   partial_out, partial_lse  workspace as for paged_attention_decode_split.
+ *   partial_out       [B, num_q_heads, max_partitions, head_dim] fp32 and
+ *   partial_lse       [B, num_q_heads, max_partitions] fp32 workspace, every
+ *                     32-bit word all ones (0xFFFFFFFF) before the first call;
+ *                     every call leaves them so.  num_q_heads / num_kv_heads *
+ *                     max_partitions * head_dim * 4 must not exceed INT32_MAX
+ *                     (else PKV_ERR_UNSUPPORTED).  Not to be shared with
+ *                     paged_attention_decode_split, which leaves values there.
  *   counters          [B, num_kv_heads] int32 workspace: must be zero before
- *                     the first call; every call leaves it zero.  Calls that
- *                     share a counter workspace must be ordered by a stream.
+ *                     the first call; every call leaves it zero.
+ * Calls that share a workspace must be ordered by a stream; a call that
+ * faults or is aborted leaves it undefined (initialise it again).
  * Other arguments as for paged_attention_decode_split.
  *
  * Each (sequence, KV head) with more than one non-empty partition is merged
- * by the workgroup that finishes its last partition (an atomic counter with
- * release/acquire ordering; nothing waits on another workgroup).  A sequence
- * that fits one partition is written directly.  Results equal append +
- * split pass + split_reduce up to fp32 summation order.
+ * in the launch by one of its workgroups: each takes a ticket from the pair's
+ * counter early, the holder of the last ticket merges, and it reads the other
+ * partitions' rows once none of their words is all ones (device-coherent
+ * accesses; the others never wait).  It sets the rows it read back to all
+ * ones and the counter back to zero.  A sequence that fits one partition is
+ * written directly.  Results equal append + split pass + split_reduce up to
+ * fp32 summation order.
  */
 int paged_decode_step(void* out, float* lse_out,
                       void* k_pool, void* v_pool,

@@ -230,17 +230,25 @@ def split_reduce(partial_out, partial_lse, context_lens, partition_size, out=Non
 
 
 class StepWorkspace:
-    """Device workspace of paged_decode_step: split partials and the
-    per-(sequence, KV head) counters (zeroed here once; every call leaves them
-    zero).  Allocated with torch by the caller's code, never by the library."""
+    """Device workspace of paged_decode_step: split partials, every word all
+    ones (0xFFFFFFFF, "not written"), and the per-(sequence, KV head) ticket
+    counters, zero.  Set up here once; every call leaves it in that state.
+    Allocated with torch by the caller's code, never by the library.  reset()
+    restores the state (after an aborted call)."""
 
     def __init__(self, B, num_q_heads, num_kv_heads, head_dim, max_partitions, device):
         self.partial_out = torch.empty((B, num_q_heads, max_partitions, head_dim),
                                        dtype=torch.float32, device=device)
         self.partial_lse = torch.empty((B, num_q_heads, max_partitions), dtype=torch.float32,
                                        device=device)
-        self.counters = torch.zeros((B, num_kv_heads), dtype=torch.int32, device=device)
+        self.counters = torch.empty((B, num_kv_heads), dtype=torch.int32, device=device)
         self.max_partitions = max_partitions
+        self.reset()
+
+    def reset(self):
+        self.partial_out.view(torch.int32).fill_(-1)
+        self.partial_lse.view(torch.int32).fill_(-1)
+        self.counters.zero_()
 
 
 def paged_decode_step(q, k_pool, v_pool, block_tables, context_lens, scale, partition_size,

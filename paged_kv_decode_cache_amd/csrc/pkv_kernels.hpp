@@ -110,6 +110,44 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
 }
 
+// Device-coherent 16-byte and 4-byte accesses for the fused step's partials
+// (workgroups of one (sequence, KV head) may run on different XCDs, whose L2s
+// are not coherent with each other): raw buffer instructions with the sc1
+// cache-policy bit, which write through to, and read from, the device's
+// coherence point.  Buffer accesses are also range-checked by the hardware:
+// reads past the resource's end return 0, writes past it are dropped.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCoherent = 16;                 // sc1
+constexpr unsigned kUnwritten = 0xFFFFFFFFu;  // a partial word not written yet
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void store_coherent4(__amdgpu_buffer_rsrc_t rs, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, kCoherent);
+}
+__device__ __forceinline__ void store_coherent1(__amdgpu_buffer_rsrc_t rs, int off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), rs, off, 0, kCoherent);
+}
+// Loads return through a bit cast to a float vector: element reads straight
+// from the builtin's integer-vector result were narrowed to the wrong dword
+// by this compiler.
+__device__ __forceinline__ f32x4 load_coherent4(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCoherent));
+}
+__device__ __forceinline__ float load_coherent1(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kCoherent));
+}
+__device__ __forceinline__ bool is_written(float x) {
+  return __builtin_bit_cast(unsigned, x) != kUnwritten;
+}
+// A computed value never has the all-ones pattern (NaNs from fp16 inputs or
+// from invalid operations have other payloads); mapped to a quiet NaN anyway,
+// so a written word can never read as unwritten.
+__device__ __forceinline__ float as_written(float x) {
+  return is_written(x) ? x : __builtin_bit_cast(float, 0x7FC00000u);
+}
+
 // LDS bytes one wave uses: V staging during the loop, merge buffers after.
 template <int D, int NS>
 struct AttnSmem {
@@ -398,46 +436,86 @@ __device__ __forceinline__ void merge_waves_impl(const SoftmaxState<D>& st, floa
   }
 }
 
-// Cross-workgroup merge of the fused step, run by the workgroup that finished
-// the last partition of (b, kvh): threads cover (head, 4 dims) x partition
-// groups with a streaming LSE merge, and the groups combine through LDS.
+// Cross-workgroup merge of the fused step, run by the merging workgroup of
+// (b, kvh) once its own partition (p_own, held in LDS at `own`) is final.
+// Threads cover (head, 4 dims) x partition groups with a streaming LSE merge,
+// and the groups combine through LDS.  Every other partition's row is polled
+// until none of its words is still unwritten, then set back to unwritten for
+// the next launch (lse words after a barrier: all threads of a head read them).
+// The wait ends: the other workgroups of the pair took their tickets before
+// this one took the last, so they are running and wait on nothing.
 constexpr int kMergeSlots = 512;  // >= 16 heads x 128/4 dims
+constexpr int kSpinLimit = 1 << 20;
 
 template <int D, int NW>
-__device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int np,
+__device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int np, int p_own,
+                                      const float* own /* [16][D] o, then [16] lse */,
                                       float* msm /* 6 * kMergeSlots floats */) {
   constexpr int NT = NW * 64;
   constexpr int TPR = D / 4;
+  constexpr int BATCH = 4;  // rows in flight per thread
   const int t = threadIdx.x;
-  const int per_group = a.G * TPR;
+  const int G = a.G;
+  const int Pm = a.max_partitions;
+  const int per_group = G * TPR;
   const int ngroups = per_group <= NT ? NT / per_group : 1;
   const int nslots = per_group * ngroups;
+  const size_t head0 = (size_t)b * a.Hq + kvh * G;
+  const __amdgpu_buffer_rsrc_t po_rs = buffer_rsrc(a.partial_out + head0 * Pm * D, G * Pm * D * 4);
+  const __amdgpu_buffer_rsrc_t pl_rs = buffer_rsrc(a.partial_lse + head0 * Pm, G * Pm * 4);
+  f32x4 unwritten4;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) unwritten4[v] = __builtin_bit_cast(float, kUnwritten);
   for (int slot = t; slot < nslots; slot += NT) {
     const int grp = slot / per_group;
     const int hc = slot % per_group;
-    const int h = kvh * a.G + hc / TPR;
+    const int hh = hc / TPR;
     const int cc = hc % TPR;
-    const float* lse = a.partial_lse + ((size_t)b * a.Hq + h) * a.max_partitions;
-    const float* po = a.partial_out + ((size_t)b * a.Hq + h) * a.max_partitions * D + 4 * cc;
     float M = -INFINITY, L = 0.0f;
     f32x4 acc = zero4f();
-#pragma unroll 4
-    for (int q = grp; q < np; q += ngroups) {
-      const float l = __hip_atomic_load(lse + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      f32x4 x;
+    for (int q0 = grp; q0 < np; q0 += BATCH * ngroups) {
+      f32x4 x[BATCH];
+      float l[BATCH];
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        x[v] = __hip_atomic_load(po + (size_t)q * D + v, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-      if (l > M) {
-        const float sc = fast_exp2((M - l) * kLog2e);  // 0 from -inf
-        acc *= sc;
-        L *= sc;
-        M = l;
+      for (int j = 0; j < BATCH; ++j) {
+        const int q = q0 + j * ngroups;
+        if (q < np && q != p_own) {
+          x[j] = load_coherent4(po_rs, ((hh * Pm + q) * D + 4 * cc) * 4);
+          l[j] = load_coherent1(pl_rs, (hh * Pm + q) * 4);
+        }
       }
-      const float w = fast_exp2((l - M) * kLog2e);
-      acc += w * x;
-      L += w;
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const int q = q0 + j * ngroups;
+        if (q < np) {
+          if (q == p_own) {
+            x[j] = *reinterpret_cast<const f32x4*>(own + hh * D + 4 * cc);
+            l[j] = own[16 * D + hh];
+          } else {
+            const int xo = ((hh * Pm + q) * D + 4 * cc) * 4;
+            for (int spin = 0; spin < kSpinLimit; ++spin) {
+              if (is_written(x[j][0]) && is_written(x[j][1]) && is_written(x[j][2]) &&
+                  is_written(x[j][3]) && is_written(l[j]))
+                break;
+              __builtin_amdgcn_s_sleep(2);
+              asm volatile("" ::: "memory");
+              x[j] = load_coherent4(po_rs, xo);
+              l[j] = load_coherent1(pl_rs, (hh * Pm + q) * 4);
+            }
+            store_coherent4(po_rs, xo, unwritten4);
+          }
+          const float lq = l[j];
+          if (lq > M) {
+            const float sc = fast_exp2((M - lq) * kLog2e);  // 0 from -inf
+            acc *= sc;
+            L *= sc;
+            M = lq;
+          }
+          const float w = fast_exp2((lq - M) * kLog2e);
+          acc += w * x[j];
+          L += w;
+        }
+      }
     }
     float* r = msm + 6 * slot;
     r[0] = M;
@@ -448,6 +526,10 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
     r[5] = acc[3];
   }
   __syncthreads();
+  for (int i = t; i < G * np; i += NT) {
+    const int q = i % np;
+    if (q != p_own) store_coherent1(pl_rs, ((i / np) * Pm + q) * 4, __builtin_bit_cast(float, kUnwritten));
+  }
   for (int hc = t; hc < per_group; hc += NT) {
     float M = -INFINITY;
     for (int gi = 0; gi < ngroups; ++gi) M = fmaxf(M, msm[6 * (gi * per_group + hc)]);
@@ -478,8 +560,17 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
 // MODE 0: unsplit decode (one workgroup per (sequence, KV head), fp16 out).
 // MODE 1: split pass (one workgroup per partition, fp32 partials + lse).
 // MODE 2: fused decode step: the split pass plus, in the same launch, the
-//         step's cache write and the LSE merge by the last workgroup to
-//         finish a (sequence, KV head).
+//         step's cache write and the LSE merge of each (sequence, KV head)
+//         by one of its workgroups.
+//
+// Fused-step hand-off.  Each workgroup of a (b, kvh) with more than one
+// partition takes a ticket from the pair's counter early (its latency hides
+// under the K/V stream); the one holding the last ticket merges.  The others
+// store their partials with device-coherent stores and exit without waiting.
+// The merger keeps its own partial in LDS and polls the others' rows, which
+// hold an all-ones word until written (the merger sets them back after
+// reading, and resets the counter), so no store->flag->load round trips sit
+// on the kernel's tail.
 template <int D, int NS, int NW, int DEPTH, int MODE, bool DUAL>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
   constexpr int KC = D / 32;   // QK MFMAs (16x16x32) per subtile
@@ -622,6 +713,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
                                   spb_shift, lane);
     }
   }
+  // Fused step: the ticket (issued after the first K/V requests; waited for
+  // only at the end).
+  int ticket = 0;
+  if (STEP && n_parts > 1 && threadIdx.x == 0)
+    ticket = __hip_atomic_fetch_add(a.counters + (size_t)b * Hkv + kvh, 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
   for (int u0 = 0; u0 < n_tiles; u0 += DEPTH) {
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) {
@@ -664,6 +761,20 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
   // Weight sum of this lane's column: row 0, held by the quad-0 lane.
   const float l_tot = __shfl(st.lsum[0], g);
 
+  // Fused step: publish whether this workgroup merges (its ticket is the
+  // pair's last), before the barriers of the wave merge; the merger resets
+  // the counter at once (every ticket of this launch is taken).
+  __shared__ int s_merge;
+  __shared__ __attribute__((aligned(16))) float own[STEP ? 16 * D + 16 : 4];
+  if (STEP && n_parts > 1 && threadIdx.x == 0) {
+    const bool m = ticket == n_parts - 1;
+    if (m)
+      __hip_atomic_store(a.counters + (size_t)b * Hkv + kvh, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    s_merge = m;
+  }
+  if (NW == 1 && STEP) __syncthreads();
+
   // Final value for column block db of this lane's head.
   const bool emits = (DUAL ? g < 8 : true) && head_col < a.G;
   auto emit = [&](int db, f32x4 acc, float L, float M) {
@@ -675,19 +786,28 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
       f32x4 r;
 #pragma unroll
       for (int v = 0; v < 4; ++v) r[v] = acc[v] * inv;
-      float* dst = a.partial_out + (((size_t)b * a.Hq + h) * a.max_partitions + p) * D + d0;
-      float* lse_dst = a.partial_lse + ((size_t)b * a.Hq + h) * a.max_partitions + p;
       const float lse_v = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
       if (STEP) {
-        // device-coherent stores: the merging workgroup may run on another XCD
+        if (s_merge) {
+          *reinterpret_cast<f32x4*>(own + head_col * D + d0) = r;
+          if (db == 0 && quad == 0) own[16 * D + head_col] = lse_v;
+        } else {
+          const size_t head0 = (size_t)b * a.Hq + kvh * a.G;
+          const int Pm = a.max_partitions;
+          const __amdgpu_buffer_rsrc_t po_rs =
+              buffer_rsrc(a.partial_out + head0 * Pm * D, a.G * Pm * D * 4);
+          const __amdgpu_buffer_rsrc_t pl_rs = buffer_rsrc(a.partial_lse + head0 * Pm, a.G * Pm * 4);
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          __hip_atomic_store(dst + v, r[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (db == 0 && quad == 0)
-          __hip_atomic_store(lse_dst, lse_v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int v = 0; v < 4; ++v) r[v] = as_written(r[v]);
+          store_coherent4(po_rs, ((head_col * Pm + p) * D + d0) * 4, r);
+          if (db == 0 && quad == 0)
+            store_coherent1(pl_rs, (head_col * Pm + p) * 4, as_written(lse_v));
+        }
       } else {
+        float* dst = a.partial_out + (((size_t)b * a.Hq + h) * a.max_partitions + p) * D + d0;
         *reinterpret_cast<f32x4*>(dst) = r;
-        if (db == 0 && quad == 0) *lse_dst = lse_v;
+        if (db == 0 && quad == 0)
+          a.partial_lse[((size_t)b * a.Hq + h) * a.max_partitions + p] = lse_v;
       }
     } else {
       f16x4 r;
@@ -705,30 +825,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
   } else {
     merge_waves_impl<D, NW>(st, l_tot, smem, SM::kWaveBytes, wave, lane, emit);
   }
-  if (!STEP || n_parts <= 1) return;
-
-  // Fused step: count finished partitions of (b, kvh); the last one merges.
-  // Message passing through device-coherent accesses only: the partials were
-  // written with device-scope atomic stores, which are complete (s_waitcnt)
-  // on every wave before the barrier and the count's increment; the merging
-  // workgroup reads them with device-scope atomic loads.  No cache-wide
-  // write-back or invalidate (an acquire/release fence on gfx950 writes back
-  // and invalidates the whole L2 of the XCD, which costs more than the merge
-  // saves while other workgroups stream K/V through that L2).
-  __shared__ int s_last;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int* ctr = a.counters + (size_t)b * Hkv + kvh;
-    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = old == n_parts - 1;
-    if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = last;
-  }
-  __syncthreads();
-  if (!s_last) return;
+  if (!STEP || n_parts <= 1 || !s_merge) return;
+  __syncthreads();  // the merger's own partial is complete in LDS
   __shared__ float msm[6 * kMergeSlots];
-  merge_step_partitions<D, NW>(a, b, kvh, n_parts, msm);
+  merge_step_partitions<D, NW>(a, b, kvh, n_parts, p, own, msm);
 }
 
 // LSE-weighted merge of the valid partitions of one (sequence, query head).

@@ -26,6 +26,14 @@ def _oracle_step(c, seqs=None):
     return out, lse, kp, vp
 
 
+def _check_workspace_restored(ws):
+    """Every call leaves the partials all ones ("not written") and the
+    counters zero, ready for the next call."""
+    assert int(ws.counters.abs().sum()) == 0
+    assert bool((ws.partial_out.view(torch.int32) == -1).all())
+    assert bool((ws.partial_lse.view(torch.int32) == -1).all())
+
+
 def _check_lse(got, want, rows=None):
     g = host64(got)
     w = np.asarray(want)
@@ -53,7 +61,7 @@ def test_step_matches_append_then_decode(name, P):
     _check_lse(lse, want_lse)
     assert np.array_equal(g.k_pool.cpu().numpy().view(np.uint16), kp.view(np.uint16))
     assert np.array_equal(g.v_pool.cpu().numpy().view(np.uint16), vp.view(np.uint16))
-    assert int(ws.counters.abs().sum()) == 0
+    _check_workspace_restored(ws)
 
 
 @pytest.mark.parametrize("name", ["skewed", "long:4:131072"])
@@ -69,7 +77,7 @@ def test_step_full_size_sampled(name):
     want, want_lse, _, _ = _oracle_step(c, seqs=rows)
     check_fp16(out, want, f"step {name}", rows=rows)
     _check_lse(lse, want_lse, rows=rows)
-    assert int(ws.counters.abs().sum()) == 0
+    _check_workspace_restored(ws)
 
 
 def test_step_repeated_calls_reuse_counters():
@@ -94,7 +102,7 @@ def test_step_repeated_calls_reuse_counters():
         kp, vp = ref.kv_cache_append(c.k_pool, c.v_pool, c.k_new, c.v_new, c.slot_mapping)
         want2 = ref.paged_attention_decode(q2, kp, vp, c.block_tables, ctx2, c.scale)
         check_fp16(out2, want2, f"step call {k}")
-        assert int(ws.counters.abs().sum()) == 0
+        _check_workspace_restored(ws)
 
 
 def test_step_without_append_equals_decode():
@@ -159,7 +167,7 @@ def test_step_in_hip_graph_replays():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
-        assert int(ws.counters.abs().sum()) == 0
+        _check_workspace_restored(ws)
         junk = torch.randn(1024, device=g.q.device).sum()  # eager work between replays
         torch.cuda.synchronize()
         del junk
@@ -182,23 +190,31 @@ def test_step_launch_shapes(waves, subtiles, depth):
 
 
 def test_step_merge_stress_against_three_launch_path():
-    """40 fused steps with new queries each time; each must match the
-    append + split pass + split_reduce path (which has no cross-workgroup
-    hand-off) within fp16 tolerance.  A merge that read a stale partial would
-    be off by O(1)."""
+    """40 fused steps with new queries and new context lengths each time (so
+    the number of partitions per sequence changes between calls); each must
+    match the append + split pass + split_reduce path (which has no
+    cross-workgroup hand-off) within fp16 tolerance.  A merge that read a
+    stale or half-written partial would be off by O(1)."""
     c = case("sweep:32:1024")
     P = 128
     g = to_gpu(c)
     ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
     gen = torch.Generator(device=g.q.device).manual_seed(5)
+    cpu_gen = torch.Generator().manual_seed(6)
+    full = g.ctx.clone()
     worst = 0.0
     for it in range(40):
         g.q = torch.randn(g.q.shape, generator=gen, device=g.q.device).to(torch.float16)
-        fused = _step(g, c, P, ws, want_lse=False)
+        if it % 2:
+            g.ctx = torch.randint(0, 1025, (c.B,), generator=cpu_gen,
+                                  dtype=torch.int32).to(g.q.device)
+        else:
+            g.ctx = full
+        fused = _step(g, c, P, ws, append=False, want_lse=False)
         po, pl = pkv.paged_attention_decode_split(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale,
                                                   P)
         ref3 = pkv.split_reduce(po, pl, g.ctx, P)
         torch.cuda.synchronize()
         worst = max(worst, (fused.float() - ref3.float()).abs().max().item())
-        assert int(ws.counters.abs().sum()) == 0
+        _check_workspace_restored(ws)
     assert worst <= 2e-3, worst

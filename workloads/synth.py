@@ -199,6 +199,8 @@ def qwen_case(seed: int = 2000) -> DecodeCase:
 
 SWEEP_B = (1, 8, 32)
 SWEEP_CTX = (128, 512, 1024, 2048, 4096)
+# Larger points on the same head configuration (trend past the sweep's corner)
+EXTRA_POINTS = ((64, 4096), (128, 4096), (32, 8192), (64, 8192), (128, 8192), (32, 16384))
 
 
 def sweep_case(B: int, ctx: int, seed: Optional[int] = None,
@@ -212,6 +214,12 @@ def sweep_case(B: int, ctx: int, seed: Optional[int] = None,
     return make_case(f"sweep_B{B}_ctx{ctx}", B=B, Hq=14, Hkv=2, D=64,
                      block_size=16, lens=lens, num_blocks=nb, seed=seed, rng=rng,
                      partition_size=partition_size)
+
+
+def extra_case(B: int, ctx: int, partition_size: int = 512) -> DecodeCase:
+    """A point of EXTRA_POINTS: the sweep's shapes at a larger batch or context."""
+    seed = 3100 + EXTRA_POINTS.index((B, ctx))
+    return sweep_case(B, ctx, seed=seed, partition_size=partition_size)
 
 
 def skewed_lengths(rng, B=256, median=1024, sigma=1.0, lo=16, hi=32768):
