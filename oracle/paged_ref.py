@@ -30,6 +30,15 @@ What it computes, and where that comes from
   the natural-log log-sum-exp of its logits; the merge weights partition p by
   exp(lse_p - LSE).  The pages name the arm but not the merge; the LSE-weighted
   merge is the plainest exact reading.
+* Chunked prefill (Inference Engineering, Day 12 post on chunked prefill in
+  vLLM): a long prompt is split into chunks that are processed and written to
+  the cache one pass at a time, as a runtime optimisation only.  So a chunk's
+  token at position p attends to positions 0..p of its sequence (the cached
+  prefix and the chunk's earlier tokens), exactly as unchunked causal
+  attention over the whole prompt would.  A call carries, per sequence, the
+  chunk's n query rows; the chunk holds the last n of the sequence's
+  context_lens positions (its K/V already written), so row i sits at position
+  ctx - n + i.
 * Cache write: each step writes the new token's K and V into its slot of the
   pool (Inference Engineering, Day 11 post on how vLLM works: the executor
   updates the cache with the new key and value vectors).  Slots are addressed
@@ -63,6 +72,7 @@ __all__ = [
     "merge_partitions",
     "paged_attention_decode",
     "paged_attention_decode_split",
+    "paged_attention_prefill",
     "split_reduce",
     "kv_cache_append",
     "fp32_scale",
@@ -143,6 +153,41 @@ def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens,
             o, ls = attend(q[b, heads].astype(np.float64), K, V, sc)
             out[b, heads] = o
             lse[b, heads] = ls
+    return (out, lse) if return_lse else out
+
+
+def paged_attention_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start,
+                            scale, return_lse: bool = False, seqs=None):
+    """Chunked-prefill attention over the paged cache (plain definition, fp64).
+
+    q [total_q, Hq, D] fp16, rows query_start[b] .. query_start[b+1]-1 being
+    sequence b's chunk of n_b tokens; context_lens[b] counts the cached
+    positions including the chunk.  Row i of the chunk is at position
+    p = ctx_b - n_b + i and attends to positions 0..p (a row with p < 0, which
+    only a chunk longer than its context has, attends to nothing: zeros,
+    lse -inf).  Returns out [total_q, Hq, D] fp64 (and lse [total_q, Hq]).
+    ``seqs`` restricts the work to some sequences.
+    """
+    T, Hq, D = q.shape
+    _, bs, Hkv, _ = k_pool.shape
+    sc = fp32_scale(scale)
+    out = np.zeros((T, Hq, D))
+    lse = np.full((T, Hq), -np.inf)
+    B = len(context_lens)
+    for b in (range(B) if seqs is None else seqs):
+        r0, r1 = int(query_start[b]), int(query_start[b + 1])
+        n, ctx = r1 - r0, int(context_lens[b])
+        for kvh in range(Hkv):
+            heads = heads_of_kv_head(kvh, Hq, Hkv)
+            K = gather_sequence_kv(k_pool, block_tables[b], ctx, bs, kvh)
+            V = gather_sequence_kv(v_pool, block_tables[b], ctx, bs, kvh)
+            for i in range(n):
+                pos = ctx - n + i
+                if pos < 0:
+                    continue
+                o, ls = attend(q[r0 + i, heads].astype(np.float64), K[:pos + 1], V[:pos + 1], sc)
+                out[r0 + i, heads] = o
+                lse[r0 + i, heads] = ls
     return (out, lse) if return_lse else out
 
 

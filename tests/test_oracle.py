@@ -16,7 +16,7 @@ import scipy.special
 import torch
 
 from oracle import paged_ref as ref
-from workloads import custom_case, tiny_case
+from workloads import custom_case, prefill_case, tiny_case
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -394,11 +394,182 @@ def test_append_brute_force():
     pin_append_brute_force()
 
 
+# ---- chunked prefill attention --------------------------------------------
+
+def _chunk_sdpa(q_rows, K, V, ctx, scale, whole):
+    """torch fp64 SDPA for one sequence's chunk: q_rows [n, Hq, D] fp16, K/V
+    [ctx, Hkv, D] contiguous.  Row i sees keys t <= ctx - n + i: torch's own
+    is_causal when the chunk is the whole prompt (n == ctx), otherwise an
+    explicit boolean mask.  GQA is made explicit by repeating KV heads."""
+    n, Hq, D = q_rows.shape
+    G = Hq // K.shape[1]
+    Q = torch.from_numpy(q_rows.astype(np.float64)).permute(1, 0, 2).unsqueeze(0)
+    Kt = torch.from_numpy(K.astype(np.float64)).permute(1, 0, 2).repeat_interleave(G, 0)
+    Vt = torch.from_numpy(V.astype(np.float64)).permute(1, 0, 2).repeat_interleave(G, 0)
+    F = torch.nn.functional
+    if whole:
+        assert n == ctx
+        o = F.scaled_dot_product_attention(Q, Kt.unsqueeze(0), Vt.unsqueeze(0), is_causal=True,
+                                           scale=scale)
+    else:
+        rows = torch.arange(n).unsqueeze(1)
+        cols = torch.arange(ctx).unsqueeze(0)
+        mask = cols <= rows + (ctx - n)
+        o = F.scaled_dot_product_attention(Q, Kt.unsqueeze(0), Vt.unsqueeze(0), attn_mask=mask,
+                                           scale=scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+PREFILL_SHAPES = [
+    # (Hq, Hkv, D, bs, ctx, chunk)
+    (2, 1, 64, 16, [37, 5], [37, 5]),               # whole prompts
+    (14, 2, 64, 16, [100, 17, 64], [100, 17, 64]),
+    (14, 2, 64, 16, [100, 40, 64], [8, 40, 1]),     # chunks after a cached prefix
+    (32, 8, 128, 32, [70, 33], [16, 9]),
+    (4, 4, 64, 16, [50], [13]),
+]
+
+
+def pin_prefill_sdpa(idx: int):
+    Hq, Hkv, D, bs, ctx, chunk = PREFILL_SHAPES[idx]
+    rng = np.random.default_rng(300 + idx)
+    seqs_k = [rng.standard_normal((n, Hkv, D)).astype(np.float16) for n in ctx]
+    seqs_v = [rng.standard_normal((n, Hkv, D)).astype(np.float16) for n in ctx]
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    q = rng.standard_normal((int(qs[-1]), Hq, D)).astype(np.float16)
+    kp, vp, bt = _paged_from_contiguous(rng, seqs_k, seqs_v, bs)
+    scale = 1.0 / math.sqrt(D)
+    got = ref.paged_attention_prefill(q, kp, vp, bt, np.array(ctx, np.int32), qs, scale)
+    sc = float(torch.tensor(scale, dtype=torch.float32))
+    for b in range(len(ctx)):
+        want = _chunk_sdpa(q[qs[b]:qs[b + 1]], seqs_k[b], seqs_v[b], ctx[b], sc,
+                           whole=chunk[b] == ctx[b])
+        _close(got[qs[b]:qs[b + 1]], want, 1e-12)
+
+
+@pytest.mark.parametrize("idx", range(len(PREFILL_SHAPES)))
+def test_prefill_matches_torch_sdpa(idx):
+    pin_prefill_sdpa(idx)
+
+
+def pin_prefill_rows_are_decodes():
+    """Row i of a chunk equals a single-token decode of that query over the
+    first ctx - n + i + 1 positions (the decode oracle is pinned on its own)."""
+    c = prefill_case("rows", Hq=14, Hkv=2, D=64, block_size=16, ctx=[45, 130], chunk=[20, 7],
+                     seed=310)
+    got = ref.paged_attention_prefill(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens,
+                                      c.query_start, c.scale)
+    for b in range(c.B):
+        n = int(c.chunk_lens[b])
+        for i in range(n):
+            r = int(c.query_start[b]) + i
+            pos = int(c.context_lens[b]) - n + i
+            one = ref.paged_attention_decode(c.q[r:r + 1], c.k_pool, c.v_pool,
+                                             c.block_tables[b:b + 1],
+                                             np.array([pos + 1], np.int32), c.scale)
+            _close(got[r], one[0], 1e-12)
+
+
+def test_prefill_rows_are_decodes():
+    pin_prefill_rows_are_decodes()
+
+
+def pin_prefill_chunking_is_invisible():
+    """Chunked prefill is a runtime optimisation only (Inference Engineering,
+    Day 12): a prompt processed in chunks -- each call with the context
+    written so far -- gives the rows of the whole prompt in one call."""
+    c = prefill_case("chunks", Hq=14, Hkv=2, D=64, block_size=16, ctx=[96], chunk=[96],
+                     seed=320)
+    whole = ref.paged_attention_prefill(c.q, c.k_pool, c.v_pool, c.block_tables,
+                                        c.context_lens, c.query_start, c.scale)
+    for edges in ([0, 8, 16, 24, 96], [0, 50, 96], [0, 1, 95, 96]):
+        for a, e in zip(edges[:-1], edges[1:]):
+            part = ref.paged_attention_prefill(c.q[a:e], c.k_pool, c.v_pool, c.block_tables,
+                                               np.array([e], np.int32),
+                                               np.array([0, e - a], np.int32), c.scale)
+            assert np.array_equal(part, whole[a:e])
+
+
+def test_prefill_chunking_is_invisible():
+    pin_prefill_chunking_is_invisible()
+
+
+def _prefill_brute_force(c):
+    """Pure-Python loops with math.exp over the causal prefix of each row."""
+    T, Hq, D = c.q.shape
+    bs = c.block_size
+    sc = float(torch.tensor(c.scale, dtype=torch.float32))
+    out = np.zeros((T, Hq, D))
+    for b in range(c.B):
+        r0, r1 = int(c.query_start[b]), int(c.query_start[b + 1])
+        ctx = int(c.context_lens[b])
+        for r in range(r0, r1):
+            last = ctx - (r1 - r0) + (r - r0)
+            for h in range(Hq):
+                kvh = h * c.Hkv // Hq
+                logits = []
+                for t in range(last + 1):
+                    blk = int(c.block_tables[b][t // bs])
+                    krow = c.k_pool[blk][t % bs][kvh]
+                    logits.append(sc * sum(float(c.q[r][h][d]) * float(krow[d])
+                                           for d in range(D)))
+                if not logits:
+                    continue
+                big = max(logits)
+                ws = [math.exp(x - big) for x in logits]
+                tot = sum(ws)
+                for d in range(D):
+                    acc = 0.0
+                    for t in range(last + 1):
+                        blk = int(c.block_tables[b][t // bs])
+                        acc += ws[t] * float(c.v_pool[blk][t % bs][kvh][d])
+                    out[r][h][d] = acc / tot
+    return out
+
+
+def pin_prefill_brute_force():
+    c = prefill_case("pbf", Hq=4, Hkv=2, D=8, block_size=16, ctx=[19, 6, 3], chunk=[5, 6, 5],
+                     seed=330)
+    got = ref.paged_attention_prefill(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens,
+                                      c.query_start, c.scale)
+    _close(got, _prefill_brute_force(c), 1e-12)
+    # the chunk of 5 over a context of 3 has two rows before position 0: zeros
+    r0 = int(c.query_start[2])
+    assert np.all(got[r0:r0 + 2] == 0)
+
+
+def test_prefill_brute_force():
+    pin_prefill_brute_force()
+
+
+def pin_prefill_block_permutation():
+    c = prefill_case("pperm", Hq=14, Hkv=2, D=64, block_size=16, ctx=[77, 30], chunk=[12, 30],
+                     seed=340)
+    base = ref.paged_attention_prefill(c.q, c.k_pool, c.v_pool, c.block_tables,
+                                       c.context_lens, c.query_start, c.scale)
+    perm = np.random.default_rng(341).permutation(c.num_blocks)
+    kp = np.empty_like(c.k_pool)
+    vp = np.empty_like(c.v_pool)
+    kp[perm] = c.k_pool
+    vp[perm] = c.v_pool
+    bt = np.where(c.block_tables >= 0, perm[np.maximum(c.block_tables, 0)], -1).astype(np.int32)
+    moved = ref.paged_attention_prefill(c.q, kp, vp, bt, c.context_lens, c.query_start, c.scale)
+    assert np.array_equal(base, moved)
+    assert not np.isnan(base).any()
+
+
+def test_prefill_block_permutation():
+    pin_prefill_block_permutation()
+
+
 ALL_PINS = (
     [lambda i=i: pin_sdpa(i) for i in range(len(SDPA_SHAPES))]
     + [pin_block_permutation, pin_ctx1_is_v_row, pin_identical_keys_mean_v,
        pin_two_token_logistic, pin_merge_closed_forms, pin_gqa_equals_repeated_mha,
        pin_brute_force_tiny, pin_ctx0_zero, pin_chunked_prefill_golden,
-       pin_append_brute_force]
+       pin_append_brute_force, pin_prefill_rows_are_decodes,
+       pin_prefill_chunking_is_invisible, pin_prefill_brute_force,
+       pin_prefill_block_permutation]
+    + [lambda i=i: pin_prefill_sdpa(i) for i in range(len(PREFILL_SHAPES))]
     + [lambda i=i: pin_split_equals_unsplit(i) for i in range(len(SPLIT_SHAPES))]
 )

@@ -106,6 +106,39 @@ def _split_factory(kind):
     return split
 
 
+def _prefill_factory(kind):
+    """The prefill oracle with one planted mistake in its causal bookkeeping."""
+    def prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale,
+                return_lse=False, seqs=None):
+        T, Hq, D = q.shape
+        _, bs, Hkv, _ = k_pool.shape
+        sc = ref.fp32_scale(scale)
+        out = np.zeros((T, Hq, D))
+        lse = np.full((T, Hq), -np.inf)
+        B = len(context_lens)
+        n_first = int(query_start[1] - query_start[0]) if B else 0
+        for b in (range(B) if seqs is None else seqs):
+            r0, r1 = int(query_start[b]), int(query_start[b + 1])
+            if kind == "rows_by_equal_chunks":
+                r0, r1 = b * n_first, (b + 1) * n_first
+            n, ctx = r1 - r0, int(context_lens[b])
+            for kvh in range(Hkv):
+                heads = ref.heads_of_kv_head(kvh, Hq, Hkv)
+                K = ref.gather_sequence_kv(k_pool, block_tables[b], ctx, bs, kvh)
+                V = ref.gather_sequence_kv(v_pool, block_tables[b], ctx, bs, kvh)
+                for i in range(n):
+                    pos = i if kind == "top_left_causal" else ctx - n + i
+                    if pos < 0 or r0 + i >= T:
+                        continue
+                    end = {"excludes_itself": pos, "sees_next_token": pos + 2,
+                           "not_causal": ctx}.get(kind, pos + 1)
+                    o, ls = ref.attend(q[r0 + i, heads].astype(np.float64), K[:end], V[:end], sc)
+                    out[r0 + i, heads] = o
+                    lse[r0 + i, heads] = ls
+        return (out, lse) if return_lse else out
+    return prefill
+
+
 MUTANTS = {
     "gqa_modulo": ("kv_head_of", lambda h, Hq, Hkv: h % Hkv),
     "no_scale": ("attend", _attend_factory("no_scale")),
@@ -123,6 +156,12 @@ MUTANTS = {
     "append_no_skip": ("kv_cache_append", _append_no_skip),
     "split_lse_base2": ("paged_attention_decode_split", _split_factory("lse_log2")),
     "scale_not_fp32": ("fp32_scale", lambda s: float(s) * (1 + 1e-7)),
+    "prefill_excludes_itself": ("paged_attention_prefill", _prefill_factory("excludes_itself")),
+    "prefill_sees_next_token": ("paged_attention_prefill", _prefill_factory("sees_next_token")),
+    "prefill_not_causal": ("paged_attention_prefill", _prefill_factory("not_causal")),
+    "prefill_top_left_causal": ("paged_attention_prefill", _prefill_factory("top_left_causal")),
+    "prefill_rows_by_equal_chunks": ("paged_attention_prefill",
+                                     _prefill_factory("rows_by_equal_chunks")),
 }
 
 

@@ -268,3 +268,83 @@ def custom_case(name, *, B, Hq, Hkv, D, block_size, lens, seed, num_blocks=None,
                      lens=lens, num_blocks=num_blocks, seed=seed, rng=rng,
                      scale=scale, q_mult=q_mult, partition_size=partition_size,
                      max_blocks=max_blocks, poison=poison)
+
+
+# ---- chunked prefill -------------------------------------------------------
+
+@dataclass
+class PrefillCase:
+    """A chunk of new tokens per sequence over a paged cache.
+
+    Sequence b's chunk is rows query_start[b] .. query_start[b+1]-1 of q; it
+    holds the last n_b of the sequence's context_lens[b] positions.  k_pool /
+    v_pool hold every attended position including the chunk's; k_chunk /
+    v_chunk are the chunk's rows (what a multi-token append writes) and
+    chunk_slots their slots, so a test can poison those slots, append, then
+    attend."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    block_size: int
+    num_blocks: int
+    scale: float
+    context_lens: np.ndarray          # int32 [B]
+    query_start: np.ndarray           # int32 [B + 1]
+    block_tables: np.ndarray          # int32 [B, max_blocks_per_seq]
+    k_pool: np.ndarray                # fp16 [NB, bs, Hkv, D]
+    v_pool: np.ndarray
+    q: np.ndarray                     # fp16 [total_q, Hq, D]
+    k_chunk: np.ndarray               # fp16 [total_q, Hkv, D]
+    v_chunk: np.ndarray
+    chunk_slots: np.ndarray           # int64 [total_q]
+    seed: int = 0
+
+    @property
+    def total_q(self) -> int:
+        return int(self.query_start[-1])
+
+    @property
+    def chunk_lens(self) -> np.ndarray:
+        return np.diff(self.query_start).astype(np.int32)
+
+    @property
+    def max_q(self) -> int:
+        return int(self.chunk_lens.max()) if self.B else 0
+
+
+def prefill_case(name, *, Hq, Hkv, D, block_size, ctx, chunk, seed, q_mult=1.0,
+                 scale=None, num_blocks=None) -> PrefillCase:
+    """Pool and tables as ``custom_case`` for context lengths ``ctx``; then
+    ``chunk[b]`` query rows per sequence (drawn after everything else)."""
+    ctx = np.asarray(ctx, dtype=np.int32)
+    chunk = np.asarray(chunk, dtype=np.int32)
+    B = len(ctx)
+    base = custom_case(name, B=B, Hq=Hq, Hkv=Hkv, D=D, block_size=block_size, lens=ctx,
+                       seed=seed, q_mult=q_mult, scale=scale, num_blocks=num_blocks)
+    rng = np.random.default_rng(seed + 7919)
+    qs = np.zeros(B + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(chunk)
+    q = _normal16(rng, (int(qs[-1]), Hq, D))
+    if q_mult != 1.0:
+        q = (q.astype(np.float32) * np.float32(q_mult)).astype(np.float16)
+    slots = []
+    for b in range(B):
+        for i in range(int(chunk[b])):
+            pos = int(ctx[b]) - int(chunk[b]) + i
+            if pos < 0:
+                slots.append(-1)
+            else:
+                slots.append(int(base.block_tables[b, pos // block_size]) * block_size
+                             + pos % block_size)
+    slots = np.asarray(slots, dtype=np.int64)
+    blk = np.where(slots >= 0, slots // block_size, 0)
+    off = np.where(slots >= 0, slots % block_size, 0)
+    k_chunk = base.k_pool[blk, off].copy()
+    v_chunk = base.v_pool[blk, off].copy()
+    return PrefillCase(name=name, B=B, Hq=Hq, Hkv=Hkv, D=D, block_size=block_size,
+                       num_blocks=base.num_blocks, scale=base.scale, context_lens=ctx,
+                       query_start=qs, block_tables=base.block_tables, k_pool=base.k_pool,
+                       v_pool=base.v_pool, q=q, k_chunk=k_chunk, v_chunk=v_chunk,
+                       chunk_slots=slots, seed=seed)
