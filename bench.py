@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--sweep", default="", help="write the full sweep as JSON lines to this file")
     ap.add_argument("--path", choices=("step", "split"), default="step",
                     help="step: fused paged_decode_step; split: append + split pass + merge")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time chunked-prefill attention instead (uses --batch, --ctx, --chunk)")
+    ap.add_argument("--chunk", type=int, default=512, help="prefill chunk length (tokens)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 20 plain device copies of MIB MiB (a known-size "
                          "reference for HBM traffic counters)")
@@ -407,6 +410,107 @@ def run_headline(args):
     return res
 
 
+PREFILL_METRIC = "chunked prefill attention: achieved TFLOP/s (% of fp16 MFMA peak) and µs/call"
+PEAK_FP16_TFLOPS = 2500.0
+
+
+def prefill_flops(case):
+    """Useful flops of a chunked-prefill call: q.K and p.V over each row's
+    causal prefix (2 flops per multiply-add, 2 products per position)."""
+    total = 0
+    for b in range(case.B):
+        n = int(case.chunk_lens[b])
+        ctx = int(case.context_lens[b])
+        first = max(0, ctx - n)          # positions of the chunk rows, +1 each
+        seen = sum(p + 1 for p in range(first, ctx))
+        total += seen
+    return 4 * case.Hq * case.D * total
+
+
+def run_prefill(args):
+    """Chunked prefill: B sequences, each a `--chunk`-token chunk ending at
+    position ctx - 1 (Hq=14, Hkv=2, D=64, bs=16).  The kernel is bound by
+    MFMA/VALU issue, not HBM (~3000 flop per K/V byte at 512-row chunks), so
+    the K/V set (16.8 MB at B=8, ctx=4096) is not rotated."""
+    import torch
+    import paged_kv_decode_cache_amd as pkv
+    import workloads
+
+    device = torch.device("cuda:0")
+    B, ctx, n = args.batch, args.ctx, args.chunk
+    case = workloads.prefill_case(f"prefill_B{B}_ctx{ctx}_chunk{n}", Hq=14, Hkv=2, D=64,
+                                  block_size=16, ctx=[ctx] * B, chunk=[n] * B, seed=6000)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    q, kp, vp = t(case.q), t(case.k_pool), t(case.v_pool)
+    bt, cl, qs = t(case.block_tables), t(case.context_lens), t(case.query_start)
+    out = torch.empty_like(q)
+
+    def call(_i):
+        pkv.paged_attention_prefill(q, kp, vp, bt, cl, qs, case.scale, case.max_q, out=out)
+
+    t0 = time.perf_counter()
+    i = 0
+    while i < args.warmup or time.perf_counter() - t0 < 0.2:
+        call(i)
+        i += 1
+    torch.cuda.synchronize()
+    R = 16
+    us = time_graph(capture([lambda r=r: call(r) for r in range(R)]), R, args.steps)
+    flops = prefill_flops(case)
+    # the library gives launches with fewer workgroups than CUs 8 waves each
+    rows_per_wg = 16 * 4 // (case.Hq // case.Hkv)
+    grid = case.B * case.Hkv * -(-case.max_q // rows_per_wg)
+    nw = 8 if grid < 256 else 4
+    kv = case.B * ctx * case.Hkv * case.D * 4
+    qo = case.total_q * case.Hq * case.D * 4
+    tflops = flops / (us * 1e-6) / 1e12
+    res = {
+        "metric": PREFILL_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us * 1e-3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"chunked prefill: {B} sequences x {n}-token chunk ending at "
+                               f"position {ctx - 1} (Hq=14, Hkv=2, D=64, block_size=16)",
+                   "B": B, "ctx": ctx, "chunk": n, "useful_flops_per_call": flops,
+                   "kv_bytes_per_call": kv, "q_out_bytes_per_call": qo,
+                   "launch": "HIP graph of 16 calls, replayed", "accumulate": "fp32"},
+        "us_per_call": round(us, 3),
+        "roofline": {"bound": "mfma", "kernel": f"pkv::prefill_kernel<64, 4, {nw}, 2>",
+                     "achieved": round(tflops, 2), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
+                     "traffic": None, "kernel_us": round(us, 3),
+                     "hbm_gbs_on_kv_and_q_out": round((kv + qo) / (us * 1e-6) / 1e9, 1)},
+    }
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_limits
+        from oracle import paged_ref as ref
+        rows = min(n, 32)
+        sub_qs = np.array([0, rows], dtype=np.int32)
+        q1 = case.q[int(case.query_start[0]):int(case.query_start[0]) + rows]
+        ctx1 = np.array([ctx - n + rows], dtype=np.int32)   # the chunk's first rows
+        sub = workloads.PrefillCase(case.name, 1, case.Hq, case.Hkv, case.D, case.block_size,
+                                    case.num_blocks, case.scale, ctx1, sub_qs,
+                                    case.block_tables[:1], case.k_pool, case.v_pool, q1,
+                                    case.k_chunk[:rows], case.v_chunk[:rows],
+                                    case.chunk_slots[:rows])
+        done = 0
+        t0 = time.perf_counter()
+        with threadpool_limits(limits=1):
+            while True:
+                ref.paged_attention_prefill(q1, case.k_pool, case.v_pool, case.block_tables[:1],
+                                            ctx1, sub_qs, case.scale)
+                done += 1
+                if time.perf_counter() - t0 >= args.cpu_seconds:
+                    break
+        dt = time.perf_counter() - t0
+        cpu = prefill_flops(sub) * done / dt / 1e12
+        res["cpu_baseline"] = {
+            "value": round(cpu, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle paged_attention_prefill on the first {rows} rows of one "
+                      f"sequence's chunk x {done} repeats in {dt:.1f} s, fp64, one thread"}
+    return res
+
+
 def run_sweep(args):
     """Every batch x context point plus the other workloads: unsplit and split
     timings (rotated over >= 4x LLC of K/V), one JSON line per point."""
@@ -498,6 +602,11 @@ def main():
         sys.exit(1)
     if args.sweep:
         run_sweep(args)
+        return
+    if args.prefill:
+        if args.batch == 32 and args.ctx == 4096 and "--batch" not in sys.argv:
+            args.batch = 8
+        print(json.dumps(run_prefill(args)), flush=True)
         return
     print(json.dumps(run_headline(args)), flush=True)
 

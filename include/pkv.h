@@ -245,6 +245,39 @@ int paged_decode_step(void* out, float* lse_out,
                       int32_t max_partitions, float scale, void* stream);
 
 /*
+ * paged_attention_prefill -- attention of a chunk of new tokens per sequence
+ * over the paged cache (chunked prefill: Inference Engineering, Day 12 post
+ * on chunked prefill in vLLM, where a long prompt is processed a chunk per
+ * pass and each pass writes its K/V into the cache).  Sequence b's chunk is
+ * rows query_start[b] .. query_start[b+1]-1 of q (n_b rows); it holds the last
+ * n_b of the sequence's context_lens[b] positions, whose K/V must already be
+ * in the pools (kv_cache_append with one slot per chunk token).  Row i of the
+ * chunk, at position p = context_lens[b] - n_b + i, gets
+ *
+ *   out[row, h, :] = softmax_t(scale * q[row, h] . K_t) V_t  over t = 0..p,
+ *
+ * which is what unchunked causal attention over the whole prompt gives that
+ * position.  A row with p < 0 (a chunk longer than its context) gets zeros.
+ * A one-row chunk is a decode step.
+ *
+ *   out            [total_q, num_q_heads, head_dim] fp16 (16-byte aligned).
+ *   q              [total_q, num_q_heads, head_dim] fp16, total_q =
+ *                  query_start[B].
+ *   query_start    [B + 1] int32, non-decreasing, query_start[0] = 0.
+ *   max_query_len  >= every n_b (sizes the grid; rows of a longer chunk past
+ *                  this bound are not written).  0 makes the call a no-op.
+ * Other arguments, ranges and device-data guards as for
+ * paged_attention_decode.
+ */
+int paged_attention_prefill(void* out, const void* q,
+                            const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            const int32_t* query_start, int32_t B, int32_t max_query_len,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks,
+                            int32_t max_blocks_per_seq, float scale, void* stream);
+
+/*
  * split_reduce -- merge the partitions written by
  * paged_attention_decode_split.  With n = ceil(context_lens[b] /
  * partition_size) valid partitions of (b, h):

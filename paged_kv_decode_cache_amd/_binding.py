@@ -41,6 +41,8 @@ _SIGNATURES = {
     "split_reduce": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "paged_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "paged_attention_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                               _I, _I, _I, _F, _P]),
 }
 
 _lib = None
@@ -171,6 +173,40 @@ def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, scale,
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
         B, Hq, Hkv, D, bs, NB, maxb, float(scale), _stream(dev, stream))
     _raise(rc, "paged_attention_decode")
+    return out
+
+
+def paged_attention_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale,
+                            max_query_len, out=None, stream=None):
+    """Chunked-prefill attention: q and out are [total_q, Hq, D]; sequence b's
+    chunk is rows query_start[b] .. query_start[b+1]-1 (int32 [B + 1] on the
+    GPU), the last rows of its context_lens[b] positions, attended causally.
+    max_query_len bounds every chunk length (it sizes the launch; the binding
+    does not read device data to find it)."""
+    _need(q, "q", torch.float16, 3)
+    dev = q.device
+    _need(k_pool, "k_pool", torch.float16, 4, dev)
+    _need(v_pool, "v_pool", torch.float16, 4, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    _need(query_start, "query_start", torch.int32, 1, dev)
+    T, Hq, D = q.shape
+    NB, bs, Hkv, D2 = k_pool.shape
+    B = context_lens.shape[0]
+    if v_pool.shape != k_pool.shape or D2 != D:
+        raise ValueError("pools must be [num_blocks, block_size, Hkv, D] with q's D")
+    if block_tables.shape[0] != B or query_start.shape != (B + 1,):
+        raise ValueError("block_tables must be [B, max_blocks] and query_start [B + 1]")
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.float16, device=dev)
+    _need(out, "out", torch.float16, 3, dev)
+    if out.shape != (T, Hq, D):
+        raise ValueError("out must have q's shape")
+    rc = load_library().paged_attention_prefill(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
+        _ptr(query_start), B, int(max_query_len), Hq, Hkv, D, bs, NB, block_tables.shape[1],
+        float(scale), _stream(dev, stream))
+    _raise(rc, "paged_attention_prefill")
     return out
 
 

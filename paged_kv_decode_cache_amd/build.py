@@ -12,7 +12,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
 SOURCES = [os.path.join(CSRC, "pkv_api.hip")]
-DEPS = SOURCES + [os.path.join(CSRC, "pkv_kernels.hpp"), os.path.join(INCLUDE, "pkv.h")]
+DEPS = SOURCES + [os.path.join(CSRC, "pkv_kernels.hpp"), os.path.join(CSRC, "pkv_prefill.hpp"),
+                  os.path.join(INCLUDE, "pkv.h")]
 # Measurement aid used by bench.py only (streaming-read bandwidth probe).
 PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "probe_read.hip")]

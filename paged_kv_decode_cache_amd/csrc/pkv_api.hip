@@ -9,6 +9,7 @@
 
 #include "pkv.h"
 #include "pkv_kernels.hpp"
+#include "pkv_prefill.hpp"
 
 namespace {
 
@@ -136,6 +137,26 @@ int check_attn_common(const void* q, const void* k_pool, const void* v_pool,
   if (!aligned(q, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return PKV_ERR_INVALID_ARG;
   return PKV_OK;
+}
+
+// Chunked prefill: NCT column tiles of 16 (query row, head) pairs; fewer at
+// head_dim 128 (register budget of the accumulators).  A launch with fewer
+// workgroups than the chip has CUs (short chunks, few sequences) gives each
+// 8 waves, so each streams its context in half the time; larger launches
+// use 4 (measured on MI355X: 56 vs 78 us at 8 x 64-row chunks over 4K
+// contexts, 186 vs 201 us at 8 x 512).
+constexpr int kComputeUnits = 256;
+
+template <int D>
+int launch_prefill(const pkv::PrefillParams& p, int64_t grid, hipStream_t st) {
+  constexpr int NCT = D == 64 ? 4 : 2;
+  if (grid < kComputeUnits)
+    hipLaunchKernelGGL((pkv::prefill_kernel<D, NCT, 8, 2>), dim3((unsigned)grid), dim3(512), 0,
+                       st, p);
+  else
+    hipLaunchKernelGGL((pkv::prefill_kernel<D, NCT, 4, 2>), dim3((unsigned)grid), dim3(256), 0,
+                       st, p);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -340,6 +361,48 @@ int paged_decode_step(void* out, float* lse_out, void* k_pool, void* v_pool, con
   p.spb_shift = spb_shift_of(block_size);
   p.scale_log2 = scale * pkv::kLog2e;
   return launch_attn<2>(p, head_dim, grid, static_cast<hipStream_t>(stream));
+}
+
+int paged_attention_prefill(void* out, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            const int32_t* query_start, int32_t B, int32_t max_query_len,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                            float scale, void* stream) {
+  int rc = check_attn_common(q, k_pool, v_pool, block_tables, context_lens, B, num_q_heads,
+                             num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                             scale);
+  if (rc != PKV_OK) return rc;
+  if (max_query_len < 0) return PKV_ERR_INVALID_ARG;
+  if (B == 0 || max_query_len == 0) return PKV_OK;
+  if (!out || !query_start || !aligned(out, 16) || !aligned(query_start, 4))
+    return PKV_ERR_INVALID_ARG;
+  const int G = num_q_heads / num_kv_heads;
+  const int rows = pkv::prefill_rows_per_tile(head_dim == 64 ? 4 : 2, G);
+  const int64_t q_tiles = (max_query_len + rows - 1) / rows;
+  const int64_t grid = (int64_t)B * num_kv_heads * q_tiles;
+  if (grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
+
+  pkv::PrefillParams p = {};
+  p.a.q = static_cast<const pkv::f16*>(q);
+  p.a.k_pool = static_cast<const pkv::f16*>(k_pool);
+  p.a.v_pool = static_cast<const pkv::f16*>(v_pool);
+  p.a.block_tables = block_tables;
+  p.a.context_lens = context_lens;
+  p.a.out = static_cast<pkv::f16*>(out);
+  p.a.Hq = num_q_heads;
+  p.a.Hkv = num_kv_heads;
+  p.a.G = G;
+  p.a.block_size = block_size;
+  p.a.num_blocks = num_blocks;
+  p.a.max_blocks = max_blocks_per_seq;
+  p.a.spb_shift = spb_shift_of(block_size);
+  p.a.scale_log2 = scale * pkv::kLog2e;
+  p.query_start = query_start;
+  p.max_q = max_query_len;
+  p.q_tiles = (int32_t)q_tiles;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return head_dim == 64 ? launch_prefill<64>(p, grid, st) : launch_prefill<128>(p, grid, st);
 }
 
 int split_reduce(void* out, float* lse_out, const float* partial_out, const float* partial_lse,

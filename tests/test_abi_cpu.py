@@ -26,7 +26,8 @@ def test_library_exports_every_declared_symbol():
     lib = pkv.load_library()
     names = pkv.declared_functions()
     for expected in ("kv_cache_append", "paged_attention_decode",
-                     "paged_attention_decode_split", "split_reduce", "pkv_status_string"):
+                     "paged_attention_decode_split", "split_reduce", "paged_decode_step",
+                     "paged_attention_prefill", "pkv_status_string"):
         assert expected in names
     for name in names:
         assert hasattr(lib, name), f"libpkv.so does not export {name}"
@@ -180,6 +181,40 @@ def test_append_rejects(name, kw, code):
 @host_only
 def test_append_zero_tokens_is_noop():
     assert _append(pkv.load_library(), N=0) == 0
+
+
+def _prefill(lib, **kw):
+    a = dict(out=A16, q=B16, k=C16, v=D16, bt=E16, ctx=F16, qs=F16 + 0x1000, B=2, maxq=8, Hq=14,
+             Hkv=2, D=64, bs=16, NB=10, maxb=4, scale=0.125)
+    a.update(kw)
+    return lib.paged_attention_prefill(a["out"], a["q"], a["k"], a["v"], a["bt"], a["ctx"],
+                                       a["qs"], a["B"], a["maxq"], a["Hq"], a["Hkv"], a["D"],
+                                       a["bs"], a["NB"], a["maxb"], a["scale"], None)
+
+
+PREFILL_BAD = [
+    ("null out", dict(out=None), -1),
+    ("null query_start", dict(qs=None), -1),
+    ("misaligned query_start", dict(qs=F16 + 0x1002), -1),
+    ("misaligned out", dict(out=A16 + 4), -1),
+    ("negative max_query_len", dict(maxq=-1), -1),
+    ("nan scale", dict(scale=math.nan), -1),
+    ("head dim 96", dict(D=96), -2),
+    ("group of 32", dict(Hq=64, Hkv=2), -2),
+]
+
+
+@host_only
+@pytest.mark.parametrize("name,kw,code", PREFILL_BAD, ids=[d[0] for d in PREFILL_BAD])
+def test_prefill_rejects(name, kw, code):
+    assert _prefill(pkv.load_library(), **kw) == code
+
+
+@host_only
+def test_prefill_empty_is_noop():
+    lib = pkv.load_library()
+    assert _prefill(lib, B=0) == 0
+    assert _prefill(lib, maxq=0) == 0
 
 
 def test_binding_rejects_cpu_tensors():
