@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--prefill", action="store_true",
                     help="time chunked-prefill attention instead (uses --batch, --ctx, --chunk)")
     ap.add_argument("--chunk", type=int, default=512, help="prefill chunk length (tokens)")
+    ap.add_argument("--allocator", action="store_true",
+                    help="time the host block allocator (no GPU needed)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 20 plain device copies of MIB MiB (a known-size "
                          "reference for HBM traffic counters)")
@@ -511,6 +513,56 @@ def run_prefill(args):
     return res
 
 
+def run_allocator(args):
+    """Host block allocator (C ABI, host memory): µs per decode-step build for
+    256 sequences (each grows by one token; slots, tables of width 256 and
+    lengths written out) and per prefill build (256 chunks of 16 tokens),
+    with the plain-Python reference model timed on the same operations."""
+    import paged_kv_decode_cache_amd as pkv
+    from oracle.block_alloc_ref import BlockAllocatorRef
+
+    B, W, bs = 256, 256, 16
+    NB = B * W
+    seqs = list(range(B))
+
+    def drive(alloc, decode, prefill, free, steps):
+        t_dec = t_pre = 0.0
+        n_dec = n_pre = 0
+        for i in range(steps):
+            if i % 200 == 0:                 # restart every sequence with a chunk
+                for s in seqs:
+                    free(s)
+                t0 = time.perf_counter()
+                prefill(seqs, [16] * B, W)
+                t_pre += time.perf_counter() - t0
+                n_pre += 1
+            t0 = time.perf_counter()
+            decode(seqs, W)
+            t_dec += time.perf_counter() - t0
+            n_dec += 1
+        return t_dec / n_dec * 1e6, t_pre / n_pre * 1e6
+
+    lib = pkv.BlockAllocator(NB, bs, B, W)
+    lib_dec, lib_pre = drive(lib, lib.decode_batch, lib.prefill_batch, lib.free, args.steps * 4)
+    m = BlockAllocatorRef(NB, bs, B, W)
+    ref_dec, ref_pre = drive(m, m.decode_batch, m.prefill_batch, m.free_seq, 400)
+    return {
+        "metric": "host block allocator: µs per decode-step build", "value": round(lib_dec, 3),
+        "unit": "µs", "n_gpus": 0, "steps": args.steps * 4, "warmup": 0,
+        "ms_per_step": round(lib_dec * 1e-3, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32/int64", "data": "synthetic",
+        "config": {"workload": f"{B} sequences grown one token per step, tables of width {W} "
+                               f"(block_size {bs}); every 200 steps all restart with a "
+                               f"16-token chunk", "B": B, "width": W, "block_size": bs},
+        "prefill_build_us": round(lib_pre, 3),
+        "roofline": None,
+        "cpu_baseline": {"value": round(ref_dec, 3), "unit": "µs", "cores": 1,
+                         "kind": "oracle",
+                         "sample": f"plain-Python reference model, 400 decode builds; "
+                                   f"prefill build {ref_pre:.1f} µs"},
+    }
+
+
 def run_sweep(args):
     """Every batch x context point plus the other workloads: unsplit and split
     timings (rotated over >= 4x LLC of K/V), one JSON line per point."""
@@ -596,6 +648,9 @@ def main():
                                    "needs no collective, see DESIGN.md for how it would shard",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.allocator:
+        print(json.dumps(run_allocator(args)), flush=True)
+        return
     import torch
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))

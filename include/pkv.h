@@ -13,6 +13,11 @@
  *                                 split), writing per-partition results
  *   split_reduce                  log-sum-exp weighted merge of the partitions
  *   paged_decode_step             append + split pass + merge in one launch
+ *   paged_attention_prefill       a chunk of new tokens per sequence attending
+ *                                 causally over the cache (chunked prefill)
+ *
+ * plus a host-side block allocator (pkv_allocator_*) that hands out the
+ * cache's blocks and builds block tables and slot mappings for a batch.
  *
  * Sources (the pages describing the method):
  *   - nanoserve project write-up, section "What I built": a paged KV cache
@@ -22,7 +27,9 @@
  *     ("flash-decoding style") decode arm next to the plain one.
  *   - Inference Engineering, Day 11 post (how vLLM works): every step writes
  *     the new key and value vectors into the cache, whose fixed-size blocks
- *     are handed out per request through a block table.
+ *     are handed out per request from a free-block queue on the host.
+ *   - Inference Engineering, Day 12 post (chunked prefill): a long prompt is
+ *     processed, and written to the cache, a chunk per pass.
  * The pages give no signatures, layouts or merge rule; the choices below are
  * this library's and are the plainest reading of the pages.
  *
@@ -74,7 +81,9 @@ enum {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, ...   */
   PKV_ERR_UNSUPPORTED = -2, /* head_dim / block_size / group not compiled  */
-  PKV_ERR_LAUNCH = -3       /* HIP reported an error for the launch        */
+  PKV_ERR_LAUNCH = -3,      /* HIP reported an error for the launch        */
+  PKV_ERR_NO_SPACE = -4     /* allocator: not enough free blocks, or a
+                               sequence would pass max_blocks_per_seq      */
 };
 
 /* Static, human-readable name of a status code. */
@@ -299,6 +308,74 @@ int split_reduce(void* out, float* lse_out,
                  const int32_t* context_lens,
                  int32_t B, int32_t num_q_heads, int32_t head_dim,
                  int32_t partition_size, int32_t max_partitions, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host block allocator (host memory only; no GPU call).
+ *
+ * The cache's num_blocks blocks are handed out on demand from a FIFO queue of
+ * free block ids kept on the host (Inference Engineering, Day 11 post on
+ * vLLM: the KV cache manager takes a free block from its free-block queue
+ * when a request needs more space).  Each sequence id in [0, max_seqs) owns a
+ * block table of at most max_blocks_per_seq blocks and holds exactly
+ * ceil(len / block_size) blocks for its len tokens, so the memory it wastes
+ * is less than one block (nanoserve write-up, "What I built": the paged
+ * cache's waste is bounded by one block per sequence).  The queue starts as
+ * 0, 1, ..., num_blocks - 1; a freed sequence's blocks go to its back in
+ * table order.  Token position t of a sequence has slot
+ * table[t / block_size] * block_size + t % block_size, the slot_mapping value
+ * kv_cache_append takes.
+ *
+ * Ownership: pkv_allocator_create allocates the handle (its only allocation)
+ * and pkv_allocator_destroy frees it.  All output arrays are caller-owned
+ * host memory.  A handle is not thread-safe; separate handles are
+ * independent.  Calls that fail return a negative status and change nothing.
+ * ------------------------------------------------------------------------ */
+typedef struct pkv_block_allocator pkv_block_allocator;
+
+/* New allocator, or NULL for a non-positive argument or out of memory. */
+pkv_block_allocator* pkv_allocator_create(int32_t num_blocks, int32_t block_size,
+                                          int32_t max_seqs, int32_t max_blocks_per_seq);
+void pkv_allocator_destroy(pkv_block_allocator* a);
+
+/* Blocks in the free queue (or PKV_ERR_INVALID_ARG for a NULL handle). */
+int32_t pkv_allocator_num_free(const pkv_block_allocator* a);
+
+/* Tokens sequence `seq` holds (or PKV_ERR_INVALID_ARG). */
+int32_t pkv_allocator_context_len(const pkv_block_allocator* a, int32_t seq);
+
+/* Grow `seq` by num_tokens positions, taking blocks from the queue as needed;
+ * writes the new positions' slots to slot_mapping[0 .. num_tokens).
+ * PKV_ERR_NO_SPACE if the queue or the sequence's table cannot hold them. */
+int pkv_allocator_append_slots(pkv_block_allocator* a, int32_t seq, int32_t num_tokens,
+                               int64_t* slot_mapping);
+
+/* Return every block of `seq` to the queue; its length becomes 0. */
+int pkv_allocator_free_seq(pkv_block_allocator* a, int32_t seq);
+
+/* Copy `seq`'s block table into row[0 .. width), padded with -1;
+ * PKV_ERR_INVALID_ARG if width is below the blocks it holds. */
+int pkv_allocator_block_table(const pkv_block_allocator* a, int32_t seq, int32_t* row,
+                              int32_t width);
+
+/* One decode step for B distinct sequences: each grows by one token (its
+ * slot in slot_mapping[b]); block_tables [B, width] and context_lens [B]
+ * receive the tables and lengths after the growth, ready for
+ * kv_cache_append + paged_attention_decode / paged_decode_step.  All or
+ * nothing: PKV_ERR_NO_SPACE if the batch does not fit, PKV_ERR_INVALID_ARG
+ * for a repeated or out-of-range id or a width below a table's blocks. */
+int pkv_allocator_build_decode_batch(pkv_block_allocator* a, const int32_t* seqs, int32_t B,
+                                     int32_t width, int64_t* slot_mapping,
+                                     int32_t* block_tables, int32_t* context_lens);
+
+/* One chunked-prefill pass: sequence seqs[b] grows by chunk_lens[b] tokens.
+ * query_start [B + 1] receives the chunks' row offsets, slot_mapping
+ * [query_start[B]] the chunk tokens' slots in row order, block_tables
+ * [B, width] and context_lens [B] the state after the growth: the inputs of
+ * kv_cache_append + paged_attention_prefill.  All or nothing, as above. */
+int pkv_allocator_build_prefill_batch(pkv_block_allocator* a, const int32_t* seqs,
+                                      const int32_t* chunk_lens, int32_t B, int32_t width,
+                                      int32_t* query_start, int64_t* slot_mapping,
+                                      int32_t* block_tables, int32_t* context_lens);
 
 #ifdef __cplusplus
 }

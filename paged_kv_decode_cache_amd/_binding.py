@@ -23,6 +23,11 @@ PKV_OK = 0
 PKV_ERR_INVALID_ARG = -1
 PKV_ERR_UNSUPPORTED = -2
 PKV_ERR_LAUNCH = -3
+PKV_ERR_NO_SPACE = -4
+
+
+class NoSpaceError(RuntimeError):
+    """The block allocator has too few free blocks (or a table is full)."""
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -43,6 +48,15 @@ _SIGNATURES = {
                                          _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "paged_attention_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                                _I, _I, _I, _F, _P]),
+    "pkv_allocator_create": (_P, [_I, _I, _I, _I]),
+    "pkv_allocator_destroy": (None, [_P]),
+    "pkv_allocator_num_free": (_I, [_P]),
+    "pkv_allocator_context_len": (_I, [_P, _I]),
+    "pkv_allocator_append_slots": (ctypes.c_int, [_P, _I, _I, _P]),
+    "pkv_allocator_free_seq": (ctypes.c_int, [_P, _I]),
+    "pkv_allocator_block_table": (ctypes.c_int, [_P, _I, _P, _I]),
+    "pkv_allocator_build_decode_batch": (ctypes.c_int, [_P, _P, _I, _I, _P, _P, _P]),
+    "pkv_allocator_build_prefill_batch": (ctypes.c_int, [_P, _P, _P, _I, _I, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -86,6 +100,8 @@ def _raise(code: int, what: str):
         raise ValueError(msg)
     if code == PKV_ERR_UNSUPPORTED:
         raise NotImplementedError(msg)
+    if code == PKV_ERR_NO_SPACE:
+        raise NoSpaceError(msg)
     raise RuntimeError(msg)
 
 
@@ -328,3 +344,92 @@ def paged_decode_step(q, k_pool, v_pool, block_tables, context_lens, scale, part
         _stream(dev, stream))
     _raise(rc, "paged_decode_step")
     return (out, lse_out) if lse_out is not None else out
+
+
+def _np_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a.size else None
+
+
+class BlockAllocator:
+    """Host block allocator of the paged cache (the library's pkv_allocator_*
+    calls on host memory): a FIFO free-block queue, one block table per
+    sequence id, slot mappings and batch metadata as numpy arrays."""
+
+    def __init__(self, num_blocks, block_size, max_seqs, max_blocks_per_seq):
+        import numpy as np
+        self._np = np
+        self._lib = load_library()
+        self._h = self._lib.pkv_allocator_create(num_blocks, block_size, max_seqs,
+                                                 max_blocks_per_seq)
+        if not self._h:
+            raise ValueError("pkv_allocator_create failed (bad sizes or out of memory)")
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.max_seqs, self.max_blocks_per_seq = max_seqs, max_blocks_per_seq
+
+    def close(self):
+        if self._h:
+            self._lib.pkv_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_free(self) -> int:
+        return int(self._lib.pkv_allocator_num_free(self._h))
+
+    def context_len(self, seq) -> int:
+        n = int(self._lib.pkv_allocator_context_len(self._h, seq))
+        if n < 0:
+            _raise(n, "pkv_allocator_context_len")
+        return n
+
+    def append_slots(self, seq, num_tokens):
+        out = self._np.empty(max(num_tokens, 0), dtype=self._np.int64)
+        _raise(self._lib.pkv_allocator_append_slots(self._h, seq, num_tokens, _np_ptr(out)),
+               "pkv_allocator_append_slots")
+        return out
+
+    def free(self, seq):
+        _raise(self._lib.pkv_allocator_free_seq(self._h, seq), "pkv_allocator_free_seq")
+
+    def block_table(self, seq, width):
+        row = self._np.empty(width, dtype=self._np.int32)
+        _raise(self._lib.pkv_allocator_block_table(self._h, seq, _np_ptr(row), width),
+               "pkv_allocator_block_table")
+        return row
+
+    def decode_batch(self, seqs, width):
+        """One new token per sequence: (slot_mapping [B] int64, block_tables
+        [B, width] int32, context_lens [B] int32)."""
+        np = self._np
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        B = seqs.size
+        slots = np.empty(B, dtype=np.int64)
+        tables = np.empty((B, width), dtype=np.int32)
+        lens = np.empty(B, dtype=np.int32)
+        _raise(self._lib.pkv_allocator_build_decode_batch(
+            self._h, _np_ptr(seqs), B, width, _np_ptr(slots), _np_ptr(tables), _np_ptr(lens)),
+            "pkv_allocator_build_decode_batch")
+        return slots, tables, lens
+
+    def prefill_batch(self, seqs, chunk_lens, width):
+        """One chunk per sequence: (query_start [B + 1], slot_mapping
+        [total] int64, block_tables [B, width], context_lens [B])."""
+        np = self._np
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        chunk_lens = np.ascontiguousarray(chunk_lens, dtype=np.int32)
+        B = seqs.size
+        if chunk_lens.size != B:
+            raise ValueError("one chunk length per sequence")
+        qs = np.empty(B + 1, dtype=np.int32)
+        slots = np.empty(int(chunk_lens.astype(np.int64).sum()) if B else 0, dtype=np.int64)
+        tables = np.empty((B, width), dtype=np.int32)
+        lens = np.empty(B, dtype=np.int32)
+        _raise(self._lib.pkv_allocator_build_prefill_batch(
+            self._h, _np_ptr(seqs), _np_ptr(chunk_lens), B, width, _np_ptr(qs), _np_ptr(slots),
+            _np_ptr(tables), _np_ptr(lens)), "pkv_allocator_build_prefill_batch")
+        return qs, slots, tables, lens

@@ -169,6 +169,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_INVALID_ARG: return "invalid argument";
     case PKV_ERR_UNSUPPORTED: return "unsupported shape";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
+    case PKV_ERR_NO_SPACE: return "no space: not enough free cache blocks";
     default: return "unknown status";
   }
 }
