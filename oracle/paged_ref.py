@@ -45,6 +45,16 @@ What it computes, and where that comes from
   by ``slot = physical_block * block_size + offset``; a negative slot is
   skipped.
 
+* 8-bit cache (the pages mention only another system's q8 KV cache: Gemma
+  on llama.cpp with 8-bit K/V, in the post on an RTX 4090, and give no
+  format).  This library's format: every (token, KV head) row of D values is
+  stored as int8 codes with one fp32 scale, quantised when written:
+  amax = max |x| (the fp16 values widened to fp32), inv = 127 / amax and
+  code = rint(x * inv) (fp32 division and multiply, nearest-even), clipped
+  to [-127, 127]; scale = amax / 127; a row of zeros has codes 0 and scale 0.
+  Its value is code * scale.  Attention over an 8-bit cache is the plain
+  definition above applied to those values.
+
 Readings where the pages are silent (all listed in the design doc):
 * GQA: query head h uses KV head ``h // (Hq // Hkv)`` (contiguous groups).
 * ``context_lens`` counts the attended positions, including the token the
@@ -76,6 +86,9 @@ __all__ = [
     "split_reduce",
     "kv_cache_append",
     "fp32_scale",
+    "quantize_rows_q8",
+    "dequantize_pool_q8",
+    "kv_cache_append_q8",
 ]
 
 
@@ -273,3 +286,42 @@ def kv_cache_append(k_pool, v_pool, k_new, v_new, slot_mapping):
     flat_k[slots[keep]] = k_new[keep]
     flat_v[slots[keep]] = v_new[keep]
     return kp, vp
+
+
+# ---- 8-bit cache ------------------------------------------------------------
+
+def quantize_rows_q8(x16: np.ndarray):
+    """int8 codes and fp32 scales of each length-D row of fp16 ``x16`` (last
+    axis), with the decisions taken in fp32 as the format defines them."""
+    x = np.asarray(x16).astype(np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    nz = amax > 0
+    inv = np.zeros_like(amax)
+    inv[nz] = np.float32(127.0) / amax[nz]
+    codes = np.rint(x * inv[..., None])
+    codes = np.clip(codes, -127, 127).astype(np.int8)
+    scales = (amax / np.float32(127.0)).astype(np.float32)
+    return codes, scales
+
+
+def dequantize_pool_q8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Values code * scale of an 8-bit pool [NB, bs, Hkv, D] (scales
+    [NB, bs, Hkv]) in fp64 -- the pool the attention oracles then read."""
+    return codes.astype(np.float64) * scales.astype(np.float64)[..., None]
+
+
+def kv_cache_append_q8(k_codes, v_codes, k_scales, v_scales, k_new, v_new, slot_mapping):
+    """Quantise each new token's K and V rows and write codes and scales to
+    its slot (copies returned; a negative slot is skipped)."""
+    kc, vc = k_codes.copy(), v_codes.copy()
+    ks, vs = k_scales.copy(), v_scales.copy()
+    nb, bs = kc.shape[:2]
+    qk, sk = quantize_rows_q8(k_new)
+    qv, sv = quantize_rows_q8(v_new)
+    for i, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0 or slot >= nb * bs:
+            continue
+        blk, off = int(slot) // bs, int(slot) % bs
+        kc[blk, off], vc[blk, off] = qk[i], qv[i]
+        ks[blk, off], vs[blk, off] = sk[i], sv[i]
+    return kc, vc, ks, vs

@@ -562,6 +562,125 @@ def test_prefill_block_permutation():
     pin_prefill_block_permutation()
 
 
+# ---- 8-bit cache --------------------------------------------------------------
+
+def _f32(v):
+    """Round a Python float to the nearest fp32 value."""
+    import struct
+    return struct.unpack("f", struct.pack("f", v))[0]
+
+
+def _quantize_brute(row):
+    """Per-row int8 quantisation with scalar Python arithmetic, each step
+    rounded to fp32 as the format prescribes (an fp32 op computed in fp64 and
+    rounded once is the correctly rounded fp32 result for *, /)."""
+    xs = [float(v) for v in row]
+    amax = max(abs(v) for v in xs)
+    if amax == 0:
+        return [0] * len(xs), 0.0
+    inv = _f32(127.0 / amax)
+    codes = [max(-127, min(127, round(_f32(v * inv)))) for v in xs]   # round(): half to even
+    return codes, _f32(amax / 127.0)
+
+
+def pin_q8_brute_force():
+    rng = np.random.default_rng(600)
+    rows = [rng.standard_normal(64).astype(np.float16) for _ in range(6)]
+    rows.append(np.zeros(64, np.float16))
+    tie = np.zeros(64, np.float16)
+    tie[0], tie[1], tie[2], tie[3] = 127.0, 63.5, -0.5, 1.5      # inv = 1: ties at .5
+    rows.append(tie)
+    rows.append((rng.standard_normal(128) * 1e-3).astype(np.float16))
+    for r in rows:
+        codes, scale = ref.quantize_rows_q8(r[None])
+        want_c, want_s = _quantize_brute(r)
+        assert list(codes[0]) == want_c
+        assert float(scale[0]) == want_s
+    c, _ = ref.quantize_rows_q8(tie[None])
+    assert list(c[0, :4]) == [127, 64, 0, 2]
+
+
+def test_q8_brute_force():
+    pin_q8_brute_force()
+
+
+def pin_q8_roundtrip_bound():
+    """Each value comes back within half a quantisation step; the largest
+    magnitude of a row maps to +-127."""
+    rng = np.random.default_rng(601)
+    x = (rng.standard_normal((200, 64)) * rng.uniform(0.01, 8, (200, 1))).astype(np.float16)
+    codes, scales = ref.quantize_rows_q8(x)
+    back = ref.dequantize_pool_q8(codes[None], scales[None])[0]
+    err = np.abs(back - x.astype(np.float64))
+    assert np.all(err <= scales[:, None].astype(np.float64) * (0.5 + 1e-6))
+    assert np.all(np.abs(codes) <= 127)
+    top = np.argmax(np.abs(x.astype(np.float32)), axis=1)
+    assert np.all(np.abs(codes[np.arange(200), top]) == 127)
+
+
+def test_q8_roundtrip_bound():
+    pin_q8_roundtrip_bound()
+
+
+def pin_q8_exact_rows_match_fp16_attention():
+    """K/V rows that are integer multiples c * 2^-k with max |c| = 127
+    quantise exactly, so attention over the 8-bit cache equals the fp16
+    oracle over the same values."""
+    c = custom_case("q8exact", B=3, Hq=14, Hkv=2, D=64, block_size=16, lens=[20, 100, 7],
+                    seed=602, poison=False)
+    rng = np.random.default_rng(603)
+    shape = c.k_pool.shape
+    def exact_pool():
+        ints = rng.integers(-127, 128, shape)
+        ints[..., 0] = 127                                     # every row reaches 127
+        k = rng.integers(4, 9, shape[:3])[..., None]           # per-row power-of-two step
+        return (ints * np.exp2(-k.astype(np.float64))).astype(np.float16)
+    kp, vp = exact_pool(), exact_pool()
+    kq, ks = ref.quantize_rows_q8(kp)
+    vq, vs = ref.quantize_rows_q8(vp)
+    assert np.array_equal(ref.dequantize_pool_q8(kq, ks), kp.astype(np.float64))
+    got = ref.paged_attention_decode(c.q, ref.dequantize_pool_q8(kq, ks),
+                                     ref.dequantize_pool_q8(vq, vs), c.block_tables,
+                                     c.context_lens, c.scale)
+    want = ref.paged_attention_decode(c.q, kp, vp, c.block_tables, c.context_lens, c.scale)
+    assert np.array_equal(got, want)
+
+
+def test_q8_exact_rows_match_fp16_attention():
+    pin_q8_exact_rows_match_fp16_attention()
+
+
+def pin_q8_append_brute_force():
+    rng = np.random.default_rng(604)
+    NB, bs, Hkv, D = 6, 16, 2, 64
+    kc = rng.integers(-127, 128, (NB, bs, Hkv, D)).astype(np.int8)
+    vc = rng.integers(-127, 128, (NB, bs, Hkv, D)).astype(np.int8)
+    ks = rng.uniform(0, 1, (NB, bs, Hkv)).astype(np.float32)
+    vs = rng.uniform(0, 1, (NB, bs, Hkv)).astype(np.float32)
+    kn = rng.standard_normal((5, Hkv, D)).astype(np.float16)
+    vn = rng.standard_normal((5, Hkv, D)).astype(np.float16)
+    slots = np.array([3, -1, 40, 95, NB * bs], np.int64)
+    gk, gv, gks, gvs = ref.kv_cache_append_q8(kc, vc, ks, vs, kn, vn, slots)
+    wk, wv, wks, wvs = kc.copy(), vc.copy(), ks.copy(), vs.copy()
+    for i, sl in enumerate(slots):
+        if sl < 0 or sl >= NB * bs:
+            continue
+        for h in range(Hkv):
+            ck, sk = _quantize_brute(kn[i, h])
+            cv, sv = _quantize_brute(vn[i, h])
+            for d in range(D):
+                wk[sl // bs, sl % bs, h, d] = ck[d]
+                wv[sl // bs, sl % bs, h, d] = cv[d]
+            wks[sl // bs, sl % bs, h] = sk
+            wvs[sl // bs, sl % bs, h] = sv
+    for g, w in ((gk, wk), (gv, wv), (gks, wks), (gvs, wvs)):
+        assert np.array_equal(g, w)
+
+
+def test_q8_append_brute_force():
+    pin_q8_append_brute_force()
+
+
 ALL_PINS = (
     [lambda i=i: pin_sdpa(i) for i in range(len(SDPA_SHAPES))]
     + [pin_block_permutation, pin_ctx1_is_v_row, pin_identical_keys_mean_v,
@@ -569,7 +688,8 @@ ALL_PINS = (
        pin_brute_force_tiny, pin_ctx0_zero, pin_chunked_prefill_golden,
        pin_append_brute_force, pin_prefill_rows_are_decodes,
        pin_prefill_chunking_is_invisible, pin_prefill_brute_force,
-       pin_prefill_block_permutation]
+       pin_prefill_block_permutation, pin_q8_brute_force, pin_q8_roundtrip_bound,
+       pin_q8_exact_rows_match_fp16_attention, pin_q8_append_brute_force]
     + [lambda i=i: pin_prefill_sdpa(i) for i in range(len(PREFILL_SHAPES))]
     + [lambda i=i: pin_split_equals_unsplit(i) for i in range(len(SPLIT_SHAPES))]
 )

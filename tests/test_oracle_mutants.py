@@ -139,6 +139,24 @@ def _prefill_factory(kind):
     return prefill
 
 
+def _q8_factory(kind):
+    """The 8-bit quantiser with one planted mistake."""
+    def quantize(x16):
+        x = np.asarray(x16).astype(np.float32)
+        amax = np.max(np.abs(x), axis=-1)
+        if kind == "per_tensor_amax":
+            amax = np.full_like(amax, np.max(np.abs(x)))
+        nz = amax > 0
+        inv = np.zeros_like(amax)
+        inv[nz] = (np.float32(1.0) if kind == "no_127" else np.float32(127.0)) / amax[nz]
+        y = x * inv[..., None]
+        codes = np.trunc(y) if kind == "truncates" else np.rint(y)
+        codes = np.clip(codes, -128 if kind == "clip_128" else -127, 127).astype(np.int8)
+        scales = (amax / np.float32(127.0)).astype(np.float32)
+        return codes, scales
+    return quantize
+
+
 MUTANTS = {
     "gqa_modulo": ("kv_head_of", lambda h, Hq, Hkv: h % Hkv),
     "no_scale": ("attend", _attend_factory("no_scale")),
@@ -156,6 +174,9 @@ MUTANTS = {
     "append_no_skip": ("kv_cache_append", _append_no_skip),
     "split_lse_base2": ("paged_attention_decode_split", _split_factory("lse_log2")),
     "scale_not_fp32": ("fp32_scale", lambda s: float(s) * (1 + 1e-7)),
+    "q8_per_tensor_amax": ("quantize_rows_q8", _q8_factory("per_tensor_amax")),
+    "q8_missing_127": ("quantize_rows_q8", _q8_factory("no_127")),
+    "q8_truncates": ("quantize_rows_q8", _q8_factory("truncates")),
     "prefill_excludes_itself": ("paged_attention_prefill", _prefill_factory("excludes_itself")),
     "prefill_sees_next_token": ("paged_attention_prefill", _prefill_factory("sees_next_token")),
     "prefill_not_causal": ("paged_attention_prefill", _prefill_factory("not_causal")),
