@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--prefill", action="store_true",
                     help="time chunked-prefill attention instead (uses --batch, --ctx, --chunk)")
     ap.add_argument("--chunk", type=int, default=512, help="prefill chunk length (tokens)")
+    ap.add_argument("--q8", action="store_true",
+                    help="time decode over the 8-bit KV cache (at --batch, --ctx)")
     ap.add_argument("--allocator", action="store_true",
                     help="time the host block allocator (no GPU needed)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -513,6 +515,119 @@ def run_prefill(args):
     return res
 
 
+Q8_METRIC = ("paged decode attention over an 8-bit KV cache: achieved HBM GB/s "
+             "(% of peak) and µs/call")
+
+
+def q8_bytes(B, ctx_sum, Hq, Hkv, D):
+    """Algorithmic bytes of decode over the 8-bit cache: int8 codes and fp32
+    scales of the attended K/V rows, q read and out written (fp16)."""
+    return ctx_sum * Hkv * (D + 4) * 2 + B * Hq * D * 2 * 2
+
+
+def run_q8(args):
+    """Decode over the 8-bit cache at the sweep point B x ctx (Hq=14, Hkv=2,
+    D=64, bs=16): the step (quantising append + split pass + merge, three
+    launches), the split pass alone and the unsplit kernel, rotated over
+    >= 4x the Infinity Cache and graph-timed."""
+    import torch
+    import paged_kv_decode_cache_amd as pkv
+    import workloads
+
+    device = torch.device("cuda:0")
+    B, ctx = args.batch, args.ctx
+    case = (workloads.sweep_case(B, ctx) if B in workloads.SWEEP_B and ctx in workloads.SWEEP_CTX
+            else workloads.sweep_case(B, ctx, seed=3999))
+    kc, vc, ks, vs = workloads.q8_pools(case)
+    NB = case.num_blocks
+    ctx_sum = int(case.context_lens.astype(np.int64).sum())
+    set_bytes = ctx_sum * case.Hkv * (case.D + 4) * 2
+    R = args.sets or max(2, math.ceil(4 * LLC_BYTES / set_bytes))
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    codes_k = torch.empty((R * NB,) + kc.shape[1:], dtype=torch.int8, device=device)
+    codes_v = torch.empty_like(codes_k)
+    sc_k = torch.empty((R * NB, case.Hkv, case.block_size), dtype=torch.float32, device=device)
+    sc_v = torch.empty_like(sc_k)
+    k0, v0 = t(kc), t(vc)
+    ks0, vs0 = t(ks.transpose(0, 2, 1)), t(vs.transpose(0, 2, 1))
+    for r in range(R):
+        codes_k[r * NB:(r + 1) * NB].copy_(k0)
+        codes_v[r * NB:(r + 1) * NB].copy_(v0)
+        sc_k[r * NB:(r + 1) * NB].copy_(ks0)
+        sc_v[r * NB:(r + 1) * NB].copy_(vs0)
+    del k0, v0, ks0, vs0
+    bt0 = case.block_tables.astype(np.int64)
+    bt = [t(np.where(bt0 >= 0, bt0 + r * NB, -1).astype(np.int32)) for r in range(R)]
+    s0 = case.slot_mapping
+    slots = [t(np.where(s0 >= 0, s0 + r * NB * case.block_size, -1)) for r in range(R)]
+    q, k_new, v_new, cl = t(case.q), t(case.k_new), t(case.v_new), t(case.context_lens)
+    out = torch.empty((B, case.Hq, case.D), dtype=torch.float16, device=device)
+    pools = (codes_k, codes_v, sc_k, sc_v)
+
+    def split_pass(i, P, Pm, po, pl):
+        pkv.paged_attention_decode_split_q8(q, *pools, bt[i % R], cl, case.scale, P, Pm, po, pl)
+
+    def step(i, P, Pm, po, pl):
+        pkv.kv_cache_append_q8(*pools, k_new, v_new, slots[i % R])
+        split_pass(i, P, Pm, po, pl)
+        pkv.split_reduce(po, pl, cl, P, out=out)
+
+    def unsplit(i):
+        pkv.paged_attention_decode_q8(q, *pools, bt[i % R], cl, case.scale, out=out)
+
+    t0 = time.perf_counter()
+    i = 0
+    while i < args.warmup or time.perf_counter() - t0 < 0.2:
+        unsplit(i)
+        i += 1
+    torch.cuda.synchronize()
+    K = args.steps
+    n = min(R, 16)
+    time_it = lambda fn: time_graph(capture([lambda r=r: fn(r) for r in range(n)]), n, K)
+    best = None
+    for P in (256, 512, 1024):
+        Pm = case.max_partitions(P)
+        po = torch.empty((B, case.Hq, Pm, case.D), dtype=torch.float32, device=device)
+        pl = torch.empty((B, case.Hq, Pm), dtype=torch.float32, device=device)
+        us_step = time_it(lambda r: step(r, P, Pm, po, pl))
+        us_split = time_it(lambda r: split_pass(r, P, Pm, po, pl))
+        if best is None or us_step < best[1]:
+            best = (P, us_step, us_split)
+    us_unsplit = time_it(unsplit)
+    P, us_step, us_split = best
+    step_bytes = q8_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
+    app = 2 * B * case.Hkv * (case.D * 2 + case.D + 4) + 8 * B   # fp16 in, codes + scale out
+    split_bytes = ctx_sum * case.Hkv * (case.D + 4) * 2 + B * case.Hq * case.D * 2
+    achieved = split_bytes / (us_split * 1e-6) / 1e9
+    value = (step_bytes + app) / (us_step * 1e-6) / 1e9
+    fp16_bytes = alg_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
+    res = {
+        "metric": Q8_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(us_step * 1e-3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8/f16",
+        "data": "synthetic",
+        "config": {"workload": f"batch x context sweep point B={B} ctx={ctx} (Hq={case.Hq}, "
+                               f"Hkv={case.Hkv}, D={case.D}, block_size={case.block_size}), "
+                               "8-bit cache (int8 codes, fp32 scale per token and head)",
+                   "partition_size": P, "rotation_sets": R,
+                   "step": "kv_cache_append_q8 + paged_attention_decode_split_q8 + split_reduce",
+                   "algorithmic_bytes_per_step": step_bytes + app,
+                   "fp16_cache_bytes_for_comparison": fp16_bytes,
+                   "launch": "HIP graph of R consecutive steps, replayed"},
+        "us_per_step": round(us_step, 3),
+        "roofline": {"bound": "hbm",
+                     "kernel": f"pkv::attn_q8_kernel<{case.D}, 2, 4, 2, true, true>",
+                     "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                     "kernel_us": round(us_split, 3),
+                     "algorithmic_bytes_per_launch": split_bytes},
+        "split_pass_us": round(us_split, 3),
+        "unsplit_decode_us": round(us_unsplit, 3),
+        "unsplit_decode_gbs": round(step_bytes / (us_unsplit * 1e-6) / 1e9, 1),
+    }
+    return res
+
+
 def run_allocator(args):
     """Host block allocator (C ABI, host memory): µs per decode-step build for
     256 sequences (each grows by one token; slots, tables of width 256 and
@@ -657,6 +772,9 @@ def main():
         sys.exit(1)
     if args.sweep:
         run_sweep(args)
+        return
+    if args.q8:
+        print(json.dumps(run_q8(args)), flush=True)
         return
     if args.prefill:
         if args.batch == 32 and args.ctx == 4096 and "--batch" not in sys.argv:

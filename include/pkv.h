@@ -310,6 +310,51 @@ int split_reduce(void* out, float* lse_out,
                  int32_t partition_size, int32_t max_partitions, void* stream);
 
 /* ------------------------------------------------------------------------
+ * 8-bit KV cache.
+ *
+ * The pages mention an 8-bit KV cache only for another system (llama.cpp's
+ * q8 cache for Gemma on an RTX 4090, Inference Engineering thread) and give
+ * no format; this library's is:
+ *   k_codes, v_codes    [num_blocks, block_size, num_kv_heads, head_dim] int8
+ *   k_scales, v_scales  [num_blocks, num_kv_heads, block_size] fp32
+ * Each (token, KV head) row of head_dim values is quantised when written:
+ * amax = max |x| (fp16 values in fp32), inv = 127 / amax and code =
+ * rint(x * inv) (IEEE fp32 division and multiply, nearest-even; within
+ * [-127, 127]), scale = amax / 127; a zero row has codes 0 and scale 0.  The
+ * row's value is code * scale.  Attention over the 8-bit cache computes the
+ * same softmax as paged_attention_decode over those values.  Arrays 16-byte
+ * aligned.  The bytes per (token, head) row are head_dim + 4 instead of
+ * 2 * head_dim.  new K/V rows must be finite.
+ * ------------------------------------------------------------------------ */
+
+/* Quantise and write new tokens' K/V rows (bit-exact with the rule above).
+ * Arguments as kv_cache_append with the pools replaced by codes + scales. */
+int kv_cache_append_q8(void* k_codes, void* v_codes, float* k_scales, float* v_scales,
+                       const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                       int32_t num_tokens, int32_t num_blocks, int32_t block_size,
+                       int32_t num_kv_heads, int32_t head_dim, void* stream);
+
+/* paged_attention_decode over the 8-bit cache. */
+int paged_attention_decode_q8(void* out, const void* q,
+                              const void* k_codes, const void* v_codes,
+                              const float* k_scales, const float* v_scales,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, float scale, void* stream);
+
+/* paged_attention_decode_split over the 8-bit cache (merge with
+ * split_reduce). */
+int paged_attention_decode_split_q8(float* partial_out, float* partial_lse, const void* q,
+                                    const void* k_codes, const void* v_codes,
+                                    const float* k_scales, const float* v_scales,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    int32_t max_blocks_per_seq, int32_t partition_size,
+                                    int32_t max_partitions, float scale, void* stream);
+
+/* ------------------------------------------------------------------------
  * Host block allocator (host memory only; no GPU call).
  *
  * The cache's num_blocks blocks are handed out on demand from a FIFO queue of

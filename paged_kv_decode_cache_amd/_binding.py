@@ -48,6 +48,11 @@ _SIGNATURES = {
                                          _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "paged_attention_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                                _I, _I, _I, _F, _P]),
+    "kv_cache_append_q8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "paged_attention_decode_q8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                                 _I, _I, _I, _F, _P]),
+    "paged_attention_decode_split_q8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I,
+                                                       _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "pkv_allocator_create": (_P, [_I, _I, _I, _I]),
     "pkv_allocator_destroy": (None, [_P]),
     "pkv_allocator_num_free": (_I, [_P]),
@@ -224,6 +229,83 @@ def paged_attention_prefill(q, k_pool, v_pool, block_tables, context_lens, query
         float(scale), _stream(dev, stream))
     _raise(rc, "paged_attention_prefill")
     return out
+
+
+def _q8_shapes(k_codes, v_codes, k_scales, v_scales, dev):
+    _need(k_codes, "k_codes", torch.int8, 4, dev)
+    _need(v_codes, "v_codes", torch.int8, 4, dev)
+    _need(k_scales, "k_scales", torch.float32, 3, dev)
+    _need(v_scales, "v_scales", torch.float32, 3, dev)
+    NB, bs, Hkv, D = k_codes.shape
+    if v_codes.shape != k_codes.shape or k_scales.shape != (NB, Hkv, bs) or \
+            v_scales.shape != (NB, Hkv, bs):
+        raise ValueError("8-bit pools: codes [num_blocks, block_size, Hkv, D] int8 and scales "
+                         "[num_blocks, Hkv, block_size] fp32")
+    return NB, bs, Hkv, D
+
+
+def kv_cache_append_q8(k_codes, v_codes, k_scales, v_scales, k_new, v_new, slot_mapping,
+                       stream=None):
+    """Quantise and write each new token's K/V rows into the 8-bit cache."""
+    _need(k_new, "k_new", torch.float16, 3)
+    dev = k_new.device
+    NB, bs, Hkv, D = _q8_shapes(k_codes, v_codes, k_scales, v_scales, dev)
+    _need(v_new, "v_new", torch.float16, 3, dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+    N = k_new.shape[0]
+    if k_new.shape != (N, Hkv, D) or v_new.shape != (N, Hkv, D) or slot_mapping.shape != (N,):
+        raise ValueError("k_new/v_new must be [N, Hkv, D] and slot_mapping [N]")
+    rc = load_library().kv_cache_append_q8(
+        _ptr(k_codes), _ptr(v_codes), _ptr(k_scales), _ptr(v_scales), _ptr(k_new), _ptr(v_new),
+        _ptr(slot_mapping), N, NB, bs, Hkv, D, _stream(dev, stream))
+    _raise(rc, "kv_cache_append_q8")
+
+
+def paged_attention_decode_q8(q, k_codes, v_codes, k_scales, v_scales, block_tables,
+                              context_lens, scale, out=None, stream=None):
+    """Paged decode over the 8-bit cache (one launch): out [B, Hq, D] fp16."""
+    _need(q, "q", torch.float16, 3)
+    dev = q.device
+    NB, bs, Hkv, D = _q8_shapes(k_codes, v_codes, k_scales, v_scales, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, Hq, Dq = q.shape
+    if Dq != D or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("q must be [B, Hq, D], block_tables [B, max_blocks], context_lens [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    _need(out, "out", torch.float16, 3, dev)
+    rc = load_library().paged_attention_decode_q8(
+        _ptr(out), _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_scales), _ptr(v_scales),
+        _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
+        float(scale), _stream(dev, stream))
+    _raise(rc, "paged_attention_decode_q8")
+    return out
+
+
+def paged_attention_decode_split_q8(q, k_codes, v_codes, k_scales, v_scales, block_tables,
+                                    context_lens, scale, partition_size, max_partitions=None,
+                                    partial_out=None, partial_lse=None, stream=None):
+    """Split pass over the 8-bit cache; merge with split_reduce."""
+    _need(q, "q", torch.float16, 3)
+    dev = q.device
+    NB, bs, Hkv, D = _q8_shapes(k_codes, v_codes, k_scales, v_scales, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, Hq, _ = q.shape
+    Pm = max_partitions or max_partitions_for(block_tables.shape[1], bs, partition_size)
+    if partial_out is None:
+        partial_out = torch.empty((B, Hq, Pm, D), dtype=torch.float32, device=dev)
+    if partial_lse is None:
+        partial_lse = torch.empty((B, Hq, Pm), dtype=torch.float32, device=dev)
+    _need(partial_out, "partial_out", torch.float32, 4, dev)
+    _need(partial_lse, "partial_lse", torch.float32, 3, dev)
+    rc = load_library().paged_attention_decode_split_q8(
+        _ptr(partial_out), _ptr(partial_lse), _ptr(q), _ptr(k_codes), _ptr(v_codes),
+        _ptr(k_scales), _ptr(v_scales), _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D,
+        bs, NB, block_tables.shape[1], partition_size, Pm, float(scale), _stream(dev, stream))
+    _raise(rc, "paged_attention_decode_split_q8")
+    return partial_out, partial_lse
 
 
 def max_partitions_for(max_blocks_per_seq: int, block_size: int, partition_size: int) -> int:

@@ -13,6 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
 SOURCES = [os.path.join(CSRC, "pkv_api.hip"), os.path.join(CSRC, "pkv_alloc.cpp")]
 DEPS = SOURCES + [os.path.join(CSRC, "pkv_kernels.hpp"), os.path.join(CSRC, "pkv_prefill.hpp"),
+                  os.path.join(CSRC, "pkv_q8.hpp"),
                   os.path.join(INCLUDE, "pkv.h")]
 # Measurement aid used by bench.py only (streaming-read bandwidth probe).
 PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")

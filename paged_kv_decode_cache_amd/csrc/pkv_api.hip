@@ -10,6 +10,7 @@
 #include "pkv.h"
 #include "pkv_kernels.hpp"
 #include "pkv_prefill.hpp"
+#include "pkv_q8.hpp"
 
 namespace {
 
@@ -157,6 +158,51 @@ int launch_prefill(const pkv::PrefillParams& p, int64_t grid, hipStream_t st) {
     hipLaunchKernelGGL((pkv::prefill_kernel<D, NCT, 4, 2>), dim3((unsigned)grid), dim3(256), 0,
                        st, p);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+// 8-bit decode: unsplit (8 waves) or split pass (4 waves), 2 subtiles per
+// tile at head_dim 64 and 1 at 128, 2 tiles in flight.
+template <int D, bool SPLIT>
+int launch_q8(const pkv::Q8Params& p, int64_t grid, hipStream_t st) {
+  constexpr int NS = D == 64 ? 2 : 1;
+  constexpr int NW = SPLIT ? 4 : 8;
+  if (p.a.G <= 8)
+    hipLaunchKernelGGL((pkv::attn_q8_kernel<D, NS, NW, 2, SPLIT, true>), dim3((unsigned)grid),
+                       dim3(NW * 64), 0, st, p);
+  else
+    hipLaunchKernelGGL((pkv::attn_q8_kernel<D, NS, NW, 2, SPLIT, false>), dim3((unsigned)grid),
+                       dim3(NW * 64), 0, st, p);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int fill_q8(pkv::Q8Params& p, const void* q, const void* k_codes, const void* v_codes,
+            const float* k_scales, const float* v_scales, const int32_t* block_tables,
+            const int32_t* context_lens, int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+            int32_t head_dim, int32_t block_size, int32_t num_blocks,
+            int32_t max_blocks_per_seq, float scale) {
+  int rc = check_attn_common(q, k_codes, v_codes, block_tables, context_lens, B, num_q_heads,
+                             num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                             scale);
+  if (rc != PKV_OK) return rc;
+  if (!k_scales || !v_scales || !aligned(k_scales, 16) || !aligned(v_scales, 16))
+    return PKV_ERR_INVALID_ARG;
+  p = {};
+  p.a.q = static_cast<const pkv::f16*>(q);
+  p.a.block_tables = block_tables;
+  p.a.context_lens = context_lens;
+  p.a.Hq = num_q_heads;
+  p.a.Hkv = num_kv_heads;
+  p.a.G = num_q_heads / num_kv_heads;
+  p.a.block_size = block_size;
+  p.a.num_blocks = num_blocks;
+  p.a.max_blocks = max_blocks_per_seq;
+  p.a.spb_shift = spb_shift_of(block_size);
+  p.a.scale_log2 = scale * pkv::kLog2e;
+  p.k_codes = static_cast<const int8_t*>(k_codes);
+  p.v_codes = static_cast<const int8_t*>(v_codes);
+  p.k_scales = k_scales;
+  p.v_scales = v_scales;
+  return PKV_OK;
 }
 
 }  // namespace
@@ -404,6 +450,93 @@ int paged_attention_prefill(void* out, const void* q, const void* k_pool, const 
   p.q_tiles = (int32_t)q_tiles;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return head_dim == 64 ? launch_prefill<64>(p, grid, st) : launch_prefill<128>(p, grid, st);
+}
+
+int kv_cache_append_q8(void* k_codes, void* v_codes, float* k_scales, float* v_scales,
+                       const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                       int32_t num_tokens, int32_t num_blocks, int32_t block_size,
+                       int32_t num_kv_heads, int32_t head_dim, void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!k_codes || !v_codes || !k_scales || !v_scales || !aligned(k_codes, 16) ||
+      !aligned(v_codes, 16) || !aligned(k_scales, 16) || !aligned(v_scales, 16))
+    return PKV_ERR_INVALID_ARG;
+  if (!head_dim_ok(head_dim) || !block_size_ok(block_size)) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slot_mapping, 8))
+    return PKV_ERR_INVALID_ARG;
+  pkv::AppendQ8Params p;
+  p.k_codes = static_cast<int8_t*>(k_codes);
+  p.v_codes = static_cast<int8_t*>(v_codes);
+  p.k_scales = k_scales;
+  p.v_scales = v_scales;
+  p.k_new = static_cast<const pkv::f16*>(k_new);
+  p.v_new = static_cast<const pkv::f16*>(v_new);
+  p.slot_mapping = slot_mapping;
+  p.num_slots = (int64_t)num_blocks * block_size;
+  p.num_tokens = num_tokens;
+  p.Hkv = num_kv_heads;
+  p.D = head_dim;
+  p.block_size = block_size;
+  const int64_t threads = (int64_t)num_tokens * num_kv_heads * (head_dim / 8);
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(pkv::append_q8_kernel, dim3((unsigned)grid), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), p);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int paged_attention_decode_q8(void* out, const void* q, const void* k_codes, const void* v_codes,
+                              const float* k_scales, const float* v_scales,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, float scale, void* stream) {
+  pkv::Q8Params p;
+  int rc = fill_q8(p, q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens, B,
+                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                   max_blocks_per_seq, scale);
+  if (rc != PKV_OK) return rc;
+  if (B == 0) return PKV_OK;
+  if (!out || !aligned(out, 16)) return PKV_ERR_INVALID_ARG;
+  const int64_t grid = (int64_t)B * num_kv_heads;
+  if (grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  p.a.out = static_cast<pkv::f16*>(out);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return head_dim == 64 ? launch_q8<64, false>(p, grid, st) : launch_q8<128, false>(p, grid, st);
+}
+
+int paged_attention_decode_split_q8(float* partial_out, float* partial_lse, const void* q,
+                                    const void* k_codes, const void* v_codes,
+                                    const float* k_scales, const float* v_scales,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    int32_t max_blocks_per_seq, int32_t partition_size,
+                                    int32_t max_partitions, float scale, void* stream) {
+  pkv::Q8Params p;
+  int rc = fill_q8(p, q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens, B,
+                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                   max_blocks_per_seq, scale);
+  if (rc != PKV_OK) return rc;
+  if (partition_size <= 0 || max_partitions <= 0 || partition_size % block_size != 0)
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_partitions * partition_size < (int64_t)max_blocks_per_seq * block_size)
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_partitions * partition_size > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  if (!partial_out || !partial_lse || !aligned(partial_out, 16) || !aligned(partial_lse, 4))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t grid = (int64_t)B * num_kv_heads * max_partitions;
+  if (grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  p.a.partial_out = partial_out;
+  p.a.partial_lse = partial_lse;
+  p.a.partition_size = partition_size;
+  p.a.max_partitions = max_partitions;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return head_dim == 64 ? launch_q8<64, true>(p, grid, st) : launch_q8<128, true>(p, grid, st);
 }
 
 int split_reduce(void* out, float* lse_out, const float* partial_out, const float* partial_lse,

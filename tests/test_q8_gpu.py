@@ -1,0 +1,180 @@
+"""8-bit KV cache on the GPU: the quantising cache write bit-exact against the
+oracle's, and decode (unsplit, split + merge) over int8 codes against the
+fp64 oracle on the dequantised cache."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_decode_cache_amd as pkv
+import workloads
+from oracle import paged_ref as ref
+from gpu_common import DEV, PARTIAL_ATOL, case, check_fp16, host64, needs_gpu, say, to_gpu
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _gpu_q8(kc, vc, ks, vs):
+    """Device copies in the library's layout (scales [NB, Hkv, bs])."""
+    return _t(kc), _t(vc), _t(ks.transpose(0, 2, 1)), _t(vs.transpose(0, 2, 1))
+
+
+def _oracle_decode_q8(c, kc, vc, ks, vs, seqs=None, q=None, ctx=None):
+    kd = ref.dequantize_pool_q8(kc, ks)
+    vd = ref.dequantize_pool_q8(vc, vs)
+    return ref.paged_attention_decode(c.q if q is None else q, kd, vd, c.block_tables,
+                                      c.context_lens if ctx is None else ctx, c.scale,
+                                      return_lse=True, seqs=seqs)
+
+
+APPEND_SHAPES = [(2, 64, 16), (8, 128, 32), (1, 64, 256), (4, 128, 16)]
+
+
+@pytest.mark.parametrize("Hkv,D,bs", APPEND_SHAPES)
+def test_append_q8_bit_exact(Hkv, D, bs):
+    rng = np.random.default_rng(700 + D + bs)
+    NB, N = 12, 40
+    kc = rng.integers(-127, 128, (NB, bs, Hkv, D), dtype=np.int8)
+    vc = rng.integers(-127, 128, (NB, bs, Hkv, D), dtype=np.int8)
+    ks = rng.uniform(0, 1, (NB, bs, Hkv)).astype(np.float32)
+    vs = rng.uniform(0, 1, (NB, bs, Hkv)).astype(np.float32)
+    kn = (rng.standard_normal((N, Hkv, D)) * rng.uniform(1e-3, 8, (N, Hkv, 1))).astype(np.float16)
+    vn = (rng.standard_normal((N, Hkv, D)) * rng.uniform(1e-3, 8, (N, Hkv, 1))).astype(np.float16)
+    kn[0] = 0.0                                   # zero rows: codes 0, scale 0
+    kn[1, :, :4] = np.array([127.0, 63.5, -0.5, 1.5], np.float16)   # inv = 1: ties
+    kn[1, :, 4:] = 0.0
+    slots = rng.permutation(NB * bs)[:N].astype(np.int64)
+    slots[5], slots[9] = -1, NB * bs + 3          # skipped
+    g = [_t(kc), _t(vc), _t(ks.transpose(0, 2, 1)), _t(vs.transpose(0, 2, 1))]
+    pkv.kv_cache_append_q8(*g, _t(kn), _t(vn), _t(slots))
+    torch.cuda.synchronize()
+    wk, wv, wks, wvs = ref.kv_cache_append_q8(kc, vc, ks, vs, kn, vn, slots)
+    assert np.array_equal(g[0].cpu().numpy(), wk)
+    assert np.array_equal(g[1].cpu().numpy(), wv)
+    assert np.array_equal(g[2].cpu().numpy().transpose(0, 2, 1).view(np.uint32), wks.view(np.uint32))
+    assert np.array_equal(g[3].cpu().numpy().transpose(0, 2, 1).view(np.uint32), wvs.view(np.uint32))
+
+
+Q8_CASES = ["tiny", "qwen", "sweep:32:4096", "sweep:1:128", "sweep:8:2048", "long:1:32768"]
+
+
+@pytest.mark.parametrize("name", Q8_CASES)
+def test_decode_q8_matches_oracle(name):
+    c = case(name)
+    say(f"decode q8 {name}")
+    kc, vc, ks, vs = workloads.q8_pools(c)
+    g = to_gpu(c)
+    out = pkv.paged_attention_decode_q8(g.q, *_gpu_q8(kc, vc, ks, vs), g.bt, g.ctx, c.scale)
+    torch.cuda.synchronize()
+    want, _ = _oracle_decode_q8(c, kc, vc, ks, vs)
+    check_fp16(out, want, f"decode q8 {name}")
+
+
+@pytest.mark.parametrize("name,P", [("qwen", 256), ("sweep:32:4096", 512), ("tiny", 16),
+                                    ("long:1:32768", 512), ("sweep:8:1024", 64)])
+def test_split_q8_matches_oracle(name, P):
+    c = case(name)
+    say(f"split q8 {name} P={P}")
+    kc, vc, ks, vs = workloads.q8_pools(c)
+    g = to_gpu(c)
+    Pm = c.max_partitions(P)
+    po, pl = pkv.paged_attention_decode_split_q8(g.q, *_gpu_q8(kc, vc, ks, vs), g.bt, g.ctx,
+                                                 c.scale, P, Pm)
+    out, lse = pkv.split_reduce(po, pl, g.ctx, P, want_lse=True)
+    torch.cuda.synchronize()
+    want, want_lse = _oracle_decode_q8(c, kc, vc, ks, vs)
+    check_fp16(out, want, f"split q8 {name}")
+    fin = np.isfinite(want_lse)
+    assert float(np.abs(host64(lse)[fin] - want_lse[fin]).max()) <= PARTIAL_ATOL
+    wpo, wpl = ref.paged_attention_decode_split(c.q, ref.dequantize_pool_q8(kc, ks),
+                                                ref.dequantize_pool_q8(vc, vs), c.block_tables,
+                                                c.context_lens, c.scale, P, Pm)
+    valid = np.isfinite(wpl)
+    assert np.array_equal(np.isneginf(host64(pl)), np.isneginf(wpl))
+    assert float(np.abs(host64(po)[valid] - wpo[valid]).max()) <= PARTIAL_ATOL
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,bs,lens", [
+    (16, 1, 128, 32, [40, 700, 1]),
+    (32, 8, 128, 16, [100, 1, 900]),
+    (4, 4, 64, 64, [3, 77, 500]),
+    (14, 2, 64, 16, [0, 1, 15, 16, 17, 1000]),
+])
+def test_decode_q8_edge_shapes(Hq, Hkv, D, bs, lens):
+    c = workloads.custom_case("q8edge", B=len(lens), Hq=Hq, Hkv=Hkv, D=D, block_size=bs,
+                              lens=lens, seed=710)
+    kc, vc, ks, vs = workloads.q8_pools(c)
+    g = to_gpu(c)
+    gq = _gpu_q8(kc, vc, ks, vs)
+    out = pkv.paged_attention_decode_q8(g.q, *gq, g.bt, g.ctx, c.scale)
+    po, pl = pkv.paged_attention_decode_split_q8(g.q, *gq, g.bt, g.ctx, c.scale, 64)
+    out_s = pkv.split_reduce(po, pl, g.ctx, 64)
+    torch.cuda.synchronize()
+    want, _ = _oracle_decode_q8(c, kc, vc, ks, vs)
+    check_fp16(out, want, f"q8 edge {Hq}/{Hkv}/{D}/{bs}")
+    check_fp16(out_s, want, f"q8 edge split {Hq}/{Hkv}/{D}/{bs}")
+
+
+def test_q8_lognormal_lengths_d128():
+    """The skewed configuration's head shape (Hq=32, Hkv=8, D=128) with 32
+    lognormal lengths (median 1024, clipped to [16, 8192])."""
+    rng = np.random.default_rng(720)
+    lens = np.clip(workloads.skewed_lengths(rng, B=32), 16, 8192)
+    c = workloads.custom_case("q8lognormal", B=32, Hq=32, Hkv=8, D=128, block_size=16,
+                              lens=lens, seed=721)
+    kc, vc, ks, vs = workloads.q8_pools(c)
+    g = to_gpu(c)
+    gq = _gpu_q8(kc, vc, ks, vs)
+    out = pkv.paged_attention_decode_q8(g.q, *gq, g.bt, g.ctx, c.scale)
+    po, pl = pkv.paged_attention_decode_split_q8(g.q, *gq, g.bt, g.ctx, c.scale, 512)
+    out_s = pkv.split_reduce(po, pl, g.ctx, 512)
+    torch.cuda.synchronize()
+    want, _ = _oracle_decode_q8(c, kc, vc, ks, vs)
+    check_fp16(out, want, "q8 lognormal")
+    check_fp16(out_s, want, "q8 lognormal split")
+
+
+def test_q8_step_append_then_decode():
+    """One decode step on the 8-bit cache: quantising append of each
+    sequence's new token at position ctx-1, then decode, against the oracle's
+    append and decode."""
+    c = case("qwen")
+    kc, vc, ks, vs = workloads.q8_pools(c)
+    g = to_gpu(c)
+    gq = _gpu_q8(kc, vc, ks, vs)
+    pkv.kv_cache_append_q8(*gq, g.k_new, g.v_new, g.slots)
+    out = pkv.paged_attention_decode_q8(g.q, *gq, g.bt, g.ctx, c.scale)
+    torch.cuda.synchronize()
+    wk, wv, wks, wvs = ref.kv_cache_append_q8(kc, vc, ks, vs, c.k_new, c.v_new, c.slot_mapping)
+    assert np.array_equal(gq[0].cpu().numpy(), wk)
+    want, _ = _oracle_decode_q8(c, wk, wv, wks, wvs)
+    check_fp16(out, want, "q8 step")
+
+
+def test_q8_quantisation_error_against_fp16():
+    """The format's own error (not the kernel's): the qwen cache quantised on
+    the GPU, position by position, then decoded, against the fp16 oracle on
+    the original cache.  N(0,1) data: the bound is loose (0.05) and the
+    measured error is reported."""
+    c = case("qwen")
+    NB, bs, Hkv, D = c.k_pool.shape
+    rows = np.nonzero(~np.isnan(c.k_pool[..., 0, 0].astype(np.float32)).ravel())[0]
+    slots = rows.astype(np.int64)
+    kn = c.k_pool.reshape(NB * bs, Hkv, D)[rows]
+    vn = c.v_pool.reshape(NB * bs, Hkv, D)[rows]
+    gq = (torch.zeros((NB, bs, Hkv, D), dtype=torch.int8, device=DEV),
+          torch.zeros((NB, bs, Hkv, D), dtype=torch.int8, device=DEV),
+          torch.zeros((NB, Hkv, bs), dtype=torch.float32, device=DEV),
+          torch.zeros((NB, Hkv, bs), dtype=torch.float32, device=DEV))
+    pkv.kv_cache_append_q8(*gq, _t(kn), _t(vn), _t(slots))
+    g = to_gpu(c)
+    out = pkv.paged_attention_decode_q8(g.q, *gq, g.bt, g.ctx, c.scale)
+    torch.cuda.synchronize()
+    want16 = ref.paged_attention_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens,
+                                        c.scale)
+    err = float(np.abs(host64(out) - want16).max())
+    say(f"8-bit cache vs fp16 cache, qwen: max abs difference {err:.4f}")
+    assert err <= 0.05

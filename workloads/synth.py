@@ -348,3 +348,31 @@ def prefill_case(name, *, Hq, Hkv, D, block_size, ctx, chunk, seed, q_mult=1.0,
                        query_start=qs, block_tables=base.block_tables, k_pool=base.k_pool,
                        v_pool=base.v_pool, q=q, k_chunk=k_chunk, v_chunk=v_chunk,
                        chunk_slots=slots, seed=seed)
+
+
+# ---- 8-bit cache -------------------------------------------------------------
+
+def q8_pools(case, seed: Optional[int] = None):
+    """Random 8-bit K/V pools with the case's shapes: int8 codes uniform in
+    [-127, 127] with one +-127 per row (as a quantised row always has), and
+    per-(token, head) fp32 scales uniform in [2, 4.5] / 127 (the amax of
+    N(0,1) rows of 64-128 values).  Rows no sequence attends (NaN in the
+    case's fp16 pools) get a NaN scale.  Scales are returned [NB, bs, Hkv];
+    the library's layout is their transpose [NB, Hkv, bs].
+    Returns (k_codes, v_codes, k_scales, v_scales)."""
+    rng = np.random.default_rng(case.seed + 13 if seed is None else seed)
+    NB, bs, Hkv, D = case.k_pool.shape
+    unattended = np.isnan(case.k_pool[..., 0].astype(np.float32))
+
+    def pool():
+        codes = rng.integers(-127, 128, (NB, bs, Hkv, D), dtype=np.int8)
+        top = rng.integers(0, D, (NB, bs, Hkv, 1))
+        sign = np.where(rng.random((NB, bs, Hkv, 1)) < 0.5, -127, 127).astype(np.int8)
+        np.put_along_axis(codes, top, sign, axis=-1)
+        scales = (rng.uniform(2.0, 4.5, (NB, bs, Hkv)) / 127.0).astype(np.float32)
+        scales[unattended] = np.nan
+        return codes, scales
+
+    kc, ks = pool()
+    vc, vs = pool()
+    return kc, vc, ks, vs
