@@ -110,6 +110,23 @@ int pkv_set_launch_config(int which, int waves_per_group, int subtiles_per_tile,
                           int tiles_in_flight);
 
 /*
+ * pkv_set_grid_mode -- tuning and test aid: the grid of the partitioned
+ * passes (paged_attention_decode_split, paged_decode_step) with the default
+ * launch shape.
+ *   0  auto (default): direct when B * num_kv_heads * max_partitions is at
+ *      most 8192 workgroups, compact above;
+ *   1  direct: one workgroup per (sequence, KV head, partition), empty ones
+ *      included;
+ *   2  compact: a fixed number of workgroups, each scanning the context
+ *      lengths and looping over the non-empty (sequence, KV head, partition)
+ *      items (B <= 4096; larger batches stay direct).
+ * Results do not depend on the mode beyond fp32 summation order; the
+ * documented outputs (including -inf partial_lse of empty partitions) are
+ * the same.  Returns PKV_OK or PKV_ERR_INVALID_ARG.
+ */
+int pkv_set_grid_mode(int mode);
+
+/*
  * kv_cache_append -- write the K and V rows of new tokens into their slots.
  *
  * Defined by the cache update of every decode step (Inference Engineering,

@@ -38,6 +38,7 @@ _SIGNATURES = {
     "pkv_version": (ctypes.c_int, []),
     "pkv_set_launch_config": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_int]),
+    "pkv_set_grid_mode": (ctypes.c_int, [ctypes.c_int]),
     "kv_cache_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "paged_attention_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                               _I, _F, _P]),
@@ -134,6 +135,13 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, device=None
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def set_grid_mode(mode: str):
+    """Tuning/test aid: grid of the partitioned passes: 'auto', 'direct' or
+    'compact'."""
+    _raise(load_library().pkv_set_grid_mode({"auto": 0, "direct": 1, "compact": 2}[mode]),
+           "pkv_set_grid_mode")
 
 
 def set_launch_config(which: str, waves_per_group: int = 0, subtiles_per_tile: int = 0,

@@ -37,7 +37,7 @@ struct Shape {
   int waves, subtiles, depth;
 };
 
-Shape pick_shape(int which, int head_dim) {
+Shape pick_default_shape(int which, int head_dim) {
   Shape s;
   // Defaults (measured on MI355X): the split pass runs one partition per
   // workgroup with 4 waves; the unsplit pass has one workgroup per
@@ -45,6 +45,11 @@ Shape pick_shape(int which, int head_dim) {
   s.waves = which == 0 ? 8 : 4;
   s.subtiles = head_dim == 64 ? 2 : 1;
   s.depth = 2;
+  return s;
+}
+
+Shape pick_shape(int which, int head_dim) {
+  Shape s = pick_default_shape(which, head_dim);
   const int w = g_cfg_waves[which].load(std::memory_order_relaxed);
   const int t = g_cfg_subtiles[which].load(std::memory_order_relaxed);
   const int d = g_cfg_depth[which].load(std::memory_order_relaxed);
@@ -106,9 +111,45 @@ int spb_shift_of(int32_t block_size) {
   return sh;
 }
 
+// Grid of the partitioned passes: direct (one workgroup per sequence x KV
+// head x partition) or compact (a fixed number of workgroups looping over the
+// non-empty items; attn_compact_kernel).  Auto picks compact when the direct
+// grid would exceed kCompactAbove workgroups (ragged batches with a wide
+// table are mostly empty partitions, each a workgroup dispatch); settable for
+// tests and tuning through pkv_set_grid_mode.
+constexpr int64_t kCompactAbove = 8192;
+constexpr int kCompactGroups = 2048;
+std::atomic<int> g_grid_mode{0};  // 0 auto, 1 direct, 2 compact
+
+template <int D, int MODE>
+void launch_compact(const AttnParams& p, int64_t grid, hipStream_t st) {
+  constexpr int NS = D == 64 ? 2 : 1;
+  const unsigned g = (unsigned)(grid < kCompactGroups ? grid : kCompactGroups);
+  if (p.G <= 8)
+    hipLaunchKernelGGL((pkv::attn_compact_kernel<D, NS, 4, 2, MODE, true>), dim3(g), dim3(256),
+                       0, st, p);
+  else
+    hipLaunchKernelGGL((pkv::attn_compact_kernel<D, NS, 4, 2, MODE, false>), dim3(g), dim3(256),
+                       0, st, p);
+}
+
 template <int MODE>
 int launch_attn(const AttnParams& p, int head_dim, int64_t grid, hipStream_t st) {
   const Shape s = pick_shape(MODE == 0 ? 0 : 1, head_dim);
+  if constexpr (MODE >= 1) {
+    const Shape d = pick_default_shape(1, head_dim);
+    const int mode = g_grid_mode.load(std::memory_order_relaxed);
+    const bool same_shape =
+        s.waves == d.waves && s.subtiles == d.subtiles && s.depth == d.depth;
+    if (p.B <= pkv::kCompactMaxB && same_shape &&
+        (mode == 2 || (mode == 0 && grid > kCompactAbove))) {
+      if (head_dim == 64)
+        launch_compact<64, MODE>(p, grid, st);
+      else
+        launch_compact<128, MODE>(p, grid, st);
+      return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+    }
+  }
   if (head_dim == 64)
     launch_attn_shape<64, MODE>(p, grid, s, st);
   else
@@ -222,6 +263,12 @@ const char* pkv_status_string(int status) {
 
 int pkv_version(void) { return kVersion; }
 
+int pkv_set_grid_mode(int mode) {
+  if (mode < 0 || mode > 2) return PKV_ERR_INVALID_ARG;
+  g_grid_mode.store(mode, std::memory_order_relaxed);
+  return PKV_OK;
+}
+
 int pkv_set_launch_config(int which, int waves_per_group, int subtiles_per_tile,
                           int tiles_in_flight) {
   if (which != 0 && which != 1) return PKV_ERR_INVALID_ARG;
@@ -292,6 +339,7 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
   p.block_tables = block_tables;
   p.context_lens = context_lens;
   p.out = static_cast<pkv::f16*>(out);
+  p.B = B;
   p.Hq = num_q_heads;
   p.Hkv = num_kv_heads;
   p.G = num_q_heads / num_kv_heads;
@@ -335,6 +383,7 @@ int paged_attention_decode_split(float* partial_out, float* partial_lse, const v
   p.context_lens = context_lens;
   p.partial_out = partial_out;
   p.partial_lse = partial_lse;
+  p.B = B;
   p.Hq = num_q_heads;
   p.Hkv = num_kv_heads;
   p.G = num_q_heads / num_kv_heads;
@@ -397,6 +446,7 @@ int paged_decode_step(void* out, float* lse_out, void* k_pool, void* v_pool, con
   p.partial_out = partial_out;
   p.partial_lse = partial_lse;
   p.counters = counters;
+  p.B = B;
   p.Hq = num_q_heads;
   p.Hkv = num_kv_heads;
   p.G = num_q_heads / num_kv_heads;

@@ -58,7 +58,7 @@ struct AttnParams {
   f16* out;             // unsplit: [B, Hq, D]
   float* partial_out;   // split:   [B, Hq, P_max, D]
   float* partial_lse;   // split:   [B, Hq, P_max]
-  int32_t Hq, Hkv, G;
+  int32_t B, Hq, Hkv, G;
   int32_t block_size, num_blocks, max_blocks;
   int32_t partition_size, max_partitions;
   int32_t spb_shift;    // log2(block_size / 16) when a power of two, else -1
@@ -571,31 +571,24 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
 // hold an all-ones word until written (the merger sets them back after
 // reading, and resets the counter), so no store->flag->load round trips sit
 // on the kernel's tail.
+// One work item -- (sequence b, KV head kvh, partition p; p = 0 unsplit) --
+// of the attention kernels.  Every thread of the workgroup calls it with the
+// same item; smem is the workgroup's NW * AttnSmem<D, NS>::kWaveBytes bytes.
 template <int D, int NS, int NW, int DEPTH, int MODE, bool DUAL>
-__global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
+__device__ __forceinline__ void attn_item(const AttnParams& a, const int b, const int kvh,
+                                          const int p, unsigned char* smem) {
   constexpr int KC = D / 32;   // QK MFMAs (16x16x32) per subtile
   constexpr int NDB = D / 16;  // PV MFMA column blocks (16 dims each)
   constexpr bool SPLIT = MODE >= 1;
   constexpr bool STEP = MODE == 2;
   using SM = AttnSmem<D, NS>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[NW * SM::kWaveBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane & 15;     // MFMA column
   const int quad = lane >> 4;  // 0..3
   const int head_col = DUAL ? (g & 7) : g;  // query head (within the group) of this column
-
   const int Hkv = a.Hkv;
-  const int kvh = blockIdx.x % Hkv;
-  const int rest = blockIdx.x / Hkv;
-  int b, p = 0;
-  if (SPLIT) {
-    p = rest % a.max_partitions;
-    b = rest / a.max_partitions;
-  } else {
-    b = rest;
-  }
 
   const int spb = a.block_size >> 4;  // subtiles per block
   const int spb_shift = a.spb_shift;
@@ -829,6 +822,108 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
   __syncthreads();  // the merger's own partial is complete in LDS
   __shared__ float msm[6 * kMergeSlots];
   merge_step_partitions<D, NW>(a, b, kvh, n_parts, p, own, msm);
+}
+
+// Direct grid: workgroup -> item from its index (B x Hkv x partitions).
+template <int D, int NS, int NW, int DEPTH, int MODE, bool DUAL>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NW * AttnSmem<D, NS>::kWaveBytes];
+  const int kvh = blockIdx.x % a.Hkv;
+  const int rest = blockIdx.x / a.Hkv;
+  if (MODE >= 1)
+    attn_item<D, NS, NW, DEPTH, MODE, DUAL>(a, rest / a.max_partitions, kvh,
+                                            rest % a.max_partitions, smem);
+  else
+    attn_item<D, NS, NW, DEPTH, MODE, DUAL>(a, rest, kvh, 0, smem);
+}
+
+// Compact grid for the split pass and the fused step when most of the
+// B x Hkv x max_partitions grid would be empty (ragged lengths, a wide
+// table): a fixed number of workgroups each scans the batch's partition
+// counts into LDS and loops over its share of the non-empty items only.  An
+// empty workgroup still costs a dispatch (~1.3 ns each on MI355X), which
+// dominates a skewed batch's launch otherwise.
+constexpr int kCompactMaxB = 4096;
+
+// Largest b in [0, B) with prefix[b] <= idx (prefix non-decreasing,
+// prefix[0] = 0 <= idx); two ballots over 64 lanes, B <= 4096.
+__device__ __forceinline__ int find_sequence(const int* prefix, int B, int idx, int lane) {
+  const int step = (B + 63) >> 6;
+  int c = lane * step;
+  int k = __popcll(__ballot(c < B && prefix[c] <= idx));
+  const int lo = (k - 1) * step;
+  c = lo + lane;
+  k = __popcll(__ballot(lane < step && c < B && prefix[c] <= idx));
+  return lo + k - 1;
+}
+
+template <int D, int NS, int NW, int DEPTH, int MODE, bool DUAL>
+__global__ __launch_bounds__(NW * 64) void attn_compact_kernel(const AttnParams a) {
+  static_assert(MODE >= 1, "the compact grid is for the partitioned passes");
+  constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NW * AttnSmem<D, NS>::kWaveBytes];
+  __shared__ int prefix[kCompactMaxB + 1];
+  __shared__ int wave_sum[NW];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int B = a.B;
+  const int cap = a.max_blocks * a.block_size;
+
+  // items of sequence b: its non-empty partitions (the fused step gives an
+  // empty sequence one, which writes its zero output)
+  const int per = (B + NT - 1) / NT;
+  const int j0 = min(B, t * per), j1 = min(B, j0 + per);
+  int local = 0;
+  for (int j = j0; j < j1; ++j) {
+    int ctx = a.context_lens[j];
+    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+    int n = (ctx + a.partition_size - 1) / a.partition_size;
+    if (MODE == 2 && n == 0) n = 1;
+    prefix[j] = n;  // the count for now; each thread touches its own indices only
+    local += n;
+  }
+  // exclusive scan of the per-thread sums across the workgroup
+  int incl = local;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wave_sum[wave] = incl;
+  __syncthreads();
+  int base = incl - local;
+  for (int w = 0; w < wave; ++w) base += wave_sum[w];
+  int run = base;
+  for (int j = j0; j < j1; ++j) {
+    const int n = prefix[j];
+    prefix[j] = run;
+    run += n;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int total = 0;
+    for (int w = 0; w < NW; ++w) total += wave_sum[w];
+    prefix[B] = total;
+  }
+  __syncthreads();
+  const int total_items = prefix[B] * a.Hkv;
+
+  // split pass: partitions at or past the context get lse = -inf
+  if (MODE == 1) {
+    for (int b = blockIdx.x; b < B; b += gridDim.x) {
+      const int n = prefix[b + 1] - prefix[b];
+      const int spare = a.max_partitions - n;
+      for (int e = t; e < a.Hq * spare; e += NT)
+        a.partial_lse[((size_t)b * a.Hq + e / spare) * a.max_partitions + n + e % spare] =
+            -INFINITY;
+    }
+  }
+  for (int i = blockIdx.x; i < total_items; i += gridDim.x) {
+    const int idx = i / a.Hkv;
+    const int b = find_sequence(prefix, B, idx, lane);
+    attn_item<D, NS, NW, DEPTH, MODE, DUAL>(a, b, i % a.Hkv, idx - prefix[b], smem);
+    __syncthreads();  // LDS is reused by the next item
+  }
 }
 
 // LSE-weighted merge of the valid partitions of one (sequence, query head).

@@ -53,6 +53,14 @@ def test_launch_config_validation():
     assert lib.pkv_set_launch_config(1, 0, 0, 0) == 0
 
 
+def test_grid_mode_validation():
+    lib = pkv.load_library()
+    assert lib.pkv_set_grid_mode(3) == -1
+    assert lib.pkv_set_grid_mode(-1) == -1
+    for mode in (2, 1, 0):
+        assert lib.pkv_set_grid_mode(mode) == 0
+
+
 def _decode(lib, **kw):
     a = dict(out=A16, q=B16, k=C16, v=D16, bt=E16, ctx=F16, B=2, Hq=14, Hkv=2, D=64, bs=16,
              NB=10, maxb=4, scale=0.125)

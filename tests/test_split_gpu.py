@@ -141,3 +141,46 @@ def test_split_every_launch_shape(waves, subtiles, depth):
         check_fp16(out2, want2, f"split d128 g16 NW={waves} NS={subtiles} DEPTH={depth}")
     finally:
         pkv.set_launch_config("split", 0, 0, 0)
+
+
+@pytest.mark.parametrize("name,P", [("tiny", 16), ("qwen", 256), ("sweep:8:1024", 64),
+                                    ("long:1:32768", 512)])
+def test_split_compact_grid_matches_oracle(name, P):
+    """The compact grid (workgroups looping over the non-empty items) gives
+    the oracle's partials, with -inf lse on every empty partition."""
+    c = case(name)
+    say(f"split compact {name}: P={P}")
+    g = to_gpu(c)
+    Pm = c.max_partitions(P) + 2
+    try:
+        pkv.set_grid_mode("compact")
+        po, pl, out, lse = _split_reduce(g, c, P, Pm)
+        torch.cuda.synchronize()
+    finally:
+        pkv.set_grid_mode("auto")
+    wpo, wpl = ref.paged_attention_decode_split(c.q, c.k_pool, c.v_pool, c.block_tables,
+                                                c.context_lens, c.scale, P, Pm)
+    gpl = host64(pl)
+    assert np.array_equal(np.isneginf(gpl), np.isneginf(wpl))
+    valid = np.isfinite(wpl)
+    assert float(np.abs(gpl[valid] - wpl[valid]).max()) <= PARTIAL_ATOL
+    assert float(np.abs(host64(po)[valid] - wpo[valid]).max()) <= PARTIAL_ATOL
+    want, want_lse = oracle_decode(c)
+    check_fp16(out, want, f"compact {name}")
+    _check_lse(lse, want_lse, name)
+
+
+def test_split_compact_ragged_and_empty_sequences():
+    c = workloads.custom_case("compact_ragged", B=7, Hq=14, Hkv=2, D=64, block_size=16,
+                              lens=[0, 1, 700, 16, 0, 2049, 33], seed=102, max_blocks=160)
+    g = to_gpu(c)
+    try:
+        pkv.set_grid_mode("compact")
+        po, pl, out, lse = _split_reduce(g, c, 64)
+        torch.cuda.synchronize()
+    finally:
+        pkv.set_grid_mode("auto")
+    want, want_lse = oracle_decode(c)
+    check_fp16(out, want, "compact ragged")
+    _check_lse(lse, want_lse, "compact ragged")
+    assert torch.isneginf(pl[0]).all() and torch.isneginf(pl[4]).all()

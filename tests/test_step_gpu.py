@@ -218,3 +218,42 @@ def test_step_merge_stress_against_three_launch_path():
         worst = max(worst, (fused.float() - ref3.float()).abs().max().item())
         _check_workspace_restored(ws)
     assert worst <= 2e-3, worst
+
+
+def test_step_compact_grid_edges_and_churn():
+    """The fused step on the compact grid: edge lengths (empty sequences write
+    zeros), then 20 steps with new queries and random lengths, each against
+    the three-launch path, the workspace restored after every call."""
+    c = workloads.custom_case("step_compact", B=6, Hq=14, Hkv=2, D=64, block_size=16,
+                              lens=[0, 1, 16, 17, 511, 1300], seed=112, q_mult=4.0,
+                              max_blocks=96)
+    P = 64
+    try:
+        pkv.set_grid_mode("compact")
+        g = to_gpu(c)
+        ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+        out, lse = _step(g, c, P, ws)
+        torch.cuda.synchronize()
+        want, want_lse, kp, _ = _oracle_step(c)
+        check_fp16(out, want, "compact step edges")
+        _check_lse(lse, want_lse)
+        assert int((out[0] != 0).sum()) == 0
+        assert np.array_equal(g.k_pool.cpu().numpy().view(np.uint16), kp.view(np.uint16))
+        _check_workspace_restored(ws)
+        gen = torch.Generator(device=g.q.device).manual_seed(8)
+        cpu_gen = torch.Generator().manual_seed(9)
+        worst = 0.0
+        for it in range(20):
+            g.q = torch.randn(g.q.shape, generator=gen, device=g.q.device).to(torch.float16)
+            g.ctx = torch.randint(0, 96 * 16 + 1, (c.B,), generator=cpu_gen,
+                                  dtype=torch.int32).to(g.q.device)
+            fused = _step(g, c, P, ws, append=False, want_lse=False)
+            po, pl = pkv.paged_attention_decode_split(g.q, g.k_pool, g.v_pool, g.bt, g.ctx,
+                                                      c.scale, P)
+            ref3 = pkv.split_reduce(po, pl, g.ctx, P)
+            torch.cuda.synchronize()
+            worst = max(worst, (fused.float() - ref3.float()).abs().max().item())
+            _check_workspace_restored(ws)
+        assert worst <= 2e-3, worst
+    finally:
+        pkv.set_grid_mode("auto")
