@@ -441,7 +441,8 @@ __device__ __forceinline__ void merge_waves_impl(const SoftmaxState<D>& st, floa
 // Threads cover (head, 4 dims) x partition groups with a streaming LSE merge,
 // and the groups combine through LDS.  Every other partition's row is polled
 // until none of its words is still unwritten, then set back to unwritten for
-// the next launch (lse words after a barrier: all threads of a head read them).
+// the next launch (data words once the thread has read all its rows; lse
+// words after a barrier, since all threads of a head read them).
 // The wait ends: the other workgroups of the pair took their tickets before
 // this one took the last, so they are running and wait on nothing.
 constexpr int kMergeSlots = 512;  // >= 16 heads x 128/4 dims
@@ -453,7 +454,7 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
                                       float* msm /* 6 * kMergeSlots floats */) {
   constexpr int NT = NW * 64;
   constexpr int TPR = D / 4;
-  constexpr int BATCH = 4;  // rows in flight per thread
+  constexpr int BATCH = 8;  // rows in flight per thread
   const int t = threadIdx.x;
   const int G = a.G;
   const int Pm = a.max_partitions;
@@ -502,7 +503,6 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
               x[j] = load_coherent4(po_rs, xo);
               l[j] = load_coherent1(pl_rs, (hh * Pm + q) * 4);
             }
-            store_coherent4(po_rs, xo, unwritten4);
           }
           const float lq = l[j];
           if (lq > M) {
@@ -517,6 +517,11 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
         }
       }
     }
+    // back to "not written", after every row is read: a store issued between
+    // two batches of loads would hold up the next batch (stores and loads
+    // share one in-order counter)
+    for (int q = grp; q < np; q += ngroups)
+      if (q != p_own) store_coherent4(po_rs, ((hh * Pm + q) * D + 4 * cc) * 4, unwritten4);
     float* r = msm + 6 * slot;
     r[0] = M;
     r[1] = L;

@@ -200,7 +200,8 @@ def qwen_case(seed: int = 2000) -> DecodeCase:
 SWEEP_B = (1, 8, 32)
 SWEEP_CTX = (128, 512, 1024, 2048, 4096)
 # Larger points on the same head configuration (trend past the sweep's corner)
-EXTRA_POINTS = ((64, 4096), (128, 4096), (32, 8192), (64, 8192), (128, 8192), (32, 16384))
+EXTRA_POINTS = ((64, 4096), (128, 4096), (32, 8192), (64, 8192), (128, 8192), (32, 16384),
+                (256, 8192))
 
 
 def sweep_case(B: int, ctx: int, seed: Optional[int] = None,
