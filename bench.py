@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--batch", type=int, default=32)
     ap.add_argument("--ctx", type=int, default=4096)
-    ap.add_argument("--partition", type=int, default=512, help="split partition size (tokens)")
+    ap.add_argument("--partition", type=int, default=1024, help="split partition size (tokens)")
     ap.add_argument("--waves", type=int, default=0, help="split pass waves/workgroup (0=default)")
     ap.add_argument("--subtiles", type=int, default=0, help="split pass subtiles/tile (0=default)")
     ap.add_argument("--depth", type=int, default=0, help="split pass tiles in flight (0=default)")
@@ -352,7 +352,7 @@ def run_headline(args):
         kname = f"void pkv::attn_kernel<{case.D}, {ns}, {nw}, {depth}, 1, {dual}>(pkv::AttnParams)"
         step_desc = "kv_cache_append + paged_attention_decode_split + split_reduce"
     tprof = TRAFFIC_PROFILES[args.path]
-    traffic = profiled_traffic(kname, tprof) if (B, ctx, P) == (32, 4096, 512) else None
+    traffic = profiled_traffic(kname, tprof) if (B, ctx, P) == (32, 4096, 1024) else None
     achieved = kbytes / (kern_us * 1e-6) / 1e9
     value = (step_bytes + app_bytes) / (ms_per_step * 1e-3) / 1e9
     res = {
@@ -716,7 +716,7 @@ def run_sweep(args):
             rot.q, rot.k_pool, rot.v_pool, rot.bt[i % R], rot.ctx, case.scale, out=out))
         best = None
         best_step = None
-        for P in (128, 256, 512, 1024, 2048):
+        for P in (128, 256, 512, 1024, 2048, 4096):
             if P % case.block_size:
                 continue
             Pm = case.max_partitions(P)

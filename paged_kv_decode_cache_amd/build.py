@@ -33,6 +33,10 @@ def command(out: str = LIB, extra=(), sources=None) -> list:
             # MFMA accumulators in VGPRs: the softmax rescale touches them
             # with VALU ops, which AGPRs would need copies for.
             "-mllvm", "-amdgpu-mfma-vgpr-form",
+            # A fused-step ticket is one lane's atomic whose result is needed
+            # only at the end; the wave-combining rewrite would wait for it
+            # (and every load before it) right where it is issued.
+            "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
             "-Wall", "-Wno-unused-function",
             "-I", INCLUDE, "-I", CSRC, *extra, *(sources or SOURCES), "-o", out]
 

@@ -148,6 +148,32 @@ __device__ __forceinline__ float as_written(float x) {
   return is_written(x) ? x : __builtin_bit_cast(float, 0x7FC00000u);
 }
 
+// Streaming loads through buffer resources.  A load past the resource's
+// range reads zeros without a memory access, so a masked-out row (a subtile
+// past the context, a block id out of range, a tile past the wave's last)
+// is a load with an empty resource rather than a branch around the load.
+// Every path through the decode loop then issues the same loads in the same
+// order, which keeps the compiler's in-order wait counts exact: a wait for
+// one tile never has to drain the tiles requested after it.
+// A byte offset past every resource it is used with (each spans < 2^30
+// bytes), with room for small immediate offsets on top.
+constexpr int kOutOfRange = 0x40000000;
+
+__device__ __forceinline__ f32x4 load_b128(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+}
+__device__ __forceinline__ f16x8 load_rows16(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(f16x8, load_b128(rs, off));
+}
+// Eight query values; `sign` is 0x80008000 to negate them (flipping fp16
+// sign bits is exact), else 0.  Lanes whose column holds no query head read
+// past the resource and get zeros.
+__device__ __forceinline__ f16x8 load_q16(__amdgpu_buffer_rsrc_t rs, int off, unsigned sign) {
+  u32x4 w = __builtin_bit_cast(u32x4, load_b128(rs, off));
+  w ^= sign;
+  return __builtin_bit_cast(f16x8, w);
+}
+
 // LDS bytes one wave uses: V staging during the loop, merge buffers after.
 template <int D, int NS>
 struct AttnSmem {
@@ -174,25 +200,31 @@ struct KVTile {
 };
 
 // Physical block ids of the NS subtiles starting at subtile s0, one per lane
-// (lanes 0..NS-1; -1 at or past subtile `limit`).  One vector load per wave.
+// (lanes 0..NS-1; 0 at or past subtile `limit`, where the caller masks the
+// subtile anyway).  One vector load per wave through the resource of the
+// sequence's table row (max_blocks * 4 bytes).
 template <int NS>
-__device__ __forceinline__ int load_block_ids(const int32_t* bt_row, int s0, int limit,
+__device__ __forceinline__ int load_block_ids(__amdgpu_buffer_rsrc_t bt_rs, int s0, int limit,
                                               int spb, int spb_shift, int lane) {
   const int s = s0 + (lane & (NS - 1));
-  int id = -1;
-  if (lane < NS && s < limit) id = bt_row[spb_shift >= 0 ? (s >> spb_shift) : (s / spb)];
-  return id;
+  const int blk = spb_shift >= 0 ? (s >> spb_shift) : (s / spb);
+  const int off = (lane < NS && s < limit) ? blk * 4 : kOutOfRange;
+  return __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(bt_rs, off, 0, 0));
 }
 
-// Issue the K/V loads of one tile.  `ids` comes from load_block_ids; a block
-// id outside [0, num_blocks) is not read and its subtile is masked out.  All
-// address arithmetic is wave-uniform except the lane's fixed offset.
+// Issue the K/V loads of one tile.  `ids` comes from load_block_ids.  A
+// subtile past sub_end, or in a block whose id is outside [0, num_blocks),
+// is loaded through an empty resource (zeros, no memory access) and masked
+// out.  Each subtile's resource starts at its first token's row of head kvh
+// and spans the subtile (16 tokens x all heads); lane_off_b is the lane's
+// fixed byte offset in it.
 template <int D, int NS>
 __device__ __forceinline__ void load_kv_tile(KVTile<D, NS>& T, const AttnParams& a, int ids,
                                              int s0, int sub_end, int t_end, int spb,
                                              int spb_shift, int64_t tok_stride, int kvh,
-                                             int lane_off) {
+                                             int lane_off_b) {
   constexpr int KC = D / 32;
+  const int sub_bytes = 32 * (int)tok_stride;
   T.s0 = s0;
   int okm = 0;
 #pragma unroll
@@ -204,20 +236,12 @@ __device__ __forceinline__ void load_kv_tile(KVTile<D, NS>& T, const AttnParams&
     const int sib = spb_shift >= 0 ? (s & (spb - 1)) : (s % spb);
     const int64_t blk_off =
         ((int64_t)(ok ? phys : 0) * a.block_size + sib * 16) * tok_stride + (int64_t)kvh * D;
-    if (ok) {
-      const f16* kp = a.k_pool + blk_off + lane_off;
-      const f16* vp = a.v_pool + blk_off + lane_off;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(a.k_pool + blk_off, ok ? sub_bytes : 0);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(a.v_pool + blk_off, ok ? sub_bytes : 0);
 #pragma unroll
-      for (int m = 0; m < KC; ++m) {
-        T.k[j][m] = *reinterpret_cast<const f16x8*>(kp + 32 * m);
-        T.v[j][m] = *reinterpret_cast<const f16x8*>(vp + 32 * m);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < KC; ++m) {
-        T.k[j][m] = zero8();
-        T.v[j][m] = zero8();
-      }
+    for (int m = 0; m < KC; ++m) {
+      T.k[j][m] = load_rows16(kr, lane_off_b + 64 * m);
+      T.v[j][m] = load_rows16(vr, lane_off_b + 64 * m);
     }
   }
   T.okmask = okm;
@@ -533,7 +557,8 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
   __syncthreads();
   for (int i = t; i < G * np; i += NT) {
     const int q = i % np;
-    if (q != p_own) store_coherent1(pl_rs, ((i / np) * Pm + q) * 4, __builtin_bit_cast(float, kUnwritten));
+    if (q != p_own)
+      store_coherent1(pl_rs, ((i / np) * Pm + q) * 4, __builtin_bit_cast(float, kUnwritten));
   }
   for (int hc = t; hc < per_group; hc += NT) {
     float M = -INFINITY;
@@ -598,8 +623,9 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   const int spb = a.block_size >> 4;  // subtiles per block
   const int spb_shift = a.spb_shift;
   const int64_t tok_stride = (int64_t)Hkv * D;
-  const int lane_off = (lane & 15) * Hkv * D + 8 * quad;
+  const int lane_off_b = ((lane & 15) * Hkv * D + 8 * quad) * 2;
   const int32_t* bt_row = a.block_tables + (size_t)b * a.max_blocks;
+  const __amdgpu_buffer_rsrc_t bt_rs = buffer_rsrc(bt_row, a.max_blocks * 4);
   constexpr int TSTEP = NW * NS;  // subtiles between a wave's consecutive tiles
 
   // The block ids of the wave's first DEPTH tiles are requested together with
@@ -612,7 +638,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   int ids[DEPTH];
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i)
-    ids[i] = load_block_ids<NS>(bt_row, s_first + i * TSTEP, sub_cap, spb, spb_shift, lane);
+    ids[i] = load_block_ids<NS>(bt_rs, s_first + i * TSTEP, sub_cap, spb, spb_shift, lane);
 
   const int cap = a.max_blocks * a.block_size;
   int ctx = a.context_lens[b];
@@ -654,6 +680,9 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
       s_new = pos >> 4;
       tok_new = pos & 15;
     }
+    // A branch around these loads sits before the K/V loop, where it costs
+    // the loop's wait counts nothing (loading them through empty resources
+    // in every workgroup measured slower).
 #pragma unroll
     for (int m = 0; m < KC; ++m) {
       kn[m] = *reinterpret_cast<const f16x8*>(a.k_new + new_row + 8 * quad + 32 * m);
@@ -675,14 +704,13 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   const float c = fmaxf(neg_scale ? -a.scale_log2 : a.scale_log2, 1.17549435e-38f);
   f16x8 qb[KC];
   {
-    const bool hv = head_col < a.G;
-    const f16* qrow =
-        a.q + ((size_t)b * a.Hq + kvh * a.G + (hv ? head_col : 0)) * D + 8 * quad;
+    // the group's G query rows; columns past G read zeros
+    const __amdgpu_buffer_rsrc_t q_rs =
+        buffer_rsrc(a.q + ((size_t)b * a.Hq + kvh * a.G) * D, a.G * D * 2);
+    const unsigned sign = neg_scale ? 0x80008000u : 0u;
 #pragma unroll
-    for (int m = 0; m < KC; ++m) {
-      const f16x8 v = *reinterpret_cast<const f16x8*>(qrow + 32 * m);
-      qb[m] = hv ? (neg_scale ? -v : v) : zero8();
-    }
+    for (int m = 0; m < KC; ++m)
+      qb[m] = load_q16(q_rs, (head_col * D + 8 * quad + 32 * m) * 2, sign);
   }
   f16x4 ones;
 #pragma unroll
@@ -699,17 +727,17 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   // DEPTH-slot software pipeline over the wave's tiles: up to DEPTH tiles of
   // K/V are in flight while one is consumed.  The block ids of tile u+DEPTH
   // are requested right after the K/V of tile u, so the in-order wait for
-  // them only ever waits for tiles already consumed.
+  // them only ever waits for tiles already consumed.  Loads past the wave's
+  // last tile go through empty resources (no memory access), so every
+  // iteration issues the same loads.
   const int n_tiles = s_first < sub_end ? (sub_end - s_first + TSTEP - 1) / TSTEP : 0;
   KVTile<D, NS> buf[DEPTH];
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) {
-    if (i < n_tiles) {
-      load_kv_tile<D, NS>(buf[i], a, ids[i], s_first + i * TSTEP, sub_end, t_end, spb, spb_shift,
-                          tok_stride, kvh, lane_off);
-      ids[i] = load_block_ids<NS>(bt_row, s_first + (i + DEPTH) * TSTEP, sub_end, spb,
-                                  spb_shift, lane);
-    }
+    load_kv_tile<D, NS>(buf[i], a, ids[i], s_first + i * TSTEP, sub_end, t_end, spb, spb_shift,
+                        tok_stride, kvh, lane_off_b);
+    ids[i] = load_block_ids<NS>(bt_rs, s_first + (i + DEPTH) * TSTEP, sub_end, spb, spb_shift,
+                                lane);
   }
   // Fused step: the ticket (issued after the first K/V requests; waited for
   // only at the end).
@@ -721,17 +749,14 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) {
       const int u = u0 + i;
-      if (u < n_tiles) {
+      if (u < n_tiles)
         consume_tile<D, NS, DUAL, STEP>(buf[i], st, qb, stage, c, t_end, lane, ones, rem_mul,
                                         s_new, tok_new, slot, new_phys, new_off,
                                         a.block_size, kn, vn);
-        if (u + DEPTH < n_tiles) {
-          load_kv_tile<D, NS>(buf[i], a, ids[i], s_first + (u + DEPTH) * TSTEP, sub_end, t_end,
-                              spb, spb_shift, tok_stride, kvh, lane_off);
-          ids[i] = load_block_ids<NS>(bt_row, s_first + (u + 2 * DEPTH) * TSTEP, sub_end, spb,
-                                      spb_shift, lane);
-        }
-      }
+      load_kv_tile<D, NS>(buf[i], a, ids[i], s_first + (u + DEPTH) * TSTEP, sub_end, t_end, spb,
+                          spb_shift, tok_stride, kvh, lane_off_b);
+      ids[i] = load_block_ids<NS>(bt_rs, s_first + (u + 2 * DEPTH) * TSTEP, sub_end, spb,
+                                  spb_shift, lane);
     }
   }
 
@@ -794,7 +819,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
           const int Pm = a.max_partitions;
           const __amdgpu_buffer_rsrc_t po_rs =
               buffer_rsrc(a.partial_out + head0 * Pm * D, a.G * Pm * D * 4);
-          const __amdgpu_buffer_rsrc_t pl_rs = buffer_rsrc(a.partial_lse + head0 * Pm, a.G * Pm * 4);
+          const __amdgpu_buffer_rsrc_t pl_rs =
+              buffer_rsrc(a.partial_lse + head0 * Pm, a.G * Pm * 4);
 #pragma unroll
           for (int v = 0; v < 4; ++v) r[v] = as_written(r[v]);
           store_coherent4(po_rs, ((head_col * Pm + p) * D + d0) * 4, r);

@@ -54,8 +54,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams pp
   const int spb = a.block_size >> 4;
   const int spb_shift = a.spb_shift;
   const int64_t tok_stride = (int64_t)Hkv * D;
-  const int lane_off = (lane & 15) * Hkv * D + 8 * quad;
+  const int lane_off_b = ((lane & 15) * Hkv * D + 8 * quad) * 2;
   const int32_t* bt_row = a.block_tables + (size_t)b * a.max_blocks;
+  const __amdgpu_buffer_rsrc_t bt_rs = buffer_rsrc(bt_row, a.max_blocks * 4);
   constexpr int TSTEP = NW;
   const int s_first = wave;
   const int sub_cap = a.max_blocks * spb;
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams pp
   int ids[DEPTH];
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i)
-    ids[i] = load_block_ids<NS>(bt_row, s_first + i * TSTEP, sub_cap, spb, spb_shift, lane);
+    ids[i] = load_block_ids<NS>(bt_rs, s_first + i * TSTEP, sub_cap, spb, spb_shift, lane);
 
   const int r0 = pp.query_start[b];
   int n = pp.query_start[b + 1] - r0;
@@ -84,20 +85,20 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams pp
   const float c_scale = fmaxf(neg_scale ? -a.scale_log2 : a.scale_log2, 1.17549435e-38f);
   f16x8 qb[NCT][KC];
   int qpos[NCT];
+  // the tile's nq rows of the group's G heads (row stride Hq * D); padding
+  // columns read past the resource (zeros)
+  const __amdgpu_buffer_rsrc_t q_rs =
+      buffer_rsrc(a.q + ((size_t)(r0 + q0) * a.Hq + kvh * G) * D, ((nq - 1) * a.Hq + G) * D * 2);
+  const unsigned sign = neg_scale ? 0x80008000u : 0u;
 #pragma unroll
   for (int t = 0; t < NCT; ++t) {
     const int col = 16 * t + g;
     const int i = col / G;
     const bool valid = col < QT * G && i < nq;
     qpos[t] = valid ? pos_first + i : -1;
-    const f16* qrow =
-        a.q + ((size_t)(r0 + q0 + (valid ? i : 0)) * a.Hq + kvh * G + (valid ? col % G : 0)) * D +
-        8 * quad;
+    const int qoff = valid ? ((i * a.Hq + col % G) * D + 8 * quad) * 2 : kOutOfRange;
 #pragma unroll
-    for (int m = 0; m < KC; ++m) {
-      const f16x8 v = *reinterpret_cast<const f16x8*>(qrow + 32 * m);
-      qb[t][m] = valid ? (neg_scale ? -v : v) : zero8();
-    }
+    for (int m = 0; m < KC; ++m) qb[t][m] = load_q16(q_rs, qoff + 64 * m, sign);
   }
   // positions every valid column sees: [0, pos_first]
   const int vis_all = pos_first;
@@ -119,107 +120,107 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams pp
   KVTile<D, NS> buf[DEPTH];
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) {
-    if (i < n_tiles) {
-      load_kv_tile<D, NS>(buf[i], a, ids[i], s_first + i * TSTEP, sub_end, t_end, spb, spb_shift,
-                          tok_stride, kvh, lane_off);
-      ids[i] = load_block_ids<NS>(bt_row, s_first + (i + DEPTH) * TSTEP, sub_end, spb, spb_shift,
-                                  lane);
-    }
+    // past the wave's last tile: empty resources, no memory access
+    load_kv_tile<D, NS>(buf[i], a, ids[i], s_first + i * TSTEP, sub_end, t_end, spb, spb_shift,
+                        tok_stride, kvh, lane_off_b);
+    ids[i] = load_block_ids<NS>(bt_rs, s_first + (i + DEPTH) * TSTEP, sub_end, spb, spb_shift,
+                                lane);
   }
   for (int u0 = 0; u0 < n_tiles; u0 += DEPTH) {
 #pragma unroll
     for (int di = 0; di < DEPTH; ++di) {
       const int u = u0 + di;
-      if (u >= n_tiles) continue;
-      KVTile<D, NS>& T = buf[di];
-      const int tok0 = T.s0 << 4;
-      // logits S^T[token][column] per column tile
-      f32x4 sc[NCT];
+      if (u < n_tiles) {
+        KVTile<D, NS>& T = buf[di];
+        const int tok0 = T.s0 << 4;
+        // logits S^T[token][column] per column tile
+        f32x4 sc[NCT];
 #pragma unroll
-      for (int t = 0; t < NCT; ++t) {
-        f32x4 acc = zero4f();
+        for (int t = 0; t < NCT; ++t) {
+          f32x4 acc = zero4f();
 #pragma unroll
-        for (int m = 0; m < KC; ++m)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(T.k[0][m], qb[t][m], acc, 0, 0, 0);
-        sc[t] = acc;
-      }
-      // tokens past some column's limit, or of an unread block, drop out
-      if (!(T.full && tok0 + 15 <= vis_all)) {
+          for (int m = 0; m < KC; ++m)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(T.k[0][m], qb[t][m], acc, 0, 0, 0);
+          sc[t] = acc;
+        }
+        // tokens past some column's limit, or of an unread block, drop out
+        if (!(T.full && tok0 + 15 <= vis_all)) {
 #pragma unroll
-        for (int t = 0; t < NCT; ++t)
+          for (int t = 0; t < NCT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int tok = tok0 + 4 * quad + v;
+              sc[t][v] = ((T.okmask & 1) && tok <= qpos[t]) ? sc[t][v] : -INFINITY;
+            }
+        }
+        f16x4 ph[NCT], pl[NCT];
+#pragma unroll
+        for (int t = 0; t < NCT; ++t) {
+          float tmax = fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3]));
+          tmax = max_across_quads(tmax);
+          const float tmax_s = tmax * c_scale;
+          const bool grow = tmax_s > st[t].m + kRescaleLog2;
+          if (__any(grow)) {
+            // only growing columns rescale: a column still at -inf (every token
+            // so far past its causal limit) must not form -inf - -inf
+            const float m_new = grow ? tmax_s : st[t].m;
+            const float alpha = grow ? fast_exp2(st[t].m - m_new) : 1.0f;
+            st[t].m = m_new;
+            st[t].lsum *= alpha;
+#pragma unroll
+            for (int i = 0; i < NDB; ++i) st[t].o[i] *= alpha;
+          }
+          const float neg_m = (st[t].m == -INFINITY) ? 0.0f : -st[t].m;
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int tok = tok0 + 4 * quad + v;
-            sc[t][v] = ((T.okmask & 1) && tok <= qpos[t]) ? sc[t][v] : -INFINITY;
+            const float p = fast_exp2(fmaf(sc[t][v], c_scale, neg_m));
+            const f16 h = (f16)p;
+            ph[t][v] = h;
+            pl[t][v] = (f16)fmaf((float)h, -1.0f, p);
           }
-      }
-      f16x4 ph[NCT], pl[NCT];
-#pragma unroll
-      for (int t = 0; t < NCT; ++t) {
-        float tmax = fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3]));
-        tmax = max_across_quads(tmax);
-        const float tmax_s = tmax * c_scale;
-        const bool grow = tmax_s > st[t].m + kRescaleLog2;
-        if (__any(grow)) {
-          // only growing columns rescale: a column still at -inf (every token
-          // so far past its causal limit) must not form -inf - -inf
-          const float m_new = grow ? tmax_s : st[t].m;
-          const float alpha = grow ? fast_exp2(st[t].m - m_new) : 1.0f;
-          st[t].m = m_new;
-          st[t].lsum *= alpha;
-#pragma unroll
-          for (int i = 0; i < NDB; ++i) st[t].o[i] *= alpha;
         }
-        const float neg_m = (st[t].m == -INFINITY) ? 0.0f : -st[t].m;
+        // V subtile -> LDS row-major (rows no column sees as zeros), then the
+        // transposed A operand once for all column tiles
+        {
+          f16* row = stage + (lane & 15) * ROW + 8 * quad;
+          const int tok = tok0 + (lane & 15);
+          const bool keep = (T.okmask & 1) && tok < t_end;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float p = fast_exp2(fmaf(sc[t][v], c_scale, neg_m));
-          const f16 h = (f16)p;
-          ph[t][v] = h;
-          pl[t][v] = (f16)fmaf((float)h, -1.0f, p);
+          for (int m = 0; m < KC; ++m) {
+            const f16x8 v = keep ? T.v[0][m] : zero8();
+            *reinterpret_cast<f16x4*>(row + 32 * m) = v.lo;
+            *reinterpret_cast<f16x4*>(row + 32 * m + 4) = v.hi;
+          }
         }
-      }
-      // V subtile -> LDS row-major (rows no column sees as zeros), then the
-      // transposed A operand once for all column tiles
-      {
-        f16* row = stage + (lane & 15) * ROW + 8 * quad;
-        const int tok = tok0 + (lane & 15);
-        const bool keep = (T.okmask & 1) && tok < t_end;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        f16x4 va[NDB];
+        {
+          typedef short s16x4 __attribute__((ext_vector_type(4)));
+          const f16* tr = stage + (4 * quad + (g >> 2)) * ROW + 4 * (g & 3);
 #pragma unroll
-        for (int m = 0; m < KC; ++m) {
-          const f16x8 v = keep ? T.v[0][m] : zero8();
-          *reinterpret_cast<f16x4*>(row + 32 * m) = v.lo;
-          *reinterpret_cast<f16x4*>(row + 32 * m + 4) = v.hi;
+          for (int db = 0; db < NDB; ++db)
+            va[db] = __builtin_bit_cast(
+                f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (__attribute__((address_space(3))) s16x4*)(tr + 16 * db)));
         }
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      f16x4 va[NDB];
-      {
-        typedef short s16x4 __attribute__((ext_vector_type(4)));
-        const f16* tr = stage + (4 * quad + (g >> 2)) * ROW + 4 * (g & 3);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          va[db] = __builtin_bit_cast(
-              f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                         (__attribute__((address_space(3))) s16x4*)(tr + 16 * db)));
-      }
+        for (int t = 0; t < NCT; ++t) {
+          st[t].lsum = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, ph[t], st[t].lsum, 0, 0, 0);
+          st[t].lsum = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pl[t], st[t].lsum, 0, 0, 0);
 #pragma unroll
-      for (int t = 0; t < NCT; ++t) {
-        st[t].lsum = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, ph[t], st[t].lsum, 0, 0, 0);
-        st[t].lsum = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pl[t], st[t].lsum, 0, 0, 0);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          st[t].o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[db], ph[t], st[t].o[db], 0, 0, 0);
-          st[t].o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[db], pl[t], st[t].o[db], 0, 0, 0);
+          for (int db = 0; db < NDB; ++db) {
+            st[t].o[db] =
+                __builtin_amdgcn_mfma_f32_16x16x16f16(va[db], ph[t], st[t].o[db], 0, 0, 0);
+            st[t].o[db] =
+                __builtin_amdgcn_mfma_f32_16x16x16f16(va[db], pl[t], st[t].o[db], 0, 0, 0);
+          }
         }
+        asm volatile("" ::: "memory");  // the next subtile's LDS writes stay after these reads
       }
-      asm volatile("" ::: "memory");  // the next subtile's LDS writes stay after these reads
-      if (u + DEPTH < n_tiles) {
-        load_kv_tile<D, NS>(buf[di], a, ids[di], s_first + (u + DEPTH) * TSTEP, sub_end, t_end,
-                            spb, spb_shift, tok_stride, kvh, lane_off);
-        ids[di] = load_block_ids<NS>(bt_row, s_first + (u + 2 * DEPTH) * TSTEP, sub_end, spb,
-                                     spb_shift, lane);
-      }
+      load_kv_tile<D, NS>(buf[di], a, ids[di], s_first + (u + DEPTH) * TSTEP, sub_end, t_end, spb,
+                          spb_shift, tok_stride, kvh, lane_off_b);
+      ids[di] = load_block_ids<NS>(bt_rs, s_first + (u + 2 * DEPTH) * TSTEP, sub_end, spb,
+                                   spb_shift, lane);
     }
   }
 

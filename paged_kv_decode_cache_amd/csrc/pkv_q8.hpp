@@ -153,28 +153,23 @@ __device__ __forceinline__ void load_kv_tile8(KVTile8<D, NS>& T, const Q8Params&
     const int s = s0 + j;
     const int sib = spb_shift >= 0 ? (s & (spb - 1)) : (s % spb);
     const int64_t p0 = ok ? phys : 0;
-    if (ok) {
-      const int8_t* kp =
-          P.k_codes + ((p0 * a.block_size + sib * 16 + (lane & 15)) * a.Hkv + kvh) * D + 16 * quad;
-      const int8_t* vp =
-          P.v_codes + ((p0 * a.block_size + sib * 16 + (lane & 15)) * a.Hkv + kvh) * D + 16 * quad;
+    // the subtile's codes of head kvh (16 tokens x all heads from its first
+    // row) and its 16 scales, through empty resources when masked out
+    const int64_t co = ((p0 * a.block_size + sib * 16) * a.Hkv + kvh) * D;
+    const int code_bytes = ok ? 16 * a.Hkv * D : 0;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(P.k_codes + co, code_bytes);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(P.v_codes + co, code_bytes);
+    const int lo = (lane & 15) * a.Hkv * D + 16 * quad;
 #pragma unroll
-      for (int c = 0; c < D / 64; ++c) {
-        T.k[j][c] = *reinterpret_cast<const u32x4*>(kp + 64 * c);
-        T.v[j][c] = *reinterpret_cast<const u32x4*>(vp + 64 * c);
-      }
-      const int64_t so = (p0 * a.Hkv + kvh) * a.block_size + sib * 16 + 4 * quad;
-      T.ks[j] = *reinterpret_cast<const f32x4*>(P.k_scales + so);
-      T.vs[j] = *reinterpret_cast<const f32x4*>(P.v_scales + so);
-    } else {
-#pragma unroll
-      for (int c = 0; c < D / 64; ++c) {
-        T.k[j][c] = u32x4{0, 0, 0, 0};
-        T.v[j][c] = u32x4{0, 0, 0, 0};
-      }
-      T.ks[j] = zero4f();
-      T.vs[j] = zero4f();
+    for (int c = 0; c < D / 64; ++c) {
+      T.k[j][c] = __builtin_bit_cast(u32x4, load_b128(kr, lo + 64 * c));
+      T.v[j][c] = __builtin_bit_cast(u32x4, load_b128(vr, lo + 64 * c));
     }
+    const int64_t so = (p0 * a.Hkv + kvh) * a.block_size + sib * 16;
+    const __amdgpu_buffer_rsrc_t ksr = buffer_rsrc(P.k_scales + so, ok ? 64 : 0);
+    const __amdgpu_buffer_rsrc_t vsr = buffer_rsrc(P.v_scales + so, ok ? 64 : 0);
+    T.ks[j] = load_b128(ksr, 16 * quad);
+    T.vs[j] = load_b128(vsr, 16 * quad);
   }
   T.okmask = okm;
   T.full = okm == (1 << NS) - 1 && ((s0 + NS) << 4) <= t_end;
@@ -317,6 +312,7 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   const int spb = a.block_size >> 4;
   const int spb_shift = a.spb_shift;
   const int32_t* bt_row = a.block_tables + (size_t)b * a.max_blocks;
+  const __amdgpu_buffer_rsrc_t bt_rs = buffer_rsrc(bt_row, a.max_blocks * 4);
   constexpr int TSTEP = NW * NS;
   const int t_begin = SPLIT ? p * a.partition_size : 0;
   const int s_first = (t_begin >> 4) + wave * NS;
@@ -324,7 +320,7 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   int ids[DEPTH];
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i)
-    ids[i] = load_block_ids<NS>(bt_row, s_first + i * TSTEP, sub_cap, spb, spb_shift, lane);
+    ids[i] = load_block_ids<NS>(bt_rs, s_first + i * TSTEP, sub_cap, spb, spb_shift, lane);
 
   const int cap = a.max_blocks * a.block_size;
   int ctx = a.context_lens[b];
@@ -347,13 +343,13 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   const float c = fmaxf(neg_scale ? -a.scale_log2 : a.scale_log2, 1.17549435e-38f);
   f16x8 qb[KC];
   {
-    const bool hv = head_col < a.G;
-    const f16* qrow = a.q + ((size_t)b * a.Hq + kvh * a.G + (hv ? head_col : 0)) * D + 16 * quad;
+    // the group's G query rows; columns past G read zeros
+    const __amdgpu_buffer_rsrc_t q_rs =
+        buffer_rsrc(a.q + ((size_t)b * a.Hq + kvh * a.G) * D, a.G * D * 2);
+    const unsigned sign = neg_scale ? 0x80008000u : 0u;
 #pragma unroll
-    for (int m = 0; m < KC; ++m) {
-      const f16x8 v = *reinterpret_cast<const f16x8*>(qrow + 64 * (m >> 1) + 8 * (m & 1));
-      qb[m] = hv ? (neg_scale ? -v : v) : zero8();
-    }
+    for (int m = 0; m < KC; ++m)
+      qb[m] = load_q16(q_rs, (head_col * D + 16 * quad + 64 * (m >> 1) + 8 * (m & 1)) * 2, sign);
   }
   const float rem_mul = (DUAL && g >= 8) ? -1.0f : 0.0f;
   SoftmaxState<D> st;
@@ -368,26 +364,22 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   KVTile8<D, NS> buf[DEPTH];
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) {
-    if (i < n_tiles) {
-      load_kv_tile8<D, NS>(buf[i], P, ids[i], s_first + i * TSTEP, sub_end, t_end, spb,
-                           spb_shift, kvh, lane);
-      ids[i] = load_block_ids<NS>(bt_row, s_first + (i + DEPTH) * TSTEP, sub_end, spb,
-                                  spb_shift, lane);
-    }
+    // past the wave's last tile: empty resources, no memory access
+    load_kv_tile8<D, NS>(buf[i], P, ids[i], s_first + i * TSTEP, sub_end, t_end, spb, spb_shift,
+                         kvh, lane);
+    ids[i] = load_block_ids<NS>(bt_rs, s_first + (i + DEPTH) * TSTEP, sub_end, spb, spb_shift,
+                                lane);
   }
   for (int u0 = 0; u0 < n_tiles; u0 += DEPTH) {
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) {
       const int u = u0 + i;
-      if (u < n_tiles) {
+      if (u < n_tiles)
         consume_tile8<D, NS, DUAL>(buf[i], st, lsum, qb, stage, c, t_end, lane, rem_mul);
-        if (u + DEPTH < n_tiles) {
-          load_kv_tile8<D, NS>(buf[i], P, ids[i], s_first + (u + DEPTH) * TSTEP, sub_end, t_end,
-                               spb, spb_shift, kvh, lane);
-          ids[i] = load_block_ids<NS>(bt_row, s_first + (u + 2 * DEPTH) * TSTEP, sub_end, spb,
-                                      spb_shift, lane);
-        }
-      }
+      load_kv_tile8<D, NS>(buf[i], P, ids[i], s_first + (u + DEPTH) * TSTEP, sub_end, t_end,
+                           spb, spb_shift, kvh, lane);
+      ids[i] = load_block_ids<NS>(bt_rs, s_first + (u + 2 * DEPTH) * TSTEP, sub_end, spb,
+                                  spb_shift, lane);
     }
   }
 
