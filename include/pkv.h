@@ -241,7 +241,7 @@ int paged_attention_decode_split(float* partial_out, float* partial_lse,
  *   partial_lse       [B, num_q_heads, max_partitions] fp32 workspace, every
  *                     32-bit word all ones (0xFFFFFFFF) before the first call;
  *                     every call leaves them so.  num_q_heads / num_kv_heads *
- *                     max_partitions * head_dim * 4 must not exceed INT32_MAX
+ *                     max_partitions * head_dim * 4 must be below 2^30
  *                     (else PKV_ERR_UNSUPPORTED).  Not to be shared with
  *                     paged_attention_decode_split, which leaves values there.
  *   counters          [B, num_kv_heads] int32 workspace: must be zero before

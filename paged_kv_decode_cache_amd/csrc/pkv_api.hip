@@ -426,8 +426,9 @@ int paged_decode_step(void* out, float* lse_out, void* k_pool, void* v_pool, con
   }
   const int64_t grid = (int64_t)B * num_kv_heads * max_partitions;
   if (grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
-  // one buffer resource spans a pair's partials (32-bit byte offsets)
-  if ((int64_t)(num_q_heads / num_kv_heads) * max_partitions * head_dim * 4 > INT32_MAX)
+  // one buffer resource spans a pair's partials; its byte offsets, and the
+  // out-of-range offset the merge uses for rows it skips (2^30), must not meet
+  if ((int64_t)(num_q_heads / num_kv_heads) * max_partitions * head_dim * 4 >= (1 << 30))
     return PKV_ERR_UNSUPPORTED;
 
   AttnParams p = {};

@@ -460,25 +460,89 @@ __device__ __forceinline__ void merge_waves_impl(const SoftmaxState<D>& st, floa
   }
 }
 
+constexpr int kMergeSlots = 512;  // >= 16 heads x 128/4 dims
+constexpr int kSpinLimit = 1 << 20;
+
+// Streaming LSE merge of one thread's rows (partitions grp, grp + ngroups, ...
+// of head hh, dims 4cc..4cc+3) into (M, L, acc), BATCH rows in flight.
+template <int D, int BATCH>
+__device__ __forceinline__ void merge_rows(__amdgpu_buffer_rsrc_t po_rs,
+                                           __amdgpu_buffer_rsrc_t pl_rs, int Pm, int np,
+                                           int p_own, int grp, int ngroups, int hh, int cc,
+                                           f32x4 own_x, float own_l, float& M, float& L,
+                                           f32x4& acc) {
+  for (int q0 = grp; q0 < np; q0 += BATCH * ngroups) {
+    // Straight-line code for the common case: every row of the batch is
+    // requested at once (rows past np, and the merger's own, through an
+    // out-of-range offset: zeros, no memory access), checked with one
+    // vector test, and merged with selects.  Rows not written yet are
+    // requested again in a wave-uniform loop, the only branch.
+    int xo[BATCH], lo[BATCH];
+    f32x4 x[BATCH];
+    float l[BATCH];
+    bool ok[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int q = q0 + j * ngroups;
+      const bool other = q < np && q != p_own;
+      xo[j] = other ? ((hh * Pm + q) * D + 4 * cc) * 4 : kOutOfRange;
+      lo[j] = other ? (hh * Pm + q) * 4 : kOutOfRange;
+      x[j] = load_coherent4(po_rs, xo[j]);
+      l[j] = load_coherent1(pl_rs, lo[j]);
+    }
+    bool all_ok = true;
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      ok[j] = is_written(x[j][0]) && is_written(x[j][1]) && is_written(x[j][2]) &&
+              is_written(x[j][3]) && is_written(l[j]);
+      all_ok = all_ok && ok[j];
+    }
+    for (int spin = 0; spin < kSpinLimit && !__all(all_ok); ++spin) {
+      __builtin_amdgcn_s_sleep(2);
+      asm volatile("" ::: "memory");
+      all_ok = true;
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const f32x4 nx = load_coherent4(po_rs, ok[j] ? kOutOfRange : xo[j]);
+        const float nl = load_coherent1(pl_rs, ok[j] ? kOutOfRange : lo[j]);
+        x[j] = ok[j] ? x[j] : nx;
+        l[j] = ok[j] ? l[j] : nl;
+        ok[j] = is_written(x[j][0]) && is_written(x[j][1]) && is_written(x[j][2]) &&
+                is_written(x[j][3]) && is_written(l[j]);
+        all_ok = all_ok && ok[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int q = q0 + j * ngroups;
+      const bool mine = q == p_own;
+      const float lq = q < np ? (mine ? own_l : l[j]) : -INFINITY;
+      const f32x4 xq = mine ? own_x : x[j];
+      const float Mn = fmaxf(M, lq);
+      const float mu = Mn == -INFINITY ? 0.0f : Mn;
+      const float sa = fast_exp2((M - mu) * kLog2e);  // 1 while M holds; 0 from -inf
+      const float sb = fast_exp2((lq - mu) * kLog2e);  // 0 for rows past np
+      acc = acc * sa + xq * sb;
+      L = L * sa + sb;
+      M = Mn;
+    }
+  }
+}
+
 // Cross-workgroup merge of the fused step, run by the merging workgroup of
 // (b, kvh) once its own partition (p_own, held in LDS at `own`) is final.
 // Threads cover (head, 4 dims) x partition groups with a streaming LSE merge,
 // and the groups combine through LDS.  Every other partition's row is polled
-// until none of its words is still unwritten, then set back to unwritten for
-// the next launch (data words once the thread has read all its rows; lse
-// words after a barrier, since all threads of a head read them).
+// until none of its words is still unwritten, and set back to unwritten for
+// the next launch once the output is stored.
 // The wait ends: the other workgroups of the pair took their tickets before
 // this one took the last, so they are running and wait on nothing.
-constexpr int kMergeSlots = 512;  // >= 16 heads x 128/4 dims
-constexpr int kSpinLimit = 1 << 20;
-
 template <int D, int NW>
 __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int np, int p_own,
                                       const float* own /* [16][D] o, then [16] lse */,
                                       float* msm /* 6 * kMergeSlots floats */) {
   constexpr int NT = NW * 64;
   constexpr int TPR = D / 4;
-  constexpr int BATCH = 8;  // rows in flight per thread
   const int t = threadIdx.x;
   const int G = a.G;
   const int Pm = a.max_partitions;
@@ -496,56 +560,18 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
     const int hc = slot % per_group;
     const int hh = hc / TPR;
     const int cc = hc % TPR;
+    const f32x4 own_x = *reinterpret_cast<const f32x4*>(own + hh * D + 4 * cc);
+    const float own_l = own[16 * D + hh];
     float M = -INFINITY, L = 0.0f;
     f32x4 acc = zero4f();
-    for (int q0 = grp; q0 < np; q0 += BATCH * ngroups) {
-      f32x4 x[BATCH];
-      float l[BATCH];
-#pragma unroll
-      for (int j = 0; j < BATCH; ++j) {
-        const int q = q0 + j * ngroups;
-        if (q < np && q != p_own) {
-          x[j] = load_coherent4(po_rs, ((hh * Pm + q) * D + 4 * cc) * 4);
-          l[j] = load_coherent1(pl_rs, (hh * Pm + q) * 4);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < BATCH; ++j) {
-        const int q = q0 + j * ngroups;
-        if (q < np) {
-          if (q == p_own) {
-            x[j] = *reinterpret_cast<const f32x4*>(own + hh * D + 4 * cc);
-            l[j] = own[16 * D + hh];
-          } else {
-            const int xo = ((hh * Pm + q) * D + 4 * cc) * 4;
-            for (int spin = 0; spin < kSpinLimit; ++spin) {
-              if (is_written(x[j][0]) && is_written(x[j][1]) && is_written(x[j][2]) &&
-                  is_written(x[j][3]) && is_written(l[j]))
-                break;
-              __builtin_amdgcn_s_sleep(2);
-              asm volatile("" ::: "memory");
-              x[j] = load_coherent4(po_rs, xo);
-              l[j] = load_coherent1(pl_rs, (hh * Pm + q) * 4);
-            }
-          }
-          const float lq = l[j];
-          if (lq > M) {
-            const float sc = fast_exp2((M - lq) * kLog2e);  // 0 from -inf
-            acc *= sc;
-            L *= sc;
-            M = lq;
-          }
-          const float w = fast_exp2((lq - M) * kLog2e);
-          acc += w * x[j];
-          L += w;
-        }
-      }
-    }
-    // back to "not written", after every row is read: a store issued between
-    // two batches of loads would hold up the next batch (stores and loads
-    // share one in-order counter)
-    for (int q = grp; q < np; q += ngroups)
-      if (q != p_own) store_coherent4(po_rs, ((hh * Pm + q) * D + 4 * cc) * 4, unwritten4);
+    // rows in flight per thread: its share of the pair's partitions, 2 to 8
+    const int rows = (np + ngroups - 1) / ngroups;
+    if (rows <= 2)
+      merge_rows<D, 2>(po_rs, pl_rs, Pm, np, p_own, grp, ngroups, hh, cc, own_x, own_l, M, L, acc);
+    else if (rows <= 4)
+      merge_rows<D, 4>(po_rs, pl_rs, Pm, np, p_own, grp, ngroups, hh, cc, own_x, own_l, M, L, acc);
+    else
+      merge_rows<D, 8>(po_rs, pl_rs, Pm, np, p_own, grp, ngroups, hh, cc, own_x, own_l, M, L, acc);
     float* r = msm + 6 * slot;
     r[0] = M;
     r[1] = L;
@@ -555,11 +581,6 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
     r[5] = acc[3];
   }
   __syncthreads();
-  for (int i = t; i < G * np; i += NT) {
-    const int q = i % np;
-    if (q != p_own)
-      store_coherent1(pl_rs, ((i / np) * Pm + q) * 4, __builtin_bit_cast(float, kUnwritten));
-  }
   for (int hc = t; hc < per_group; hc += NT) {
     float M = -INFINITY;
     for (int gi = 0; gi < ngroups; ++gi) M = fmaxf(M, msm[6 * (gi * per_group + hc)]);
@@ -584,6 +605,23 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
     *reinterpret_cast<f16x4*>(a.out + ((size_t)b * a.Hq + h) * D + 4 * cc) = o;
     if (a.lse_out != nullptr && cc == 0)
       a.lse_out[(size_t)b * a.Hq + h] = L > 0.0f ? M + logf(L) : -INFINITY;
+  }
+  // Back to "not written" for the next launch, last: a store issued between
+  // two batches of loads holds up the next batch (loads and stores count down
+  // one in-order counter), and one pending before the combine above made it
+  // wait for the write-through of every reset.  Data words: each thread's own
+  // rows; lse words: read by every thread of a head, so after the barrier.
+  for (int slot = t; slot < nslots; slot += NT) {
+    const int grp = slot / per_group;
+    const int hh = (slot % per_group) / TPR;
+    const int cc = (slot % per_group) % TPR;
+    for (int q = grp; q < np; q += ngroups)
+      if (q != p_own) store_coherent4(po_rs, ((hh * Pm + q) * D + 4 * cc) * 4, unwritten4);
+  }
+  for (int i = t; i < G * np; i += NT) {
+    const int q = i % np;
+    if (q != p_own)
+      store_coherent1(pl_rs, ((i / np) * Pm + q) * 4, __builtin_bit_cast(float, kUnwritten));
   }
 }
 
@@ -760,19 +798,6 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
     }
   }
 
-  // Fused step: the append of the new token's row of this head.
-  if (owns_new && slot >= 0 && slot < (int64_t)a.num_blocks * a.block_size) {
-    f16* kd = a.k_pool_w + (slot * Hkv + kvh) * D + 8 * quad;
-    f16* vd = a.v_pool_w + (slot * Hkv + kvh) * D + 8 * quad;
-    if (wave == 0 && g == 0) {
-#pragma unroll
-      for (int m = 0; m < KC; ++m) {
-        *reinterpret_cast<f16x8*>(kd + 32 * m) = kn[m];
-        *reinterpret_cast<f16x8*>(vd + 32 * m) = vn[m];
-      }
-    }
-  }
-
   // DUAL: fold the remainder columns (8..15) into the head columns (0..7).
   if (DUAL) {
 #pragma unroll
@@ -797,6 +822,20 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
     s_merge = m;
   }
   if (NW == 1 && STEP) __syncthreads();
+
+  // Fused step: the append of the new token's row of this head (after the
+  // ticket is read: the wait for it would otherwise include these stores).
+  if (owns_new && slot >= 0 && slot < (int64_t)a.num_blocks * a.block_size) {
+    f16* kd = a.k_pool_w + (slot * Hkv + kvh) * D + 8 * quad;
+    f16* vd = a.v_pool_w + (slot * Hkv + kvh) * D + 8 * quad;
+    if (wave == 0 && g == 0) {
+#pragma unroll
+      for (int m = 0; m < KC; ++m) {
+        *reinterpret_cast<f16x8*>(kd + 32 * m) = kn[m];
+        *reinterpret_cast<f16x8*>(vd + 32 * m) = vn[m];
+      }
+    }
+  }
 
   // Final value for column block db of this lane's head.
   const bool emits = (DUAL ? g < 8 : true) && head_col < a.G;

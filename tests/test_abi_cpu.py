@@ -225,6 +225,42 @@ def test_prefill_empty_is_noop():
     assert _prefill(lib, maxq=0) == 0
 
 
+def _step(lib, **kw):
+    a = dict(out=A16, lse=None, k=C16, v=D16, q=B16, kn=0x70000, vn=0x80000, slots=0x90000,
+             bt=E16, ctx=F16, po=0xA0000, pl=0xB0000, cnt=0xC0000, B=2, Hq=14, Hkv=2, D=64,
+             bs=16, NB=10, maxb=4, P=32, Pm=2, scale=0.125)
+    a.update(kw)
+    return lib.paged_decode_step(a["out"], a["lse"], a["k"], a["v"], a["q"], a["kn"], a["vn"],
+                                 a["slots"], a["bt"], a["ctx"], a["po"], a["pl"], a["cnt"],
+                                 a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["maxb"],
+                                 a["P"], a["Pm"], a["scale"], None)
+
+
+STEP_BAD = [
+    ("null out", dict(out=None), -1),
+    ("null partials", dict(po=None), -1),
+    ("null counters", dict(cnt=None), -1),
+    ("misaligned partials", dict(po=0xA0000 + 4), -1),
+    ("misaligned new key", dict(kn=0x70000 + 2), -1),
+    ("partition not a block multiple", dict(P=24), -1),
+    ("partitions do not cover the table", dict(Pm=1), -1),
+    # one resource spans a (sequence, KV head)'s partials: G * Pm * D * 4 < 2^30
+    ("partials of a pair past 2^30 bytes", dict(Hq=16, Hkv=1, D=128, maxb=131072, P=16,
+                                                Pm=131072), -2),
+]
+
+
+@host_only
+@pytest.mark.parametrize("name,kw,code", STEP_BAD, ids=[c[0] for c in STEP_BAD])
+def test_step_rejects(name, kw, code):
+    assert _step(pkv.load_library(), **kw) == code
+
+
+@host_only
+def test_step_batch0_is_noop():
+    assert _step(pkv.load_library(), B=0) == 0
+
+
 def test_binding_rejects_cpu_tensors():
     q = torch.zeros((1, 2, 64), dtype=torch.float16)
     kp = torch.zeros((2, 16, 1, 64), dtype=torch.float16)
