@@ -244,7 +244,9 @@ int paged_attention_decode_split(float* partial_out, float* partial_lse,
  *                     max_partitions * head_dim * 4 must be below 2^30
  *                     (else PKV_ERR_UNSUPPORTED).  Not to be shared with
  *                     paged_attention_decode_split, which leaves values there.
- *   counters          [B, num_kv_heads] int32 workspace: must be zero before
+ *   counters          [B, num_kv_heads, 32] int32 workspace (one 128-byte
+ *                     line per sequence and KV head, so tickets of different
+ *                     pairs never contend for a line): must be zero before
  *                     the first call; every call leaves it zero.
  * Calls that share a workspace must be ordered by a stream; a call that
  * faults or is aborted leaves it undefined (initialise it again).

@@ -371,6 +371,9 @@ def split_reduce(partial_out, partial_lse, context_lens, partition_size, out=Non
     return (out, lse_out) if lse_out is not None else out
 
 
+COUNTER_STRIDE = 32  # int32 words per ticket counter (one 128-byte line)
+
+
 class StepWorkspace:
     """Device workspace of paged_decode_step: split partials, every word all
     ones (0xFFFFFFFF, "not written"), and the per-(sequence, KV head) ticket
@@ -383,7 +386,9 @@ class StepWorkspace:
                                        dtype=torch.float32, device=device)
         self.partial_lse = torch.empty((B, num_q_heads, max_partitions), dtype=torch.float32,
                                        device=device)
-        self.counters = torch.empty((B, num_kv_heads), dtype=torch.int32, device=device)
+        # one 128-byte line of ticket counter per (sequence, KV head)
+        self.counters = torch.empty((B, num_kv_heads, COUNTER_STRIDE), dtype=torch.int32,
+                                    device=device)
         self.max_partitions = max_partitions
         self.reset()
 
@@ -406,10 +411,10 @@ def paged_decode_step(q, k_pool, v_pool, block_tables, context_lens, scale, part
     ws = workspace
     _need(ws.partial_out, "partial_out", torch.float32, 4, dev)
     _need(ws.partial_lse, "partial_lse", torch.float32, 3, dev)
-    _need(ws.counters, "counters", torch.int32, 2, dev)
+    _need(ws.counters, "counters", torch.int32, 3, dev)
     Pm = ws.max_partitions
     if ws.partial_out.shape != (B, Hq, Pm, D) or ws.partial_lse.shape != (B, Hq, Pm) or \
-            ws.counters.shape != (B, Hkv):
+            ws.counters.shape != (B, Hkv, COUNTER_STRIDE):
         raise ValueError("workspace shapes do not match the call")
     if slot_mapping is not None:
         _need(k_new, "k_new", torch.float16, 3, dev)

@@ -47,6 +47,10 @@ typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.44269504088896340736f;
+// Ticket counters of the fused step, one per 128-byte line: the tickets of
+// different (sequence, KV head) pairs never contend for one line (measured:
+// B=8 x 4096 with 16 partitions per pair, 12.0 -> 10.5 us).
+constexpr int kCounterStride = 32;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 struct AttnParams {
@@ -69,7 +73,8 @@ struct AttnParams {
   const f16* k_new;     // [B, Hkv, D] the step's new token per sequence
   const f16* v_new;
   const int64_t* slot_mapping;  // [B] or null (no append)
-  int32_t* counters;    // [B, Hkv] finished-partition counters, zero between calls
+  int32_t* counters;    // [B, Hkv, kCounterStride] ticket counters (word 0 used), zero
+                        // between calls
   float* lse_out;       // [B, Hq] or null
 };
 
@@ -781,8 +786,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   // only at the end).
   int ticket = 0;
   if (STEP && n_parts > 1 && threadIdx.x == 0)
-    ticket = __hip_atomic_fetch_add(a.counters + (size_t)b * Hkv + kvh, 1, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
+    ticket = __hip_atomic_fetch_add(a.counters + ((size_t)b * Hkv + kvh) * kCounterStride, 1,
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (int u0 = 0; u0 < n_tiles; u0 += DEPTH) {
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) {
@@ -817,8 +822,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   if (STEP && n_parts > 1 && threadIdx.x == 0) {
     const bool m = ticket == n_parts - 1;
     if (m)
-      __hip_atomic_store(a.counters + (size_t)b * Hkv + kvh, 0, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.counters + ((size_t)b * Hkv + kvh) * kCounterStride, 0,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_merge = m;
   }
   if (NW == 1 && STEP) __syncthreads();
