@@ -201,6 +201,7 @@ struct KVTile {
   f16x8 v[NS][D / 32];
   int okmask;  // bit j: subtile j was loaded (valid block id, inside the range)
   int s0;
+  int new_phys;  // block id of subtile s_new when the tile holds it, else -1
   bool full;   // every position of the tile is attended: no masking needed
 };
 
@@ -227,7 +228,7 @@ template <int D, int NS>
 __device__ __forceinline__ void load_kv_tile(KVTile<D, NS>& T, const AttnParams& a, int ids,
                                              int s0, int sub_end, int t_end, int spb,
                                              int spb_shift, int64_t tok_stride, int kvh,
-                                             int lane_off_b) {
+                                             int lane_off_b, int s_new = -1) {
   constexpr int KC = D / 32;
   const int sub_bytes = 32 * (int)tok_stride;
   T.s0 = s0;
@@ -250,6 +251,8 @@ __device__ __forceinline__ void load_kv_tile(KVTile<D, NS>& T, const AttnParams&
     }
   }
   T.okmask = okm;
+  T.new_phys =
+      s_new >= s0 && s_new < s0 + NS ? __builtin_amdgcn_readlane(ids, s_new - s0) : -1;
   T.full = okm == (1 << NS) - 1 && ((s0 + NS) << 4) <= t_end;
 }
 
@@ -287,14 +290,14 @@ __device__ __forceinline__ float max_across_quads(float x) {
 //   rem_mul: -1 in DUAL remainder columns, else 0 (selects P or P - fp16(P)
 //   with one exact fused multiply-add).
 //   SUB: position (s_new, tok_new) takes K/V from kn/vn (the fused step's new
-//   token, which this launch also writes to the pool) when its slot is the
-//   position's slot: new_phys * block_size + new_off.
+//   token, which this launch also writes to the pool) when `slot` is the
+//   position's slot in the table: T.new_phys * block_size + new_off.
 template <int D, int NS, bool DUAL, bool SUB>
 __device__ __forceinline__ void consume_tile(KVTile<D, NS>& T, SoftmaxState<D>& st,
                                              const f16x8 (&qb)[D / 32], f16* stage, float c,
                                              int t_end, int lane, f16x4 ones, float rem_mul,
-                                             int s_new, int tok_new, int64_t slot, int new_phys,
-                                             int new_off, int block_size,
+                                             int s_new, int tok_new, int64_t slot, int new_off,
+                                             int block_size,
                                              const f16x8 (&kn)[D / 32],
                                              const f16x8 (&vn)[D / 32]) {
   constexpr int KC = D / 32;
@@ -302,8 +305,7 @@ __device__ __forceinline__ void consume_tile(KVTile<D, NS>& T, SoftmaxState<D>& 
   constexpr int ROW = D + 4;
   const int g = lane & 15;
   const int quad = lane >> 4;
-  if (SUB && s_new >= T.s0 && s_new < T.s0 + NS &&
-      (int64_t)new_phys * block_size + new_off == slot) {
+  if (SUB && T.new_phys >= 0 && (int64_t)T.new_phys * block_size + new_off == slot) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const bool mine = T.s0 + j == s_new && (lane & 15) == tok_new;
@@ -683,6 +685,10 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   for (int i = 0; i < DEPTH; ++i)
     ids[i] = load_block_ids<NS>(bt_rs, s_first + i * TSTEP, sub_cap, spb, spb_shift, lane);
 
+  // Fused step: the new token's slot, requested before the length so that
+  // one round trip brings both (the owner of the new token must not wait for
+  // it after the length is known).
+  const int64_t slot_in = STEP && a.slot_mapping != nullptr ? a.slot_mapping[b] : -1;
   const int cap = a.max_blocks * a.block_size;
   int ctx = a.context_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
@@ -704,22 +710,18 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   // writes the new token's K/V row of its head into the pool (at the end of
   // the kernel), and takes that position's K/V from k_new/v_new instead of
   // the pool when the slot is the position's slot in the block table (so the
-  // launch never reads its own write).  Everything it needs is requested here
-  // and waited for only where it is used.
+  // launch never reads its own write).  That block id comes with the tile
+  // that holds the position; nothing here waits for a load after the length.
   const bool owns_new =
       STEP && a.slot_mapping != nullptr && p == (ctx > 0 ? (ctx - 1) / a.partition_size : 0);
-  int64_t slot = -1;
-  int new_phys = -1;
+  const int64_t slot = owns_new ? slot_in : -1;
   int s_new = -1, tok_new = -1, new_off = 0;
   f16x8 kn[KC], vn[KC];
   const size_t new_row = ((size_t)b * Hkv + kvh) * D;
   if (owns_new) {
-    slot = a.slot_mapping[b];
     if (ctx > 0) {
       const int pos = ctx - 1;
-      const int blk = pos / a.block_size;
-      new_phys = bt_row[blk];
-      new_off = pos - blk * a.block_size;
+      new_off = pos % a.block_size;
       s_new = pos >> 4;
       tok_new = pos & 15;
     }
@@ -778,7 +780,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) {
     load_kv_tile<D, NS>(buf[i], a, ids[i], s_first + i * TSTEP, sub_end, t_end, spb, spb_shift,
-                        tok_stride, kvh, lane_off_b);
+                        tok_stride, kvh, lane_off_b, s_new);
     ids[i] = load_block_ids<NS>(bt_rs, s_first + (i + DEPTH) * TSTEP, sub_end, spb, spb_shift,
                                 lane);
   }
@@ -794,10 +796,9 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
       const int u = u0 + i;
       if (u < n_tiles)
         consume_tile<D, NS, DUAL, STEP>(buf[i], st, qb, stage, c, t_end, lane, ones, rem_mul,
-                                        s_new, tok_new, slot, new_phys, new_off,
-                                        a.block_size, kn, vn);
+                                        s_new, tok_new, slot, new_off, a.block_size, kn, vn);
       load_kv_tile<D, NS>(buf[i], a, ids[i], s_first + (u + DEPTH) * TSTEP, sub_end, t_end, spb,
-                          spb_shift, tok_stride, kvh, lane_off_b);
+                          spb_shift, tok_stride, kvh, lane_off_b, s_new);
       ids[i] = load_block_ids<NS>(bt_rs, s_first + (u + 2 * DEPTH) * TSTEP, sub_end, spb,
                                   spb_shift, lane);
     }
