@@ -406,19 +406,29 @@ __device__ __forceinline__ void consume_tile(KVTile<D, NS>& T, SoftmaxState<D>& 
   // lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4 point at.  Lane j of quad q points
   // at V[4q + j/4][16 db + 4 (j%4) ..], so lane (q, i) receives
   // V[4q + k][16 db + i] for k = 0..3: the A operand of the 16x16x16 MFMA.
+  // Without DUAL both parts of P go into one 16x16x32 MFMA: its lane (q, i)
+  // holds k = 8q .. 8q + 7, taken as the lane's 4 tokens' high parts then
+  // their remainders (B), against the same 4 V values twice (A).
   const f16* tr = stage + (4 * quad + (g >> 2)) * ROW + 4 * (g & 3);
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    st.lsum = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, ph[j], st.lsum, 0, 0, 0);
-    if (!DUAL) st.lsum = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pl[j], st.lsum, 0, 0, 0);
+    const f16x8 pb = __builtin_shufflevector(ph[j], pl[j], 0, 1, 2, 3, 4, 5, 6, 7);
+    if (DUAL)
+      st.lsum = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, ph[j], st.lsum, 0, 0, 0);
+    else
+      st.lsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          __builtin_shufflevector(ones, ones, 0, 1, 2, 3, 4, 5, 6, 7), pb, st.lsum, 0, 0, 0);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       typedef short s16x4 __attribute__((ext_vector_type(4)));
       const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s16x4*)(tr + j * 16 * ROW + 16 * db));
       const f16x4 va = __builtin_bit_cast(f16x4, raw);
-      st.o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph[j], st.o[db], 0, 0, 0);
-      if (!DUAL) st.o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pl[j], st.o[db], 0, 0, 0);
+      if (DUAL)
+        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph[j], st.o[db], 0, 0, 0);
+      else
+        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            __builtin_shufflevector(va, va, 0, 1, 2, 3, 0, 1, 2, 3), pb, st.o[db], 0, 0, 0);
     }
   }
   asm volatile("" ::: "memory");  // next tile's LDS writes stay after these reads

@@ -203,17 +203,23 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams pp
                 f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                            (__attribute__((address_space(3))) s16x4*)(tr + 16 * db)));
         }
+        // P.V with both parts of P in one 16x16x32 MFMA: in the k = 32 layout
+        // this lane holds k = 8 quad .. 8 quad + 7, taken here as its own 4
+        // tokens' high parts then their remainders (B operand), against the
+        // same 4 tokens' V values twice (A operand).  The product is
+        // V.P_high + V.P_remainder at half the MFMA issue of two 16x16x16.
+        const f16x8 ones8 = __builtin_shufflevector(ones, ones, 0, 1, 2, 3, 4, 5, 6, 7);
+        f16x8 va8[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          va8[db] = __builtin_shufflevector(va[db], va[db], 0, 1, 2, 3, 0, 1, 2, 3);
 #pragma unroll
         for (int t = 0; t < NCT; ++t) {
-          st[t].lsum = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, ph[t], st[t].lsum, 0, 0, 0);
-          st[t].lsum = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pl[t], st[t].lsum, 0, 0, 0);
+          const f16x8 pb = __builtin_shufflevector(ph[t], pl[t], 0, 1, 2, 3, 4, 5, 6, 7);
+          st[t].lsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8, pb, st[t].lsum, 0, 0, 0);
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            st[t].o[db] =
-                __builtin_amdgcn_mfma_f32_16x16x16f16(va[db], ph[t], st[t].o[db], 0, 0, 0);
-            st[t].o[db] =
-                __builtin_amdgcn_mfma_f32_16x16x16f16(va[db], pl[t], st[t].o[db], 0, 0, 0);
-          }
+          for (int db = 0; db < NDB; ++db)
+            st[t].o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va8[db], pb, st[t].o[db], 0, 0, 0);
         }
         asm volatile("" ::: "memory");  // the next subtile's LDS writes stay after these reads
       }

@@ -276,8 +276,14 @@ __device__ __forceinline__ void consume_tile8(KVTile8<D, NS>& T, SoftmaxState<D>
       const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s16x4*)(tr + j * 16 * ROW + 16 * db));
       const f16x4 va = __builtin_bit_cast(f16x4, raw);
-      st.o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph[j], st.o[db], 0, 0, 0);
-      if (!DUAL) st.o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pl[j], st.o[db], 0, 0, 0);
+      // without DUAL: both parts of P in one 16x16x32 MFMA (as in the fp16
+      // kernel: the lane's high parts then remainders against V twice)
+      if (DUAL)
+        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph[j], st.o[db], 0, 0, 0);
+      else
+        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            __builtin_shufflevector(va, va, 0, 1, 2, 3, 0, 1, 2, 3),
+            __builtin_shufflevector(ph[j], pl[j], 0, 1, 2, 3, 4, 5, 6, 7), st.o[db], 0, 0, 0);
     }
   }
   asm volatile("" ::: "memory");
