@@ -287,8 +287,10 @@ __device__ __forceinline__ float max_across_quads(float x) {
 //   at -inf and rounds every weight of a uniform softmax to exactly 1).
 //   ones: the A operand with row 0 all ones, so one more MFMA per part sums
 //   the weights of every column (no per-value VALU adds).
-//   rem_mul: -1 in DUAL remainder columns, else 0 (selects P or P - fp16(P)
-//   with one exact fused multiply-add).
+//   rem_mul: with DUAL, -1 in the remainder columns, else 0 (selects P or
+//   P - fp16(P) with one exact fused multiply-add); without DUAL, -1 (the
+//   remainder's multiplier).  Opaque to the compiler, so the remainder stays
+//   one mixed-precision FMA rather than a convert, a subtract and a convert.
 //   SUB: position (s_new, tok_new) takes K/V from kn/vn (the fused step's new
 //   token, which this launch also writes to the pool) when `slot` is the
 //   position's slot in the table: T.new_phys * block_size + new_off.
@@ -372,8 +374,8 @@ __device__ __forceinline__ void consume_tile(KVTile<D, NS>& T, SoftmaxState<D>& 
       } else {
         ph[j][v] = h0;
         ph[j][v + 1] = h1;
-        pl[j][v] = (f16)fmaf((float)h0, -1.0f, pv[v]);
-        pl[j][v + 1] = (f16)fmaf((float)h1, -1.0f, pv[v + 1]);
+        pl[j][v] = (f16)fmaf((float)h0, rem_mul, pv[v]);
+        pl[j][v + 1] = (f16)fmaf((float)h1, rem_mul, pv[v + 1]);
       }
     }
   }
@@ -770,7 +772,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   f16x4 ones;
 #pragma unroll
   for (int i = 0; i < 4; ++i) ones[i] = (f16)(g == 0 ? 1.0f : 0.0f);
-  const float rem_mul = (DUAL && g >= 8) ? -1.0f : 0.0f;
+  float rem_mul = DUAL ? (g >= 8 ? -1.0f : 0.0f) : -1.0f;
+  asm volatile("" : "+v"(rem_mul));
 
   SoftmaxState<D> st;
 #pragma unroll

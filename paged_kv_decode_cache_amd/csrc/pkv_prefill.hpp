@@ -102,6 +102,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams pp
   }
   // positions every valid column sees: [0, pos_first]
   const int vis_all = pos_first;
+  // the remainder P - fp16(P) as one mixed-precision FMA: the multiplier -1
+  // is opaque to the compiler, which otherwise emits convert, subtract, convert
+  float neg1 = -1.0f;
+  asm volatile("" : "+v"(neg1));
   f16x4 ones;
 #pragma unroll
   for (int i = 0; i < 4; ++i) ones[i] = (f16)(g == 0 ? 1.0f : 0.0f);
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams pp
             const float p = fast_exp2(fmaf(sc[t][v], c_scale, neg_m));
             const f16 h = (f16)p;
             ph[t][v] = h;
-            pl[t][v] = (f16)fmaf((float)h, -1.0f, p);
+            pl[t][v] = (f16)fmaf((float)h, neg1, p);
           }
         }
         // V subtile -> LDS row-major (rows no column sees as zeros), then the

@@ -244,7 +244,7 @@ __device__ __forceinline__ void consume_tile8(KVTile8<D, NS>& T, SoftmaxState<D>
         ph[j][v] = (f16)fmaf((float)h, rem_mul, pv[v]);
       } else {
         ph[j][v] = h;
-        pl[j][v] = (f16)fmaf((float)h, -1.0f, pv[v]);
+        pl[j][v] = (f16)fmaf((float)h, rem_mul, pv[v]);
       }
     }
   }
@@ -357,7 +357,8 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
     for (int m = 0; m < KC; ++m)
       qb[m] = load_q16(q_rs, (head_col * D + 16 * quad + 64 * (m >> 1) + 8 * (m & 1)) * 2, sign);
   }
-  const float rem_mul = (DUAL && g >= 8) ? -1.0f : 0.0f;
+  float rem_mul = DUAL ? (g >= 8 ? -1.0f : 0.0f) : -1.0f;  // as in the fp16 kernel
+  asm volatile("" : "+v"(rem_mul));
   SoftmaxState<D> st;
 #pragma unroll
   for (int i = 0; i < NDB; ++i) st.o[i] = zero4f();
