@@ -142,6 +142,8 @@ EDGE = [
     ("g2_bs256", 4, 2, 64, 256, [255, 256, 257, 2000]),
     ("g1_d64_bs32", 3, 3, 64, 32, [5, 32, 96, 1000]),
     ("g8_d128_bs16", 8, 1, 128, 16, [16, 48, 4096]),
+    ("g12_d64_bs16", 12, 1, 64, 16, [1, 100, 777]),      # 9..15 heads: padded columns
+    ("g10_d128_bs32", 20, 2, 128, 32, [31, 500, 2049]),
 ]
 
 

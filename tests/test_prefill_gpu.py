@@ -46,6 +46,7 @@ CASES = [
     ("g4_d128", 32, 8, 128, 16, [129, 1024], [16, 200]),
     ("mha_bs64", 4, 4, 64, 64, [200, 64], [37, 64]),
     ("g2_bs256", 4, 2, 64, 256, [513, 1000], [100, 1]),
+    ("g12_d64", 12, 1, 64, 16, [90, 600], [33, 100]),
 ]
 
 

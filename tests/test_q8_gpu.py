@@ -102,6 +102,7 @@ def test_split_q8_matches_oracle(name, P):
     (32, 8, 128, 16, [100, 1, 900]),
     (4, 4, 64, 64, [3, 77, 500]),
     (14, 2, 64, 16, [0, 1, 15, 16, 17, 1000]),
+    (12, 1, 64, 16, [1, 90, 700]),
 ])
 def test_decode_q8_edge_shapes(Hq, Hkv, D, bs, lens):
     c = workloads.custom_case("q8edge", B=len(lens), Hq=Hq, Hkv=Hkv, D=D, block_size=bs,

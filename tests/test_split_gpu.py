@@ -131,7 +131,7 @@ def test_split_every_launch_shape(waves, subtiles, depth):
         want, want_lse = oracle_decode(c)
         check_fp16(out, want, f"split NW={waves} NS={subtiles} DEPTH={depth}")
         _check_lse(lse, want_lse, "split shapes")
-        # head_dim 128, group 16 (separate hi/lo MFMAs), block size 32
+        # head_dim 128, group 16 (both parts of P in one 16x16x32 MFMA), block size 32
         c2 = workloads.custom_case("split_d128_g16", B=3, Hq=16, Hkv=1, D=128, block_size=32,
                                    lens=[33, 700, 1500], seed=100)
         g2 = to_gpu(c2)

@@ -129,7 +129,35 @@ def test_step_edge_lengths_and_single_partition():
         assert np.array_equal(g2.k_pool.cpu().numpy().view(np.uint16), kp.view(np.uint16))
 
 
-@pytest.mark.parametrize("Hq,Hkv,D,bs", [(16, 1, 128, 32), (32, 8, 128, 16), (4, 4, 64, 64)])
+def test_step_slot_elsewhere_or_skipped():
+    """A new token whose slot is not its position's slot in the table is
+    written there, and this step's attention keeps the pool's row at position
+    ctx-1 (no substitution); a negative slot writes nothing.  The slots used
+    are in blocks no table references, so the expected attention is the plain
+    decode over the pool as given."""
+    c = workloads.custom_case("step_elsewhere", B=4, Hq=14, Hkv=2, D=64, block_size=16,
+                              lens=[5, 300, 1024, 77], seed=112)
+    bs = c.block_size
+    used = set(c.block_tables[c.block_tables >= 0].tolist())
+    spare = [blk for blk in range(c.num_blocks) if blk not in used]
+    assert len(spare) >= 2
+    slots = np.array([spare[0] * bs + 3, -1, spare[1] * bs + bs - 1, -1], dtype=np.int64)
+    for P in (64, 2048):
+        g = to_gpu(c)
+        g.slots = torch.from_numpy(slots).to(g.q.device)
+        out, lse = _step(g, c, P)
+        torch.cuda.synchronize()
+        want, want_lse = ref.paged_attention_decode(c.q, c.k_pool, c.v_pool, c.block_tables,
+                                                    c.context_lens, c.scale, return_lse=True)
+        check_fp16(out, want, f"slot elsewhere P={P}")
+        _check_lse(lse, want_lse)
+        kp, vp = ref.kv_cache_append(c.k_pool, c.v_pool, c.k_new, c.v_new, slots)
+        assert np.array_equal(g.k_pool.cpu().numpy().view(np.uint16), kp.view(np.uint16))
+        assert np.array_equal(g.v_pool.cpu().numpy().view(np.uint16), vp.view(np.uint16))
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,bs", [(16, 1, 128, 32), (32, 8, 128, 16), (4, 4, 64, 64),
+                                         (12, 1, 64, 16)])
 def test_step_other_shapes(Hq, Hkv, D, bs):
     c = workloads.custom_case("step_shapes", B=4, Hq=Hq, Hkv=Hkv, D=D, block_size=bs,
                               lens=[3, 200, 1000, 2500], seed=111)
