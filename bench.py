@@ -214,13 +214,16 @@ def probe_read_gbs(rot, nbytes, R, K):
 
 KERNEL_SOURCES = ("paged_kv_decode_cache_amd/csrc/pkv_kernels.hpp",
                   "paged_kv_decode_cache_amd/csrc/pkv_api.hip")
+Q8_KERNEL_SOURCES = KERNEL_SOURCES + ("paged_kv_decode_cache_amd/csrc/pkv_q8.hpp",)
 TRAFFIC_PROFILES = {"step": "profiles/hbm_traffic_decode_step__sweep_B32_ctx4096.md",
-                    "split": "profiles/hbm_traffic_attn_split__sweep_B32_ctx4096.md"}
+                    "split": "profiles/hbm_traffic_attn_split__sweep_B32_ctx4096.md",
+                    "q8": "profiles/hbm_traffic_attn_split_q8__sweep_B32_ctx4096.md"}
 
 
-def profiled_traffic(kernel_name, profile):
+def profiled_traffic(kernel_name, profile, sources=KERNEL_SOURCES, partition_size=None):
     """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources for this kernel; else None."""
+    on the current kernel sources for this kernel (and, where the summary
+    names one, at this partition size); else None."""
     import hashlib
     path = os.path.join(ROOT, profile)
     if not os.path.exists(path):
@@ -231,11 +234,29 @@ def profiled_traffic(kernel_name, profile):
             k, v = line.strip().split("=", 1)
             kv[k] = v
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         h.update(open(os.path.join(ROOT, rel), "rb").read())
     if kv.get("kernel_sources_sha256") != h.hexdigest() or kv.get("kernel") != kernel_name:
         return None
+    if "partition_size" in kv and partition_size is not None and \
+            int(kv["partition_size"]) != partition_size:
+        return None
     return int(kv["traffic_bytes"])
+
+
+def copy_calibration(args, device):
+    """With --copy-calibration MIB: 20 plain device copies of MIB MiB, a
+    known-size reference for the HBM traffic counters of the same run."""
+    import torch
+    if not args.copy_calibration:
+        return
+    n = args.copy_calibration << 20
+    src = torch.empty(n, dtype=torch.uint8, device=device).random_()
+    dst = torch.empty_like(src)
+    for _ in range(20):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def run_headline(args):
@@ -245,14 +266,7 @@ def run_headline(args):
 
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.empty(n, dtype=torch.uint8, device=device).random_()
-        dst = torch.empty_like(src)
-        for _ in range(20):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(args, device)
     B, ctx = args.batch, args.ctx
     if B in workloads.SWEEP_B and ctx in workloads.SWEEP_CTX:
         case = workloads.sweep_case(B, ctx)
@@ -535,6 +549,7 @@ def run_q8(args):
     import workloads
 
     device = torch.device("cuda:0")
+    copy_calibration(args, device)
     B, ctx = args.batch, args.ctx
     case = (workloads.sweep_case(B, ctx) if B in workloads.SWEEP_B and ctx in workloads.SWEEP_CTX
             else workloads.sweep_case(B, ctx, seed=3999))
@@ -542,13 +557,15 @@ def run_q8(args):
     NB = case.num_blocks
     ctx_sum = int(case.context_lens.astype(np.int64).sum())
     set_bytes = ctx_sum * case.Hkv * (case.D + 4) * 2
-    R = args.sets or max(2, math.ceil(4 * LLC_BYTES / set_bytes))
+    R = args.sets or min(64, max(2, math.ceil(4 * LLC_BYTES / set_bytes)))
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
-    codes_k = torch.empty((R * NB,) + kc.shape[1:], dtype=torch.int8, device=device)
+    # codes in the library's head-major layout [NB, Hkv, bs, D]
+    codes_k = torch.empty((R * NB, case.Hkv, case.block_size, case.D), dtype=torch.int8,
+                          device=device)
     codes_v = torch.empty_like(codes_k)
     sc_k = torch.empty((R * NB, case.Hkv, case.block_size), dtype=torch.float32, device=device)
     sc_v = torch.empty_like(sc_k)
-    k0, v0 = t(kc), t(vc)
+    k0, v0 = t(kc.transpose(0, 2, 1, 3)), t(vc.transpose(0, 2, 1, 3))
     ks0, vs0 = t(ks.transpose(0, 2, 1)), t(vs.transpose(0, 2, 1))
     for r in range(R):
         codes_k[r * NB:(r + 1) * NB].copy_(k0)
@@ -582,8 +599,7 @@ def run_q8(args):
         i += 1
     torch.cuda.synchronize()
     K = args.steps
-    n = min(R, 16)
-    time_it = lambda fn: time_graph(capture([lambda r=r: fn(r) for r in range(n)]), n, K)
+    time_it = lambda fn: time_graph(capture([lambda r=r: fn(r) for r in range(R)]), R, K)
     best = None
     for P in (256, 512, 1024):
         Pm = case.max_partitions(P)
@@ -601,6 +617,9 @@ def run_q8(args):
     achieved = split_bytes / (us_split * 1e-6) / 1e9
     value = (step_bytes + app) / (us_step * 1e-6) / 1e9
     fp16_bytes = alg_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
+    q8_kernel = f"void pkv::attn_q8_kernel<{case.D}, 2, 4, 2, true, true>(pkv::Q8Params)"
+    traffic = (profiled_traffic(q8_kernel, TRAFFIC_PROFILES["q8"], Q8_KERNEL_SOURCES, P)
+               if (B, ctx) == (32, 4096) and case.D == 64 else None)
     res = {
         "metric": Q8_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(us_step * 1e-3, 5),
@@ -615,10 +634,9 @@ def run_q8(args):
                    "fp16_cache_bytes_for_comparison": fp16_bytes,
                    "launch": "HIP graph of R consecutive steps, replayed"},
         "us_per_step": round(us_step, 3),
-        "roofline": {"bound": "hbm",
-                     "kernel": f"pkv::attn_q8_kernel<{case.D}, 2, 4, 2, true, true>",
+        "roofline": {"bound": "hbm", "kernel": q8_kernel,
                      "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
                      "kernel_us": round(us_split, 3),
                      "algorithmic_bytes_per_launch": split_bytes},
         "split_pass_us": round(us_split, 3),
@@ -709,8 +727,7 @@ def run_sweep(args):
         out = torch.empty((case.B, case.Hq, case.D), dtype=torch.float16, device=device)
 
         def time_it(fn):
-            n = min(R, 16)
-            return time_graph(capture([lambda r=r: fn(r) for r in range(n)]), n, K)
+            return time_graph(capture([lambda r=r: fn(r) for r in range(R)]), R, K)
 
         us_unsplit = time_it(lambda i: pkv.paged_attention_decode(
             rot.q, rot.k_pool, rot.v_pool, rot.bt[i % R], rot.ctx, case.scale, out=out))

@@ -334,8 +334,12 @@ int split_reduce(void* out, float* lse_out,
  * The pages mention an 8-bit KV cache only for another system (llama.cpp's
  * q8 cache for Gemma on an RTX 4090, Inference Engineering thread) and give
  * no format; this library's is:
- *   k_codes, v_codes    [num_blocks, block_size, num_kv_heads, head_dim] int8
+ *   k_codes, v_codes    [num_blocks, num_kv_heads, block_size, head_dim] int8
  *   k_scales, v_scales  [num_blocks, num_kv_heads, block_size] fp32
+ * Both are head-major within a block (unlike the fp16 pools): the row of
+ * position t of KV head h is codes[block_tables[b, t / block_size], h,
+ * t % block_size, :], so one head's rows of a block are contiguous and a
+ * pass that reads one head fetches no other head's bytes.
  * Each (token, KV head) row of head_dim values is quantised when written:
  * amax = max |x| (fp16 values in fp32), inv = 127 / amax and code =
  * rint(x * inv) (IEEE fp32 division and multiply, nearest-even; within

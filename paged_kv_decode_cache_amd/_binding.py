@@ -244,10 +244,10 @@ def _q8_shapes(k_codes, v_codes, k_scales, v_scales, dev):
     _need(v_codes, "v_codes", torch.int8, 4, dev)
     _need(k_scales, "k_scales", torch.float32, 3, dev)
     _need(v_scales, "v_scales", torch.float32, 3, dev)
-    NB, bs, Hkv, D = k_codes.shape
+    NB, Hkv, bs, D = k_codes.shape
     if v_codes.shape != k_codes.shape or k_scales.shape != (NB, Hkv, bs) or \
             v_scales.shape != (NB, Hkv, bs):
-        raise ValueError("8-bit pools: codes [num_blocks, block_size, Hkv, D] int8 and scales "
+        raise ValueError("8-bit pools: codes [num_blocks, Hkv, block_size, D] int8 and scales "
                          "[num_blocks, Hkv, block_size] fp32")
     return NB, bs, Hkv, D
 

@@ -3,9 +3,12 @@
 // head) row.
 //
 // Format (this library's; the pages only mention another system's q8 cache):
-// codes [num_blocks, block_size, Hkv, D] int8, scales [num_blocks, Hkv,
-// block_size] fp32 (a block's scales of one head are contiguous, so a lane
-// fetches its four tokens' scales with one 16-byte load).  A row's value is
+// codes [num_blocks, Hkv, block_size, D] int8, scales [num_blocks, Hkv,
+// block_size] fp32: head-major within a block, so one head's rows of a block
+// are contiguous (16 rows of 64 codes fill whole 128-byte lines; with the
+// heads interleaved per token, as in the fp16 pools, a workgroup reading one
+// head used half of every line it fetched), and a lane fetches its four
+// tokens' scales with one 16-byte load.  A row's value is
 // code * scale, quantised when written: amax = max |x|, inv = 127 / amax and
 // code = rint(x * inv) in fp32 (IEEE division, nearest-even), scale =
 // amax / 127; a zero row has codes 0 and scale 0.
@@ -90,14 +93,14 @@ __global__ __launch_bounds__(256) void append_q8_kernel(const AppendQ8Params p) 
     kw[i >> 2] |= (uint32_t)((int)kc & 0xFF) << (8 * (i & 3));
     vw[i >> 2] |= (uint32_t)((int)vc & 0xFF) << (8 * (i & 3));
   }
-  const int64_t base = (slot * p.Hkv + h) * D + 8 * part;
+  const int64_t blk = slot / p.block_size;
+  const int off = (int)(slot - blk * p.block_size);
+  const int64_t si = (blk * p.Hkv + h) * p.block_size + off;  // (block, head, offset)
+  const int64_t base = si * D + 8 * part;
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   *reinterpret_cast<u32x2*>(p.k_codes + base) = u32x2{kw[0], kw[1]};
   *reinterpret_cast<u32x2*>(p.v_codes + base) = u32x2{vw[0], vw[1]};
   if (part == 0) {
-    const int64_t blk = slot / p.block_size;
-    const int off = (int)(slot - blk * p.block_size);
-    const int64_t si = (blk * p.Hkv + h) * p.block_size + off;
     p.k_scales[si] = ka / 127.0f;
     p.v_scales[si] = va / 127.0f;
   }
@@ -153,19 +156,19 @@ __device__ __forceinline__ void load_kv_tile8(KVTile8<D, NS>& T, const Q8Params&
     const int s = s0 + j;
     const int sib = spb_shift >= 0 ? (s & (spb - 1)) : (s % spb);
     const int64_t p0 = ok ? phys : 0;
-    // the subtile's codes of head kvh (16 tokens x all heads from its first
-    // row) and its 16 scales, through empty resources when masked out
-    const int64_t co = ((p0 * a.block_size + sib * 16) * a.Hkv + kvh) * D;
-    const int code_bytes = ok ? 16 * a.Hkv * D : 0;
+    // the subtile's codes of head kvh (16 contiguous rows of D codes) and
+    // its 16 scales, through empty resources when masked out
+    const int64_t so = (p0 * a.Hkv + kvh) * a.block_size + sib * 16;
+    const int64_t co = so * D;
+    const int code_bytes = ok ? 16 * D : 0;
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(P.k_codes + co, code_bytes);
     const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(P.v_codes + co, code_bytes);
-    const int lo = (lane & 15) * a.Hkv * D + 16 * quad;
+    const int lo = (lane & 15) * D + 16 * quad;
 #pragma unroll
     for (int c = 0; c < D / 64; ++c) {
       T.k[j][c] = __builtin_bit_cast(u32x4, load_b128(kr, lo + 64 * c));
       T.v[j][c] = __builtin_bit_cast(u32x4, load_b128(vr, lo + 64 * c));
     }
-    const int64_t so = (p0 * a.Hkv + kvh) * a.block_size + sib * 16;
     const __amdgpu_buffer_rsrc_t ksr = buffer_rsrc(P.k_scales + so, ok ? 64 : 0);
     const __amdgpu_buffer_rsrc_t vsr = buffer_rsrc(P.v_scales + so, ok ? 64 : 0);
     T.ks[j] = load_b128(ksr, 16 * quad);

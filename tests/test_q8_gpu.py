@@ -17,9 +17,22 @@ def _t(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
+def _lib_codes(c):
+    """Codes [NB, bs, Hkv, D] (the oracle's order) in the library's
+    head-major layout [NB, Hkv, bs, D]."""
+    return c.transpose(0, 2, 1, 3)
+
+
+def _oracle_codes(g):
+    """Device codes [NB, Hkv, bs, D] back in the oracle's order."""
+    return g.cpu().numpy().transpose(0, 2, 1, 3)
+
+
 def _gpu_q8(kc, vc, ks, vs):
-    """Device copies in the library's layout (scales [NB, Hkv, bs])."""
-    return _t(kc), _t(vc), _t(ks.transpose(0, 2, 1)), _t(vs.transpose(0, 2, 1))
+    """Device copies in the library's layout (codes [NB, Hkv, bs, D], scales
+    [NB, Hkv, bs])."""
+    return (_t(_lib_codes(kc)), _t(_lib_codes(vc)), _t(ks.transpose(0, 2, 1)),
+            _t(vs.transpose(0, 2, 1)))
 
 
 def _oracle_decode_q8(c, kc, vc, ks, vs, seqs=None, q=None, ctx=None):
@@ -48,12 +61,12 @@ def test_append_q8_bit_exact(Hkv, D, bs):
     kn[1, :, 4:] = 0.0
     slots = rng.permutation(NB * bs)[:N].astype(np.int64)
     slots[5], slots[9] = -1, NB * bs + 3          # skipped
-    g = [_t(kc), _t(vc), _t(ks.transpose(0, 2, 1)), _t(vs.transpose(0, 2, 1))]
+    g = list(_gpu_q8(kc, vc, ks, vs))
     pkv.kv_cache_append_q8(*g, _t(kn), _t(vn), _t(slots))
     torch.cuda.synchronize()
     wk, wv, wks, wvs = ref.kv_cache_append_q8(kc, vc, ks, vs, kn, vn, slots)
-    assert np.array_equal(g[0].cpu().numpy(), wk)
-    assert np.array_equal(g[1].cpu().numpy(), wv)
+    assert np.array_equal(_oracle_codes(g[0]), wk)
+    assert np.array_equal(_oracle_codes(g[1]), wv)
     assert np.array_equal(g[2].cpu().numpy().transpose(0, 2, 1).view(np.uint32), wks.view(np.uint32))
     assert np.array_equal(g[3].cpu().numpy().transpose(0, 2, 1).view(np.uint32), wvs.view(np.uint32))
 
@@ -150,7 +163,8 @@ def test_q8_step_append_then_decode():
     out = pkv.paged_attention_decode_q8(g.q, *gq, g.bt, g.ctx, c.scale)
     torch.cuda.synchronize()
     wk, wv, wks, wvs = ref.kv_cache_append_q8(kc, vc, ks, vs, c.k_new, c.v_new, c.slot_mapping)
-    assert np.array_equal(gq[0].cpu().numpy(), wk)
+    assert np.array_equal(_oracle_codes(gq[0]), wk)
+    assert np.array_equal(_oracle_codes(gq[1]), wv)
     want, _ = _oracle_decode_q8(c, wk, wv, wks, wvs)
     check_fp16(out, want, "q8 step")
 
@@ -166,8 +180,8 @@ def test_q8_quantisation_error_against_fp16():
     slots = rows.astype(np.int64)
     kn = c.k_pool.reshape(NB * bs, Hkv, D)[rows]
     vn = c.v_pool.reshape(NB * bs, Hkv, D)[rows]
-    gq = (torch.zeros((NB, bs, Hkv, D), dtype=torch.int8, device=DEV),
-          torch.zeros((NB, bs, Hkv, D), dtype=torch.int8, device=DEV),
+    gq = (torch.zeros((NB, Hkv, bs, D), dtype=torch.int8, device=DEV),
+          torch.zeros((NB, Hkv, bs, D), dtype=torch.int8, device=DEV),
           torch.zeros((NB, Hkv, bs), dtype=torch.float32, device=DEV),
           torch.zeros((NB, Hkv, bs), dtype=torch.float32, device=DEV))
     pkv.kv_cache_append_q8(*gq, _t(kn), _t(vn), _t(slots))

@@ -358,8 +358,9 @@ def q8_pools(case, seed: Optional[int] = None):
     [-127, 127] with one +-127 per row (as a quantised row always has), and
     per-(token, head) fp32 scales uniform in [2, 4.5] / 127 (the amax of
     N(0,1) rows of 64-128 values).  Rows no sequence attends (NaN in the
-    case's fp16 pools) get a NaN scale.  Scales are returned [NB, bs, Hkv];
-    the library's layout is their transpose [NB, Hkv, bs].
+    case's fp16 pools) get a NaN scale.  Codes are returned [NB, bs, Hkv, D]
+    and scales [NB, bs, Hkv] (the oracle's order); the library's layouts are
+    head-major, [NB, Hkv, bs, D] and [NB, Hkv, bs].
     Returns (k_codes, v_codes, k_scales, v_scales)."""
     rng = np.random.default_rng(case.seed + 13 if seed is None else seed)
     NB, bs, Hkv, D = case.k_pool.shape
