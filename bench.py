@@ -217,7 +217,7 @@ KERNEL_SOURCES = ("paged_kv_decode_cache_amd/csrc/pkv_kernels.hpp",
 Q8_KERNEL_SOURCES = KERNEL_SOURCES + ("paged_kv_decode_cache_amd/csrc/pkv_q8.hpp",)
 TRAFFIC_PROFILES = {"step": "profiles/hbm_traffic_decode_step__sweep_B32_ctx4096.md",
                     "split": "profiles/hbm_traffic_attn_split__sweep_B32_ctx4096.md",
-                    "q8": "profiles/hbm_traffic_attn_split_q8__sweep_B32_ctx4096.md"}
+                    "q8": "profiles/hbm_traffic_decode_step_q8__sweep_B32_ctx4096.md"}
 
 
 def profiled_traffic(kernel_name, profile, sources=KERNEL_SOURCES, partition_size=None):
@@ -592,6 +592,10 @@ def run_q8(args):
     def unsplit(i):
         pkv.paged_attention_decode_q8(q, *pools, bt[i % R], cl, case.scale, out=out)
 
+    def fused_step(i, P, ws):
+        pkv.paged_decode_step_q8(q, *pools, bt[i % R], cl, case.scale, P, k_new=k_new,
+                                 v_new=v_new, slot_mapping=slots[i % R], workspace=ws, out=out)
+
     t0 = time.perf_counter()
     i = 0
     while i < args.warmup or time.perf_counter() - t0 < 0.2:
@@ -600,24 +604,32 @@ def run_q8(args):
     torch.cuda.synchronize()
     K = args.steps
     time_it = lambda fn: time_graph(capture([lambda r=r: fn(r) for r in range(R)]), R, K)
-    best = None
+    # each path at its best partition size: the fused step (the step of
+    # record), the three-launch step and the split pass alone
+    best, best3, best_split = None, None, None
     for P in (256, 512, 1024):
         Pm = case.max_partitions(P)
         po = torch.empty((B, case.Hq, Pm, case.D), dtype=torch.float32, device=device)
         pl = torch.empty((B, case.Hq, Pm), dtype=torch.float32, device=device)
-        us_step = time_it(lambda r: step(r, P, Pm, po, pl))
+        ws = pkv.StepWorkspace(B, case.Hq, case.Hkv, case.D, Pm, device)
+        us_fused = time_it(lambda r: fused_step(r, P, ws))
+        us_three = time_it(lambda r: step(r, P, Pm, po, pl))
         us_split = time_it(lambda r: split_pass(r, P, Pm, po, pl))
-        if best is None or us_step < best[1]:
-            best = (P, us_step, us_split)
+        if best is None or us_fused < best[1]:
+            best = (P, us_fused)
+        if best3 is None or us_three < best3[1]:
+            best3 = (P, us_three)
+        if best_split is None or us_split < best_split[1]:
+            best_split = (P, us_split)
     us_unsplit = time_it(unsplit)
-    P, us_step, us_split = best
+    P, us_step = best
     step_bytes = q8_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
     app = 2 * B * case.Hkv * (case.D * 2 + case.D + 4) + 8 * B   # fp16 in, codes + scale out
-    split_bytes = ctx_sum * case.Hkv * (case.D + 4) * 2 + B * case.Hq * case.D * 2
-    achieved = split_bytes / (us_split * 1e-6) / 1e9
     value = (step_bytes + app) / (us_step * 1e-6) / 1e9
     fp16_bytes = alg_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
-    q8_kernel = f"void pkv::attn_q8_kernel<{case.D}, 2, 4, 2, true, true>(pkv::Q8Params)"
+    G = case.Hq // case.Hkv
+    q8_kernel = (f"void pkv::attn_q8_kernel<{case.D}, {2 if case.D == 64 else 1}, 4, 2, 2, "
+                 f"{'true' if G <= 8 else 'false'}>(pkv::Q8Params)")
     traffic = (profiled_traffic(q8_kernel, TRAFFIC_PROFILES["q8"], Q8_KERNEL_SOURCES, P)
                if (B, ctx) == (32, 4096) and case.D == 64 else None)
     res = {
@@ -629,17 +641,23 @@ def run_q8(args):
                                f"Hkv={case.Hkv}, D={case.D}, block_size={case.block_size}), "
                                "8-bit cache (int8 codes, fp32 scale per token and head)",
                    "partition_size": P, "rotation_sets": R,
-                   "step": "kv_cache_append_q8 + paged_attention_decode_split_q8 + split_reduce",
+                   "step": "paged_decode_step_q8 (quantising append + split pass + merge in "
+                           "one launch)",
                    "algorithmic_bytes_per_step": step_bytes + app,
                    "fp16_cache_bytes_for_comparison": fp16_bytes,
                    "launch": "HIP graph of R consecutive steps, replayed"},
         "us_per_step": round(us_step, 3),
         "roofline": {"bound": "hbm", "kernel": q8_kernel,
-                     "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
-                     "kernel_us": round(us_split, 3),
-                     "algorithmic_bytes_per_launch": split_bytes},
-        "split_pass_us": round(us_split, 3),
+                     "achieved": round(value, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / PEAK_GBS, 4), "traffic": traffic,
+                     "kernel_us": round(us_step, 3),
+                     "kernel_timing": "HIP events around graph replays of R back-to-back "
+                                      "launches",
+                     "algorithmic_bytes_per_launch": step_bytes + app},
+        "three_launch_step_us": round(best3[1], 3),
+        "three_launch_best_partition": best3[0],
+        "split_pass_us": round(best_split[1], 3),
+        "split_pass_best_partition": best_split[0],
         "unsplit_decode_us": round(us_unsplit, 3),
         "unsplit_decode_gbs": round(step_bytes / (us_unsplit * 1e-6) / 1e9, 1),
     }

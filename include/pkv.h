@@ -377,6 +377,31 @@ int paged_attention_decode_split_q8(float* partial_out, float* partial_lse, cons
                                     int32_t max_blocks_per_seq, int32_t partition_size,
                                     int32_t max_partitions, float scale, void* stream);
 
+/* paged_decode_step over the 8-bit cache: the quantising cache write of
+ * kv_cache_append_q8, the split pass of paged_attention_decode_split_q8 and
+ * the merge of split_reduce in one launch (the single-launch step of
+ * paged_decode_step, for the 8-bit format above).
+ *   k_codes, v_codes, k_scales, v_scales   the 8-bit cache, updated in place
+ *                     by the append.
+ *   k_new, v_new      [B, num_kv_heads, head_dim] fp16, finite: one new token
+ *                     per sequence, quantised by the format's rule (codes and
+ *                     scale bit-identical to kv_cache_append_q8's).
+ * Every other argument, the workspace and its state between calls, the slot
+ * rule (the slot of position context_lens[b] - 1, else undefined attention
+ * over the new value) and the merge are as for paged_decode_step.  Results
+ * equal kv_cache_append_q8 + paged_attention_decode_split_q8 + split_reduce up
+ * to fp32 summation order. */
+int paged_decode_step_q8(void* out, float* lse_out,
+                         void* k_codes, void* v_codes, float* k_scales, float* v_scales,
+                         const void* q, const void* k_new, const void* v_new,
+                         const int64_t* slot_mapping,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         float* partial_out, float* partial_lse, int32_t* counters,
+                         int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         int32_t max_blocks_per_seq, int32_t partition_size,
+                         int32_t max_partitions, float scale, void* stream);
+
 /* ------------------------------------------------------------------------
  * Host block allocator (host memory only; no GPU call).
  *

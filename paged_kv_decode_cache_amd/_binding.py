@@ -47,6 +47,9 @@ _SIGNATURES = {
     "split_reduce": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "paged_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "paged_decode_step_q8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                            _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                                            _P]),
     "paged_attention_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                                _I, _I, _I, _F, _P]),
     "kv_cache_append_q8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
@@ -438,6 +441,57 @@ def paged_decode_step(q, k_pool, v_pool, block_tables, context_lens, scale, part
         _ptr(ws.counters), B, Hq, Hkv, D, bs, NB, maxb, int(partition_size), Pm, float(scale),
         _stream(dev, stream))
     _raise(rc, "paged_decode_step")
+    return (out, lse_out) if lse_out is not None else out
+
+
+def paged_decode_step_q8(q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens,
+                         scale, partition_size, k_new=None, v_new=None, slot_mapping=None,
+                         workspace=None, out=None, lse_out=None, want_lse=False, stream=None):
+    """Fused decode step over the 8-bit cache: quantising append (if
+    slot_mapping is given) + split pass + merge in one launch.  Returns out
+    [B, Hq, D] fp16 (and lse [B, Hq])."""
+    _need(q, "q", torch.float16, 3)
+    dev = q.device
+    NB, bs, Hkv, D = _q8_shapes(k_codes, v_codes, k_scales, v_scales, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, Hq, Dq = q.shape
+    if Dq != D or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("q must be [B, Hq, D], block_tables [B, max_blocks], context_lens [B]")
+    maxb = block_tables.shape[1]
+    Pm = max_partitions_for(maxb, bs, partition_size)
+    if workspace is None:
+        workspace = StepWorkspace(B, Hq, Hkv, D, Pm, dev)
+    ws = workspace
+    _need(ws.partial_out, "partial_out", torch.float32, 4, dev)
+    _need(ws.partial_lse, "partial_lse", torch.float32, 3, dev)
+    _need(ws.counters, "counters", torch.int32, 3, dev)
+    Pm = ws.max_partitions
+    if ws.partial_out.shape != (B, Hq, Pm, D) or ws.partial_lse.shape != (B, Hq, Pm) or \
+            ws.counters.shape != (B, Hkv, COUNTER_STRIDE):
+        raise ValueError("workspace shapes do not match the call")
+    if slot_mapping is not None:
+        _need(k_new, "k_new", torch.float16, 3, dev)
+        _need(v_new, "v_new", torch.float16, 3, dev)
+        _need(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+        if k_new.shape != (B, Hkv, D) or v_new.shape != (B, Hkv, D) or \
+                slot_mapping.shape != (B,):
+            raise ValueError("k_new/v_new must be [B, Hkv, D] and slot_mapping [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    _need(out, "out", torch.float16, 3, dev)
+    if want_lse and lse_out is None:
+        lse_out = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, 2, dev)
+    rc = load_library().paged_decode_step_q8(
+        _ptr(out), _ptr(lse_out), _ptr(k_codes), _ptr(v_codes), _ptr(k_scales), _ptr(v_scales),
+        _ptr(q), _ptr(k_new) if slot_mapping is not None else None,
+        _ptr(v_new) if slot_mapping is not None else None, _ptr(slot_mapping),
+        _ptr(block_tables), _ptr(context_lens), _ptr(ws.partial_out), _ptr(ws.partial_lse),
+        _ptr(ws.counters), B, Hq, Hkv, D, bs, NB, maxb, int(partition_size), Pm, float(scale),
+        _stream(dev, stream))
+    _raise(rc, "paged_decode_step_q8")
     return (out, lse_out) if lse_out is not None else out
 
 

@@ -201,17 +201,18 @@ int launch_prefill(const pkv::PrefillParams& p, int64_t grid, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
-// 8-bit decode: unsplit (8 waves) or split pass (4 waves), 2 subtiles per
-// tile at head_dim 64 and 1 at 128, 2 tiles in flight.
-template <int D, bool SPLIT>
+// 8-bit decode: unsplit (8 waves), split pass or fused step (4 waves), 2
+// subtiles per tile at head_dim 64 and 1 at 128, 2 tiles in flight.
+// MODE: 0 unsplit, 1 split pass, 2 fused decode step.
+template <int D, int MODE>
 int launch_q8(const pkv::Q8Params& p, int64_t grid, hipStream_t st) {
   constexpr int NS = D == 64 ? 2 : 1;
-  constexpr int NW = SPLIT ? 4 : 8;
+  constexpr int NW = MODE >= 1 ? 4 : 8;
   if (p.a.G <= 8)
-    hipLaunchKernelGGL((pkv::attn_q8_kernel<D, NS, NW, 2, SPLIT, true>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((pkv::attn_q8_kernel<D, NS, NW, 2, MODE, true>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, st, p);
   else
-    hipLaunchKernelGGL((pkv::attn_q8_kernel<D, NS, NW, 2, SPLIT, false>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((pkv::attn_q8_kernel<D, NS, NW, 2, MODE, false>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, st, p);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
@@ -556,7 +557,7 @@ int paged_attention_decode_q8(void* out, const void* q, const void* k_codes, con
   if (grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
   p.a.out = static_cast<pkv::f16*>(out);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return head_dim == 64 ? launch_q8<64, false>(p, grid, st) : launch_q8<128, false>(p, grid, st);
+  return head_dim == 64 ? launch_q8<64, 0>(p, grid, st) : launch_q8<128, 0>(p, grid, st);
 }
 
 int paged_attention_decode_split_q8(float* partial_out, float* partial_lse, const void* q,
@@ -587,7 +588,61 @@ int paged_attention_decode_split_q8(float* partial_out, float* partial_lse, cons
   p.a.partition_size = partition_size;
   p.a.max_partitions = max_partitions;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return head_dim == 64 ? launch_q8<64, true>(p, grid, st) : launch_q8<128, true>(p, grid, st);
+  return head_dim == 64 ? launch_q8<64, 1>(p, grid, st) : launch_q8<128, 1>(p, grid, st);
+}
+
+int paged_decode_step_q8(void* out, float* lse_out, void* k_codes, void* v_codes,
+                         float* k_scales, float* v_scales, const void* q, const void* k_new,
+                         const void* v_new, const int64_t* slot_mapping,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         float* partial_out, float* partial_lse, int32_t* counters, int32_t B,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                         int32_t partition_size, int32_t max_partitions, float scale,
+                         void* stream) {
+  pkv::Q8Params p;
+  int rc = fill_q8(p, q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens, B,
+                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                   max_blocks_per_seq, scale);
+  if (rc != PKV_OK) return rc;
+  if (partition_size <= 0 || max_partitions <= 0 || partition_size % block_size != 0)
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_partitions * partition_size < (int64_t)max_blocks_per_seq * block_size)
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_partitions * partition_size > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  if (!out || !partial_out || !partial_lse || !counters) return PKV_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(partial_out, 16) || !aligned(partial_lse, 4) ||
+      !aligned(counters, 4) || (lse_out && !aligned(lse_out, 4)))
+    return PKV_ERR_INVALID_ARG;
+  if (slot_mapping) {
+    if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+        !aligned(slot_mapping, 8))
+      return PKV_ERR_INVALID_ARG;
+  }
+  const int64_t grid = (int64_t)B * num_kv_heads * max_partitions;
+  if (grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  // as paged_decode_step: a pair's partials fit one buffer resource below the
+  // merge's out-of-range offset (2^30)
+  if ((int64_t)(num_q_heads / num_kv_heads) * max_partitions * head_dim * 4 >= (1 << 30))
+    return PKV_ERR_UNSUPPORTED;
+  p.a.out = static_cast<pkv::f16*>(out);
+  p.a.lse_out = lse_out;
+  p.a.partial_out = partial_out;
+  p.a.partial_lse = partial_lse;
+  p.a.counters = counters;
+  p.a.B = B;
+  p.a.partition_size = partition_size;
+  p.a.max_partitions = max_partitions;
+  p.a.k_new = static_cast<const pkv::f16*>(k_new);
+  p.a.v_new = static_cast<const pkv::f16*>(v_new);
+  p.a.slot_mapping = slot_mapping;
+  p.k_codes_w = static_cast<int8_t*>(k_codes);
+  p.v_codes_w = static_cast<int8_t*>(v_codes);
+  p.k_scales_w = k_scales;
+  p.v_scales_w = v_scales;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return head_dim == 64 ? launch_q8<64, 2>(p, grid, st) : launch_q8<128, 2>(p, grid, st);
 }
 
 int split_reduce(void* out, float* lse_out, const float* partial_out, const float* partial_lse,

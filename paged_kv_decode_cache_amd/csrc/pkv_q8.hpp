@@ -35,10 +35,15 @@ typedef f16 f16x2 __attribute__((ext_vector_type(2)));
 
 struct Q8Params {
   AttnParams a;            // k_pool / v_pool unused
-  const int8_t* k_codes;   // [NB, bs, Hkv, D]
+  const int8_t* k_codes;   // [NB, Hkv, bs, D]
   const int8_t* v_codes;
   const float* k_scales;   // [NB, Hkv, bs]
   const float* v_scales;
+  // fused decode step: the same arrays, written by the step's append
+  int8_t* k_codes_w;
+  int8_t* v_codes_w;
+  float* k_scales_w;
+  float* v_scales_w;
 };
 
 struct AppendQ8Params {
@@ -137,20 +142,62 @@ struct KVTile8 {
   f32x4 vs[NS];
   int okmask;
   int s0;
+  int new_phys;  // block id of subtile s_new when the tile holds it, else -1
   bool full;
 };
+
+// The fused step's new token row of one KV head (fp16, D values at `row`),
+// quantised by the format's rule into a tile's lane layout: lane quad q holds
+// the codes of dims 64c + 16q .. 64c + 16q + 15 (bytes in dim order), and
+// every lane gets the row's scale.  The decisions are append_q8_kernel's
+// (fp32 amax, IEEE division 127 / amax, nearest-even rint of x * inv, clip),
+// so the codes and scale are bit-identical to the cache write's.  All 64
+// lanes of the wave must run it (cross-quad maximum).
+template <int D>
+__device__ __forceinline__ void quantize_row_lanes(const f16* row, int quad,
+                                                   u32x4 (&codes)[D / 64], float& scale) {
+  f16x8 x[D / 64][2];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      x[c][h] = *reinterpret_cast<const f16x8*>(row + 64 * c + 16 * quad + 8 * h);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)x[c][h][i]));
+    }
+  amax = max_across_quads(amax);
+  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;  // IEEE division
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float q =
+            fminf(fmaxf(__builtin_rintf((float)x[c][h][i] * inv), -127.0f), 127.0f);
+        w[2 * h + (i >> 2)] |= (uint32_t)((int)q & 0xFF) << (8 * (i & 3));
+      }
+    codes[c] = w;
+  }
+  scale = amax / 127.0f;
+}
 
 template <int D, int NS>
 __device__ __forceinline__ void load_kv_tile8(KVTile8<D, NS>& T, const Q8Params& P, int ids,
                                               int s0, int sub_end, int t_end, int spb,
-                                              int spb_shift, int kvh, int lane) {
+                                              int spb_shift, int kvh, int lane,
+                                              int s_new = -1) {
   const AttnParams& a = P.a;
   const int quad = lane >> 4;
   T.s0 = s0;
   int okm = 0;
+  int new_phys = -1;
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const int phys = __builtin_amdgcn_readlane(ids, j);
+    new_phys = s0 + j == s_new ? phys : new_phys;
     const bool ok = s0 + j < sub_end && phys >= 0 && phys < a.num_blocks;
     okm |= (ok ? 1 : 0) << j;
     const int s = s0 + j;
@@ -175,21 +222,47 @@ __device__ __forceinline__ void load_kv_tile8(KVTile8<D, NS>& T, const Q8Params&
     T.vs[j] = load_b128(vsr, 16 * quad);
   }
   T.okmask = okm;
+  T.new_phys = new_phys;
   T.full = okm == (1 << NS) - 1 && ((s0 + NS) << 4) <= t_end;
 }
 
 // QK^T, online-softmax update and PV for one tile of codes (see the header).
+// SUB: position (s_new, tok_new) takes the codes and scales of the fused
+// step's new token (kq/vq, ksc/vsc, quantised in registers and written to
+// the cache by this launch) when `slot` is the position's slot in the table.
 // lsum: this lane's running sum of its column's (unscaled) weights.
-template <int D, int NS, bool DUAL>
+template <int D, int NS, bool DUAL, bool SUB>
 __device__ __forceinline__ void consume_tile8(KVTile8<D, NS>& T, SoftmaxState<D>& st,
                                               float& lsum, const f16x8 (&qb)[D / 32],
                                               f16* stage, float c, int t_end, int lane,
-                                              float rem_mul) {
+                                              float rem_mul, int s_new, int tok_new,
+                                              int64_t slot, int new_off, int block_size,
+                                              const u32x4 (&kq)[D / 64],
+                                              const u32x4 (&vq)[D / 64], float ksc,
+                                              float vsc) {
   constexpr int KC = D / 32;
   constexpr int NDB = D / 16;
   constexpr int ROW = D + 4;
   const int g = lane & 15;
   const int quad = lane >> 4;
+  if (SUB && T.new_phys >= 0 && (int64_t)T.new_phys * block_size + new_off == slot) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const bool here = T.s0 + j == s_new;
+      const bool mine = here && (lane & 15) == tok_new;
+#pragma unroll
+      for (int cc = 0; cc < D / 64; ++cc) {
+        T.k[j][cc] = mine ? kq[cc] : T.k[j][cc];
+        T.v[j][cc] = mine ? vq[cc] : T.v[j][cc];
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const bool its = here && 4 * quad + v == tok_new;
+        T.ks[j][v] = its ? ksc : T.ks[j][v];
+        T.vs[j][v] = its ? vsc : T.vs[j][v];
+      }
+    }
+  }
 
   f32x4 sc[NS];
 #pragma unroll
@@ -292,13 +365,20 @@ __device__ __forceinline__ void consume_tile8(KVTile8<D, NS>& T, SoftmaxState<D>
   asm volatile("" ::: "memory");
 }
 
-// Decode over the 8-bit cache.  SPLIT = false: one workgroup per (sequence,
-// KV head), fp16 out.  SPLIT = true: one per partition, fp32 partials + lse
-// (merged by split_reduce).
-template <int D, int NS, int NW, int DEPTH, bool SPLIT, bool DUAL>
+// Decode over the 8-bit cache.  MODE 0: one workgroup per (sequence, KV
+// head), fp16 out.  MODE 1: one per partition, fp32 partials + lse (merged by
+// split_reduce).  MODE 2: the fused decode step -- MODE 1 plus, in the same
+// launch, the quantising cache write of each sequence's new token and the
+// merge of each (sequence, KV head) by the holder of its last ticket, with
+// the fp16 step's hand-off (device-coherent partial rows polled until
+// written; merge_step_partitions).
+template <int D, int NS, int NW, int DEPTH, int MODE, bool DUAL>
 __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   constexpr int KC = D / 32;
   constexpr int NDB = D / 16;
+  constexpr int DC = D / 64;  // 16-code chunks per lane and row
+  constexpr bool SPLIT = MODE >= 1;
+  constexpr bool STEP = MODE == 2;
   using SM = AttnSmem<D, NS>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[NW * SM::kWaveBytes];
   const AttnParams& a = P.a;
@@ -331,13 +411,16 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   for (int i = 0; i < DEPTH; ++i)
     ids[i] = load_block_ids<NS>(bt_rs, s_first + i * TSTEP, sub_cap, spb, spb_shift, lane);
 
+  // Fused step: the new token's slot, requested with the length.
+  const int64_t slot_in = STEP && a.slot_mapping != nullptr ? a.slot_mapping[b] : -1;
   const int cap = a.max_blocks * a.block_size;
   int ctx = a.context_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
   int t_end = ctx;
   if (SPLIT) {
-    if (t_begin >= ctx) {
-      if (threadIdx.x < a.G)
+    // the fused step's partition 0 of an empty sequence still writes zeros
+    if (t_begin >= ctx && !(STEP && ctx == 0 && p == 0)) {
+      if (!STEP && threadIdx.x < a.G)
         a.partial_lse[((size_t)b * a.Hq + kvh * a.G + threadIdx.x) * a.max_partitions + p] =
             -INFINITY;
       return;
@@ -345,6 +428,36 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
     t_end = min(ctx, t_begin + a.partition_size);
   }
   const int sub_end = (t_end + 15) >> 4;
+  const int n_parts = STEP ? (ctx + a.partition_size - 1) / a.partition_size : 1;
+
+  // Fused step: the workgroup owning position ctx-1 (partition 0 if ctx = 0)
+  // quantises the new token's K/V rows of its head in registers, attends
+  // over them in place of the cache's position ctx-1 when the slot is that
+  // position's slot in the block table, and writes codes and scales at the
+  // end (the launch never reads its own write).
+  const bool owns_new =
+      STEP && a.slot_mapping != nullptr && p == (ctx > 0 ? (ctx - 1) / a.partition_size : 0);
+  const int64_t slot = owns_new ? slot_in : -1;
+  int s_new = -1, tok_new = -1, new_off = 0;
+  u32x4 kq[DC], vq[DC];
+  float ksc = 0.0f, vsc = 0.0f;
+  if (owns_new) {
+    if (ctx > 0) {
+      const int pos = ctx - 1;
+      new_off = pos % a.block_size;
+      s_new = pos >> 4;
+      tok_new = pos & 15;
+    }
+    const size_t new_row = ((size_t)b * Hkv + kvh) * D;
+    quantize_row_lanes<D>(a.k_new + new_row, quad, kq, ksc);
+    quantize_row_lanes<D>(a.v_new + new_row, quad, vq, vsc);
+  } else {
+#pragma unroll
+    for (int cc = 0; cc < DC; ++cc) {
+      kq[cc] = u32x4{0u, 0u, 0u, 0u};
+      vq[cc] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
 
   // q as the B operand in the codes' dim order: MFMA m takes dims
   // 64*(m/2) + 16*quad + 8*(m%2) .. +7
@@ -376,18 +489,26 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   for (int i = 0; i < DEPTH; ++i) {
     // past the wave's last tile: empty resources, no memory access
     load_kv_tile8<D, NS>(buf[i], P, ids[i], s_first + i * TSTEP, sub_end, t_end, spb, spb_shift,
-                         kvh, lane);
+                         kvh, lane, s_new);
     ids[i] = load_block_ids<NS>(bt_rs, s_first + (i + DEPTH) * TSTEP, sub_end, spb, spb_shift,
                                 lane);
   }
+  // Fused step: the ticket (issued after the first K/V requests; waited for
+  // only at the end).
+  int ticket = 0;
+  if (STEP && n_parts > 1 && threadIdx.x == 0)
+    ticket = __hip_atomic_fetch_add(a.counters + ((size_t)b * Hkv + kvh) * kCounterStride, 1,
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (int u0 = 0; u0 < n_tiles; u0 += DEPTH) {
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) {
       const int u = u0 + i;
       if (u < n_tiles)
-        consume_tile8<D, NS, DUAL>(buf[i], st, lsum, qb, stage, c, t_end, lane, rem_mul);
+        consume_tile8<D, NS, DUAL, STEP>(buf[i], st, lsum, qb, stage, c, t_end, lane, rem_mul,
+                                         s_new, tok_new, slot, new_off, a.block_size, kq, vq,
+                                         ksc, vsc);
       load_kv_tile8<D, NS>(buf[i], P, ids[i], s_first + (u + DEPTH) * TSTEP, sub_end, t_end,
-                           spb, spb_shift, kvh, lane);
+                           spb, spb_shift, kvh, lane, s_new);
       ids[i] = load_block_ids<NS>(bt_rs, s_first + (u + 2 * DEPTH) * TSTEP, sub_end, spb,
                                   spb_shift, lane);
     }
@@ -403,26 +524,78 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   float l_tot = lsum + __shfl_xor(lsum, 16);
   l_tot += __shfl_xor(l_tot, 32);
 
+  // Fused step: whether this workgroup merges (its ticket is the pair's
+  // last); the merger resets the counter at once (every ticket is taken).
+  __shared__ int s_merge;
+  __shared__ __attribute__((aligned(16))) float own[STEP ? 16 * D + 16 : 4];
+  if (STEP && n_parts > 1 && threadIdx.x == 0) {
+    const bool m = ticket == n_parts - 1;
+    if (m)
+      __hip_atomic_store(a.counters + ((size_t)b * Hkv + kvh) * kCounterStride, 0,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_merge = m;
+  }
+  if (NW == 1 && STEP) __syncthreads();
+
+  // Fused step: the new token's codes and scale of this head, at (block,
+  // head, offset) of the head-major layout.
+  if (owns_new && slot >= 0 && slot < (int64_t)a.num_blocks * a.block_size && wave == 0 &&
+      g == 0) {
+    const int64_t blk = slot / a.block_size;
+    const int off = (int)(slot - blk * a.block_size);
+    const int64_t si = (blk * Hkv + kvh) * a.block_size + off;
+#pragma unroll
+    for (int cc = 0; cc < DC; ++cc) {
+      *reinterpret_cast<u32x4*>(P.k_codes_w + si * D + 64 * cc + 16 * quad) = kq[cc];
+      *reinterpret_cast<u32x4*>(P.v_codes_w + si * D + 64 * cc + 16 * quad) = vq[cc];
+    }
+    if (quad == 0) {
+      P.k_scales_w[si] = ksc;
+      P.v_scales_w[si] = vsc;
+    }
+  }
+
   const bool emits = (DUAL ? g < 8 : true) && head_col < a.G;
   auto emit = [&](int db, f32x4 acc, float L, float M) {
     if (!emits) return;
     const int h = kvh * a.G + head_col;
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     const int d0 = 16 * db + 4 * quad;
-    if (SPLIT) {
+    if (SPLIT && !(STEP && n_parts <= 1)) {
       f32x4 r;
 #pragma unroll
       for (int v = 0; v < 4; ++v) r[v] = acc[v] * inv;
-      *reinterpret_cast<f32x4*>(a.partial_out +
-                                (((size_t)b * a.Hq + h) * a.max_partitions + p) * D + d0) = r;
-      if (db == 0 && quad == 0)
-        a.partial_lse[((size_t)b * a.Hq + h) * a.max_partitions + p] =
-            L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+      const float lse_v = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+      if (STEP) {
+        if (s_merge) {
+          *reinterpret_cast<f32x4*>(own + head_col * D + d0) = r;
+          if (db == 0 && quad == 0) own[16 * D + head_col] = lse_v;
+        } else {
+          const size_t head0 = (size_t)b * a.Hq + kvh * a.G;
+          const int Pm = a.max_partitions;
+          const __amdgpu_buffer_rsrc_t po_rs =
+              buffer_rsrc(a.partial_out + head0 * Pm * D, a.G * Pm * D * 4);
+          const __amdgpu_buffer_rsrc_t pl_rs =
+              buffer_rsrc(a.partial_lse + head0 * Pm, a.G * Pm * 4);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) r[v] = as_written(r[v]);
+          store_coherent4(po_rs, ((head_col * Pm + p) * D + d0) * 4, r);
+          if (db == 0 && quad == 0)
+            store_coherent1(pl_rs, (head_col * Pm + p) * 4, as_written(lse_v));
+        }
+      } else {
+        *reinterpret_cast<f32x4*>(a.partial_out +
+                                  (((size_t)b * a.Hq + h) * a.max_partitions + p) * D + d0) = r;
+        if (db == 0 && quad == 0)
+          a.partial_lse[((size_t)b * a.Hq + h) * a.max_partitions + p] = lse_v;
+      }
     } else {
       f16x4 r;
 #pragma unroll
       for (int v = 0; v < 4; ++v) r[v] = (f16)(acc[v] * inv);
       *reinterpret_cast<f16x4*>(a.out + ((size_t)b * a.Hq + h) * D + d0) = r;
+      if (STEP && a.lse_out != nullptr && db == 0 && quad == 0)
+        a.lse_out[(size_t)b * a.Hq + h] = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
     }
   };
   if (NW == 1) {
@@ -431,6 +604,10 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   } else {
     merge_waves_impl<D, NW>(st, l_tot, smem, SM::kWaveBytes, wave, lane, emit);
   }
+  if (!STEP || n_parts <= 1 || !s_merge) return;
+  __syncthreads();  // the merger's own partial is complete in LDS
+  __shared__ float msm[6 * kMergeSlots];
+  merge_step_partitions<D, NW>(a, b, kvh, n_parts, p, own, msm);
 }
 
 }  // namespace pkv

@@ -261,6 +261,36 @@ def test_step_batch0_is_noop():
     assert _step(pkv.load_library(), B=0) == 0
 
 
+def _step_q8(lib, **kw):
+    a = dict(out=A16, lse=None, kc=C16, vc=D16, ks=0x50000, vs=0x60000, q=B16, kn=0x70000,
+             vn=0x80000, slots=0x90000, bt=E16, ctx=F16, po=0xA0000, pl=0xB0000, cnt=0xC0000,
+             B=2, Hq=14, Hkv=2, D=64, bs=16, NB=10, maxb=4, P=32, Pm=2, scale=0.125)
+    a.update(kw)
+    return lib.paged_decode_step_q8(a["out"], a["lse"], a["kc"], a["vc"], a["ks"], a["vs"],
+                                    a["q"], a["kn"], a["vn"], a["slots"], a["bt"], a["ctx"],
+                                    a["po"], a["pl"], a["cnt"], a["B"], a["Hq"], a["Hkv"],
+                                    a["D"], a["bs"], a["NB"], a["maxb"], a["P"], a["Pm"],
+                                    a["scale"], None)
+
+
+STEP_Q8_BAD = STEP_BAD + [
+    ("null scales", dict(ks=None), -1),
+    ("misaligned scales", dict(vs=0x60000 + 4), -1),
+    ("head_dim 96", dict(D=96), -2),
+]
+
+
+@host_only
+@pytest.mark.parametrize("name,kw,code", STEP_Q8_BAD, ids=[c[0] for c in STEP_Q8_BAD])
+def test_step_q8_rejects(name, kw, code):
+    assert _step_q8(pkv.load_library(), **kw) == code
+
+
+@host_only
+def test_step_q8_batch0_is_noop():
+    assert _step_q8(pkv.load_library(), B=0) == 0
+
+
 def test_binding_rejects_cpu_tensors():
     q = torch.zeros((1, 2, 64), dtype=torch.float16)
     kp = torch.zeros((2, 16, 1, 64), dtype=torch.float16)

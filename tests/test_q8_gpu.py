@@ -193,3 +193,159 @@ def test_q8_quantisation_error_against_fp16():
     err = float(np.abs(host64(out) - want16).max())
     say(f"8-bit cache vs fp16 cache, qwen: max abs difference {err:.4f}")
     assert err <= 0.05
+
+
+# ---- fused decode step over the 8-bit cache ---------------------------------
+
+def _step_q8(g, gq, c, P, ws=None, slots=None, want_lse=True):
+    return pkv.paged_decode_step_q8(g.q, *gq, g.bt, g.ctx, c.scale, P, k_new=g.k_new,
+                                    v_new=g.v_new, slot_mapping=g.slots if slots is None else slots,
+                                    workspace=ws, want_lse=want_lse)
+
+
+def _check_pools_q8(gq, want):
+    """The device 8-bit cache equals the oracle's, bitwise (codes and scales,
+    NaN scales of unattended rows included)."""
+    wk, wv, wks, wvs = want
+    assert np.array_equal(_oracle_codes(gq[0]), wk)
+    assert np.array_equal(_oracle_codes(gq[1]), wv)
+    assert np.array_equal(gq[2].cpu().numpy().transpose(0, 2, 1).view(np.uint32),
+                          wks.view(np.uint32))
+    assert np.array_equal(gq[3].cpu().numpy().transpose(0, 2, 1).view(np.uint32),
+                          wvs.view(np.uint32))
+
+
+def _check_workspace_restored(ws):
+    assert int(ws.counters.abs().sum()) == 0
+    assert bool((ws.partial_out.view(torch.int32) == -1).all())
+    assert bool((ws.partial_lse.view(torch.int32) == -1).all())
+
+
+@pytest.mark.parametrize("name,P", [("tiny", 16), ("qwen", 256), ("qwen", 1024),
+                                    ("sweep:32:4096", 1024), ("sweep:8:2048", 256),
+                                    ("long:1:32768", 1024)])
+def test_q8_step_matches_append_then_decode(name, P):
+    """The fused 8-bit step (quantising append + split pass + merge in one
+    launch) against the oracle's kv_cache_append_q8 followed by its decode
+    over the dequantised cache; the cache write bit-exact."""
+    c = case(name)
+    say(f"q8 step {name} P={P}")
+    kc, vc, ks, vs = workloads.q8_pools(c)
+    g = to_gpu(c)
+    gq = _gpu_q8(kc, vc, ks, vs)
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    out, lse = _step_q8(g, gq, c, P, ws)
+    torch.cuda.synchronize()
+    want_pools = ref.kv_cache_append_q8(kc, vc, ks, vs, c.k_new, c.v_new, c.slot_mapping)
+    _check_pools_q8(gq, want_pools)
+    want, want_lse = _oracle_decode_q8(c, *want_pools)
+    check_fp16(out, want, f"q8 step {name}")
+    g_lse = host64(lse)
+    assert np.array_equal(np.isneginf(g_lse), np.isneginf(want_lse))
+    fin = np.isfinite(want_lse)
+    assert float(np.abs(g_lse[fin] - want_lse[fin]).max()) <= PARTIAL_ATOL
+    _check_workspace_restored(ws)
+
+
+def test_q8_step_equals_three_launch_path_and_repeats():
+    """Two steps in a row on one workspace: each equals the three-launch
+    8-bit step (append + split pass + split_reduce) on its own copy of the
+    cache, and every call leaves the workspace ready for the next."""
+    c = case("qwen")
+    P = 256
+    kc, vc, ks, vs = workloads.q8_pools(c)
+    g = to_gpu(c)
+    gq = _gpu_q8(kc, vc, ks, vs)
+    gq3 = _gpu_q8(kc, vc, ks, vs)
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    for rep in range(2):
+        out = _step_q8(g, gq, c, P, ws, want_lse=False)
+        pkv.kv_cache_append_q8(*gq3, g.k_new, g.v_new, g.slots)
+        po, pl = pkv.paged_attention_decode_split_q8(g.q, *gq3, g.bt, g.ctx, c.scale, P)
+        out3 = pkv.split_reduce(po, pl, g.ctx, P)
+        torch.cuda.synchronize()
+        for a_, b_ in zip(gq, gq3):
+            assert torch.equal(a_.view(torch.uint8), b_.view(torch.uint8)), f"cache rep {rep}"
+        err = float((out.float() - out3.float()).abs().max())
+        assert err <= 2e-3, f"rep {rep}: {err}"
+        _check_workspace_restored(ws)
+
+
+def test_q8_step_edge_lengths_and_slots():
+    """Context lengths 0, 1, a block, a block + 1 and several partitions; a
+    skipped slot (-1) writes nothing and attends over the cache as it is."""
+    c = workloads.custom_case("q8_step_edges", B=6, Hq=14, Hkv=2, D=64, block_size=16,
+                              lens=[0, 1, 16, 17, 511, 1300], seed=120, q_mult=4.0)
+    kc, vc, ks, vs = workloads.q8_pools(c)
+    # the skipped sequence's position ctx-1 keeps the pool's own (finite) row
+    slots = c.slot_mapping.copy()
+    skip = 4
+    blk = c.block_tables[skip, (c.context_lens[skip] - 1) // c.block_size]
+    off = (c.context_lens[skip] - 1) % c.block_size
+    ks[blk, off] = 0.02
+    vs[blk, off] = 0.03
+    slots[skip] = -1
+    for P in (16, 512, 2048):
+        g = to_gpu(c)
+        gq = _gpu_q8(kc, vc, ks, vs)
+        s_gpu = torch.from_numpy(slots).to(g.q.device)
+        out, lse = _step_q8(g, gq, c, P, slots=s_gpu)
+        torch.cuda.synchronize()
+        want_pools = ref.kv_cache_append_q8(kc, vc, ks, vs, c.k_new, c.v_new, slots)
+        _check_pools_q8(gq, want_pools)
+        want, _ = _oracle_decode_q8(c, *want_pools)
+        check_fp16(out, want, f"q8 step edges P={P}")
+        assert int((out[0] != 0).sum()) == 0
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,bs", [(16, 1, 128, 32), (32, 8, 128, 16), (12, 1, 64, 16)])
+def test_q8_step_other_shapes(Hq, Hkv, D, bs):
+    c = workloads.custom_case("q8_step_shapes", B=4, Hq=Hq, Hkv=Hkv, D=D, block_size=bs,
+                              lens=[3, 200, 1000, 2500], seed=121)
+    kc, vc, ks, vs = workloads.q8_pools(c)
+    g = to_gpu(c)
+    gq = _gpu_q8(kc, vc, ks, vs)
+    out = _step_q8(g, gq, c, 256, want_lse=False)
+    torch.cuda.synchronize()
+    want_pools = ref.kv_cache_append_q8(kc, vc, ks, vs, c.k_new, c.v_new, c.slot_mapping)
+    _check_pools_q8(gq, want_pools)
+    want, _ = _oracle_decode_q8(c, *want_pools)
+    check_fp16(out, want, f"q8 step shapes {Hq}/{Hkv}/{D}/{bs}")
+
+
+def test_q8_step_in_hip_graph_replays():
+    """Replays of a captured 8-bit step, with eager work and synchronisation
+    between them, equal the eager result bitwise (the append rewrites the same
+    slots with the same codes, so every replay sees the same cache)."""
+    c = case("sweep:32:1024")
+    P = 256
+    kc, vc, ks, vs = workloads.q8_pools(c)
+    g = to_gpu(c)
+    gq = _gpu_q8(kc, vc, ks, vs)
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    out = torch.empty((c.B, c.Hq, c.D), dtype=torch.float16, device=g.q.device)
+    eager = _step_q8(g, gq, c, P, ws, want_lse=False).clone()
+    torch.cuda.synchronize()
+
+    def launch():
+        pkv.paged_decode_step_q8(g.q, *gq, g.bt, g.ctx, c.scale, P, k_new=g.k_new,
+                                 v_new=g.v_new, slot_mapping=g.slots, workspace=ws, out=out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        launch()
+    for rep in range(4):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        _check_workspace_restored(ws)
+        junk = torch.randn(1024, device=g.q.device).sum()
+        torch.cuda.synchronize()
+        del junk
