@@ -473,15 +473,53 @@ def run_prefill(args):
         i += 1
     torch.cuda.synchronize()
     R = 16
-    us = time_graph(capture([lambda r=r: call(r) for r in range(R)]), R, args.steps)
+    us_whole = time_graph(capture([lambda r=r: call(r) for r in range(R)]), R, args.steps)
+
+    # the split over context partitions: split pass + split_reduce (two
+    # launches), and the split pass alone, at the best partition size
+    maxb = case.block_tables.shape[1]
+    T = case.total_q
+    split = None
+    for P in (256, 512, 1024, 2048):
+        if P > ctx:
+            continue
+        Pm = pkv.max_partitions_for(maxb, case.block_size, P)
+        po = torch.empty((T, case.Hq, Pm, case.D), dtype=torch.float32, device=device)
+        pl = torch.empty((T, case.Hq, Pm), dtype=torch.float32, device=device)
+        rl = torch.zeros((T,), dtype=torch.int32, device=device)
+
+        def split_pass(_i, P=P, Pm=Pm, po=po, pl=pl, rl=rl):
+            pkv.paged_attention_prefill_split(q, kp, vp, bt, cl, qs, case.scale, case.max_q, P,
+                                              Pm, partial_out=po, partial_lse=pl,
+                                              row_context_lens=rl)
+
+        def split_merged(i, P=P, po=po, pl=pl, rl=rl, split_pass=split_pass):
+            split_pass(i)
+            pkv.split_reduce(po, pl, rl, P, out=out)
+
+        us_sm = time_graph(capture([lambda r=r: split_merged(r) for r in range(R)]), R,
+                           args.steps)
+        us_sp = time_graph(capture([lambda r=r: split_pass(r) for r in range(R)]), R,
+                           args.steps)
+        if split is None or us_sm < split[1]:
+            split = (P, us_sm, us_sp, Pm)
     flops = prefill_flops(case)
     # the library gives launches with fewer workgroups than CUs 8 waves each
     rows_per_wg = 16 * 4 // (case.Hq // case.Hkv)
-    grid = case.B * case.Hkv * -(-case.max_q // rows_per_wg)
+    q_tiles = -(-case.max_q // rows_per_wg)
+    grid = case.B * case.Hkv * q_tiles
+    use_split = split is not None and split[1] < us_whole
+    if use_split:
+        grid *= split[3]
     nw = 8 if grid < 256 else 4
+    kname = f"void pkv::prefill_kernel<64, 4, {nw}, 2, {'true' if use_split else 'false'}>" \
+            "(pkv::PrefillParams)"
+    us = split[1] if use_split else us_whole
+    kernel_us = split[2] if use_split else us_whole
     kv = case.B * ctx * case.Hkv * case.D * 4
     qo = case.total_q * case.Hq * case.D * 4
     tflops = flops / (us * 1e-6) / 1e12
+    kernel_tflops = flops / (kernel_us * 1e-6) / 1e12
     res = {
         "metric": PREFILL_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us * 1e-3, 5),
@@ -491,13 +529,19 @@ def run_prefill(args):
                                f"position {ctx - 1} (Hq=14, Hkv=2, D=64, block_size=16)",
                    "B": B, "ctx": ctx, "chunk": n, "useful_flops_per_call": flops,
                    "kv_bytes_per_call": kv, "q_out_bytes_per_call": qo,
+                   "path": (f"paged_attention_prefill_split (partition {split[0]}) + "
+                            "split_reduce" if use_split else "paged_attention_prefill"),
                    "launch": "HIP graph of 16 calls, replayed", "accumulate": "fp32"},
         "us_per_call": round(us, 3),
-        "roofline": {"bound": "mfma", "kernel": f"pkv::prefill_kernel<64, 4, {nw}, 2>",
-                     "achieved": round(tflops, 2), "peak": PEAK_FP16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
-                     "traffic": None, "kernel_us": round(us, 3),
-                     "hbm_gbs_on_kv_and_q_out": round((kv + qo) / (us * 1e-6) / 1e9, 1)},
+        "roofline": {"bound": "mfma", "kernel": kname,
+                     "achieved": round(kernel_tflops, 2), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_FP16_TFLOPS, 4),
+                     "traffic": None, "kernel_us": round(kernel_us, 3),
+                     "hbm_gbs_on_kv_and_q_out": round((kv + qo) / (kernel_us * 1e-6) / 1e9, 1)},
+        "whole_context_us": round(us_whole, 3),
+        "split_merged_us": round(split[1], 3) if split else None,
+        "split_pass_us": round(split[2], 3) if split else None,
+        "split_best_partition": split[0] if split else None,
     }
     if not args.no_cpu:
         from threadpoolctl import threadpool_limits

@@ -14,7 +14,8 @@
  *   split_reduce                  log-sum-exp weighted merge of the partitions
  *   paged_decode_step             append + split pass + merge in one launch
  *   paged_attention_prefill       a chunk of new tokens per sequence attending
- *                                 causally over the cache (chunked prefill)
+ *                                 causally over the cache (chunked prefill),
+ *                                 also split over context partitions
  *
  * plus a host-side block allocator (pkv_allocator_*) that hands out the
  * cache's blocks and builds block tables and slot mappings for a batch.
@@ -304,6 +305,40 @@ int paged_attention_prefill(void* out, const void* q,
                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                             int32_t block_size, int32_t num_blocks,
                             int32_t max_blocks_per_seq, float scale, void* stream);
+
+/*
+ * paged_attention_prefill_split -- paged_attention_prefill with each
+ * sequence's context cut into partitions of partition_size positions (the
+ * split of paged_attention_decode_split applied to a chunk's rows), for short
+ * chunks over long contexts, where one workgroup per query tile streams the
+ * whole context alone.  Merge with split_reduce over the chunk rows:
+ * split_reduce(out, lse_out, partial_out, partial_lse, row_context_lens,
+ * total_q, num_q_heads, head_dim, partition_size, max_partitions).
+ *
+ *   partial_out       [total_q, num_q_heads, max_partitions, head_dim] fp32
+ *   partial_lse       [total_q, num_q_heads, max_partitions] fp32 workspace,
+ *                     as paged_attention_decode_split's per chunk row: for a
+ *                     row that sees no position of a partition that exists
+ *                     for its sequence, lse = -inf and a zero row.
+ *   row_context_lens  [total_q] int32 out: row r of sequence b gets
+ *                     context_lens[b] (clamped), the length split_reduce needs
+ *                     to count the row's partitions.  Rows past
+ *                     query_start[B] are not written.
+ * Other arguments as paged_attention_prefill, plus partition_size (a multiple
+ * of block_size) and max_partitions (max_partitions * partition_size >=
+ * max_blocks_per_seq * block_size).  The merged result equals
+ * paged_attention_prefill up to fp32 summation order.
+ */
+int paged_attention_prefill_split(float* partial_out, float* partial_lse,
+                                  int32_t* row_context_lens, const void* q,
+                                  const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  const int32_t* query_start, int32_t B,
+                                  int32_t max_query_len, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, int32_t max_blocks_per_seq,
+                                  int32_t partition_size, int32_t max_partitions, float scale,
+                                  void* stream);
 
 /*
  * split_reduce -- merge the partitions written by

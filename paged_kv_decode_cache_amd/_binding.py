@@ -52,6 +52,8 @@ _SIGNATURES = {
                                             _P]),
     "paged_attention_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                                _I, _I, _I, _F, _P]),
+    "paged_attention_prefill_split": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I,
+                                                     _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "kv_cache_append_q8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "paged_attention_decode_q8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                                  _I, _I, _I, _F, _P]),
@@ -240,6 +242,56 @@ def paged_attention_prefill(q, k_pool, v_pool, block_tables, context_lens, query
         float(scale), _stream(dev, stream))
     _raise(rc, "paged_attention_prefill")
     return out
+
+
+def paged_attention_prefill_split(q, k_pool, v_pool, block_tables, context_lens, query_start,
+                                  scale, max_query_len, partition_size, max_partitions=None,
+                                  partial_out=None, partial_lse=None, row_context_lens=None,
+                                  stream=None):
+    """Split pass of chunked-prefill attention over context partitions.
+    Returns (partial_out [total_q, Hq, Pm, D] fp32, partial_lse [total_q, Hq,
+    Pm] fp32, row_context_lens [total_q] int32); merge with
+    split_reduce(partial_out, partial_lse, row_context_lens, partition_size).
+    row_context_lens starts as zeros when allocated here, so rows no sequence
+    owns merge to zeros."""
+    _need(q, "q", torch.float16, 3)
+    dev = q.device
+    _need(k_pool, "k_pool", torch.float16, 4, dev)
+    _need(v_pool, "v_pool", torch.float16, 4, dev)
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    _need(query_start, "query_start", torch.int32, 1, dev)
+    T, Hq, D = q.shape
+    NB, bs, Hkv, D2 = k_pool.shape
+    B = context_lens.shape[0]
+    if v_pool.shape != k_pool.shape or D2 != D:
+        raise ValueError("pools must be [num_blocks, block_size, Hkv, D] with q's D")
+    if block_tables.shape[0] != B or query_start.shape != (B + 1,):
+        raise ValueError("block_tables must be [B, max_blocks] and query_start [B + 1]")
+    maxb = block_tables.shape[1]
+    if max_partitions is None:
+        max_partitions = max_partitions_for(maxb, bs, partition_size)
+    Pm = int(max_partitions)
+    if partial_out is None:
+        partial_out = torch.empty((T, Hq, Pm, D), dtype=torch.float32, device=dev)
+    if partial_lse is None:
+        partial_lse = torch.empty((T, Hq, Pm), dtype=torch.float32, device=dev)
+    if row_context_lens is None:
+        row_context_lens = torch.zeros((T,), dtype=torch.int32, device=dev)
+    _need(partial_out, "partial_out", torch.float32, 4, dev)
+    _need(partial_lse, "partial_lse", torch.float32, 3, dev)
+    _need(row_context_lens, "row_context_lens", torch.int32, 1, dev)
+    if partial_out.shape != (T, Hq, Pm, D) or partial_lse.shape != (T, Hq, Pm) or \
+            row_context_lens.shape != (T,):
+        raise ValueError("partials must be [total_q, Hq, Pm, D] / [total_q, Hq, Pm] and "
+                         "row_context_lens [total_q]")
+    rc = load_library().paged_attention_prefill_split(
+        _ptr(partial_out), _ptr(partial_lse), _ptr(row_context_lens), _ptr(q), _ptr(k_pool),
+        _ptr(v_pool), _ptr(block_tables), _ptr(context_lens), _ptr(query_start), B,
+        int(max_query_len), Hq, Hkv, D, bs, NB, maxb, int(partition_size), Pm, float(scale),
+        _stream(dev, stream))
+    _raise(rc, "paged_attention_prefill_split")
+    return partial_out, partial_lse, row_context_lens
 
 
 def _q8_shapes(k_codes, v_codes, k_scales, v_scales, dev):

@@ -189,15 +189,15 @@ int check_attn_common(const void* q, const void* k_pool, const void* v_pool,
 // contexts, 186 vs 201 us at 8 x 512).
 constexpr int kComputeUnits = 256;
 
-template <int D>
+template <int D, bool SPLIT>
 int launch_prefill(const pkv::PrefillParams& p, int64_t grid, hipStream_t st) {
   constexpr int NCT = D == 64 ? 4 : 2;
   if (grid < kComputeUnits)
-    hipLaunchKernelGGL((pkv::prefill_kernel<D, NCT, 8, 2>), dim3((unsigned)grid), dim3(512), 0,
-                       st, p);
+    hipLaunchKernelGGL((pkv::prefill_kernel<D, NCT, 8, 2, SPLIT>), dim3((unsigned)grid),
+                       dim3(512), 0, st, p);
   else
-    hipLaunchKernelGGL((pkv::prefill_kernel<D, NCT, 4, 2>), dim3((unsigned)grid), dim3(256), 0,
-                       st, p);
+    hipLaunchKernelGGL((pkv::prefill_kernel<D, NCT, 4, 2, SPLIT>), dim3((unsigned)grid),
+                       dim3(256), 0, st, p);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
@@ -501,7 +501,65 @@ int paged_attention_prefill(void* out, const void* q, const void* k_pool, const 
   p.max_q = max_query_len;
   p.q_tiles = (int32_t)q_tiles;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return head_dim == 64 ? launch_prefill<64>(p, grid, st) : launch_prefill<128>(p, grid, st);
+  return head_dim == 64 ? launch_prefill<64, false>(p, grid, st)
+                        : launch_prefill<128, false>(p, grid, st);
+}
+
+int paged_attention_prefill_split(float* partial_out, float* partial_lse,
+                                  int32_t* row_context_lens, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* block_tables,
+                                  const int32_t* context_lens, const int32_t* query_start,
+                                  int32_t B, int32_t max_query_len, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, int32_t max_blocks_per_seq,
+                                  int32_t partition_size, int32_t max_partitions, float scale,
+                                  void* stream) {
+  int rc = check_attn_common(q, k_pool, v_pool, block_tables, context_lens, B, num_q_heads,
+                             num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                             scale);
+  if (rc != PKV_OK) return rc;
+  if (max_query_len < 0) return PKV_ERR_INVALID_ARG;
+  if (partition_size <= 0 || max_partitions <= 0 || partition_size % block_size != 0)
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_partitions * partition_size < (int64_t)max_blocks_per_seq * block_size)
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_partitions * partition_size > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  if (B == 0 || max_query_len == 0) return PKV_OK;
+  if (!partial_out || !partial_lse || !row_context_lens || !query_start ||
+      !aligned(partial_out, 16) || !aligned(partial_lse, 4) || !aligned(row_context_lens, 4) ||
+      !aligned(query_start, 4))
+    return PKV_ERR_INVALID_ARG;
+  const int G = num_q_heads / num_kv_heads;
+  const int rows = pkv::prefill_rows_per_tile(head_dim == 64 ? 4 : 2, G);
+  const int64_t q_tiles = (max_query_len + rows - 1) / rows;
+  const int64_t grid = (int64_t)B * num_kv_heads * q_tiles * max_partitions;
+  if (grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
+
+  pkv::PrefillParams p = {};
+  p.a.q = static_cast<const pkv::f16*>(q);
+  p.a.k_pool = static_cast<const pkv::f16*>(k_pool);
+  p.a.v_pool = static_cast<const pkv::f16*>(v_pool);
+  p.a.block_tables = block_tables;
+  p.a.context_lens = context_lens;
+  p.a.partial_out = partial_out;
+  p.a.partial_lse = partial_lse;
+  p.a.Hq = num_q_heads;
+  p.a.Hkv = num_kv_heads;
+  p.a.G = G;
+  p.a.block_size = block_size;
+  p.a.num_blocks = num_blocks;
+  p.a.max_blocks = max_blocks_per_seq;
+  p.a.partition_size = partition_size;
+  p.a.max_partitions = max_partitions;
+  p.a.spb_shift = spb_shift_of(block_size);
+  p.a.scale_log2 = scale * pkv::kLog2e;
+  p.query_start = query_start;
+  p.max_q = max_query_len;
+  p.q_tiles = (int32_t)q_tiles;
+  p.row_ctx = row_context_lens;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return head_dim == 64 ? launch_prefill<64, true>(p, grid, st)
+                        : launch_prefill<128, true>(p, grid, st);
 }
 
 int kv_cache_append_q8(void* k_codes, void* v_codes, float* k_scales, float* v_scales,
@@ -645,6 +703,9 @@ int paged_decode_step_q8(void* out, float* lse_out, void* k_codes, void* v_codes
   return head_dim == 64 ? launch_q8<64, 2>(p, grid, st) : launch_q8<128, 2>(p, grid, st);
 }
 
+constexpr int64_t kRowsMergeAbove = 4096;
+constexpr int32_t kRowsMergeMaxPartitions = 64;
+
 int split_reduce(void* out, float* lse_out, const float* partial_out, const float* partial_lse,
                  const int32_t* context_lens, int32_t B, int32_t num_q_heads, int32_t head_dim,
                  int32_t partition_size, int32_t max_partitions, void* stream) {
@@ -669,7 +730,20 @@ int split_reduce(void* out, float* lse_out, const float* partial_out, const floa
   p.Hq = num_q_heads;
   p.partition_size = partition_size;
   p.max_partitions = max_partitions;
+  p.B = B;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  // Many (row, head) pairs with few partitions each (the rows of a split
+  // prefill): a workgroup per 16 (D=64) or 8 (D=128) pairs instead of one per
+  // pair, whose dispatches would dominate (7,168 for 8 x 64-row chunks).
+  if (grid >= kRowsMergeAbove && max_partitions <= kRowsMergeMaxPartitions) {
+    const int rpw = 256 / (head_dim / 4);
+    const unsigned g = (unsigned)((grid + rpw - 1) / rpw);
+    if (head_dim == 64)
+      hipLaunchKernelGGL(pkv::split_reduce_rows_kernel<64>, dim3(g), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL(pkv::split_reduce_rows_kernel<128>, dim3(g), dim3(256), 0, st, p);
+    return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+  }
   if (head_dim == 64)
     hipLaunchKernelGGL(pkv::split_reduce_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, p);
   else

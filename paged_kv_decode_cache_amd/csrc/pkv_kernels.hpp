@@ -85,6 +85,7 @@ struct ReduceParams {
   const float* partial_lse;
   const int32_t* context_lens;
   int32_t Hq, partition_size, max_partitions;
+  int32_t B;
 };
 
 struct AppendParams {
@@ -1136,6 +1137,57 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const ReduceParams a)
     *reinterpret_cast<f16x4*>(a.out + (size_t)bh * D + 4 * t) = o;
     if (a.lse_out != nullptr && t == 0) a.lse_out[bh] = L > 0.0f ? M + logf(L) : -INFINITY;
   }
+}
+
+// The same merge for many (row, head) pairs with few partitions each (chunk
+// rows of a split prefill, large decode batches): D/4 threads per pair, 4
+// dims each, so a workgroup merges 256/(D/4) pairs.  Each thread streams its
+// pair's partitions with the LSE update, four rows in flight; a -inf lse
+// weighs its (finite) row by zero.
+template <int D>
+__global__ __launch_bounds__(256) void split_reduce_rows_kernel(const ReduceParams a) {
+  constexpr int TPR = D / 4;
+  constexpr int RPW = 256 / TPR;
+  const int t = threadIdx.x;
+  const int64_t bh = (int64_t)blockIdx.x * RPW + t / TPR;
+  const int c = t % TPR;
+  if (bh >= (int64_t)a.B * a.Hq) return;
+  const int b = (int)(bh / a.Hq);
+  const int Pm = a.max_partitions;
+  const int cap = Pm * a.partition_size;
+  int ctx = a.context_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+  const int np = (ctx + a.partition_size - 1) / a.partition_size;
+  const float* lse = a.partial_lse + bh * Pm;
+  const float* po = a.partial_out + bh * Pm * D + 4 * c;
+  float M = -INFINITY, L = 0.0f;
+  f32x4 acc = zero4f();
+  for (int q0 = 0; q0 < np; q0 += 4) {
+    float l[4];
+    f32x4 x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = q0 + j < np;
+      l[j] = in ? lse[q0 + j] : -INFINITY;
+      x[j] = in ? *reinterpret_cast<const f32x4*>(po + (size_t)(q0 + j) * D) : zero4f();
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float Mn = fmaxf(M, l[j]);
+      const float mu = Mn == -INFINITY ? 0.0f : Mn;
+      const float sa = fast_exp2((M - mu) * kLog2e);  // 1 while M holds; 0 from -inf
+      const float sb = fast_exp2((l[j] - mu) * kLog2e);
+      acc = acc * sa + x[j] * sb;
+      L = L * sa + sb;
+      M = Mn;
+    }
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  f16x4 o;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) o[v] = (f16)(acc[v] * inv);
+  *reinterpret_cast<f16x4*>(a.out + (size_t)bh * D + 4 * c) = o;
+  if (a.lse_out != nullptr && c == 0) a.lse_out[bh] = L > 0.0f ? M + logf(L) : -INFINITY;
 }
 
 // Bit-exact scatter of new K/V rows: one thread per 16-byte chunk of one

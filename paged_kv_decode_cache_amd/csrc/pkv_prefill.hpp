@@ -24,12 +24,19 @@ struct PrefillParams {
   const int32_t* query_start;  // [B + 1]: sequence b's rows are query_start[b] .. [b+1]-1
   int32_t max_q;               // bound on every chunk length
   int32_t q_tiles;             // ceil(max_q / QT)
+  int32_t* row_ctx;            // split pass: [total_q], each row's context_lens[b]
 };
 
 // Query rows per workgroup for a group of G heads over NCT column tiles.
 __host__ __device__ constexpr int prefill_rows_per_tile(int nct, int G) { return 16 * nct / G; }
 
-template <int D, int NCT, int NW, int DEPTH>
+// SPLIT: the context is cut into partitions of a.partition_size positions,
+// one workgroup per (sequence, KV head, query tile, partition); each writes
+// fp32 partials and lse per (row, head) into a.partial_out / a.partial_lse
+// ([total_q, Hq, max_partitions, ...]), merged by split_reduce over rows with
+// pp.row_ctx as their lengths.  A row that sees none of a partition's
+// positions gets lse = -inf and a zero row there.
+template <int D, int NCT, int NW, int DEPTH, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams pp) {
   constexpr int NS = 1;
   constexpr int KC = D / 32;
@@ -47,9 +54,15 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams pp
   const int G = a.G;
   const int QT = prefill_rows_per_tile(NCT, G);
   const int kvh = blockIdx.x % Hkv;
-  const int rest = blockIdx.x / Hkv;
+  int rest = blockIdx.x / Hkv;
+  int p = 0;
+  if (SPLIT) {
+    p = rest % a.max_partitions;
+    rest /= a.max_partitions;
+  }
   const int qt = rest % pp.q_tiles;
   const int b = rest / pp.q_tiles;
+  const int t_lo = SPLIT ? p * a.partition_size : 0;  // first position of the partition
 
   const int spb = a.block_size >> 4;
   const int spb_shift = a.spb_shift;
@@ -58,7 +71,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams pp
   const int32_t* bt_row = a.block_tables + (size_t)b * a.max_blocks;
   const __amdgpu_buffer_rsrc_t bt_rs = buffer_rsrc(bt_row, a.max_blocks * 4);
   constexpr int TSTEP = NW;
-  const int s_first = wave;
+  const int s_first = (t_lo >> 4) + wave;
   const int sub_cap = a.max_blocks * spb;
   // first block ids together with the lengths (every table entry is readable)
   int ids[DEPTH];
@@ -77,7 +90,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams pp
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
   const int pos_first = ctx - n + q0;          // position of the tile's first row
   const int t_end = max(0, pos_first + nq);    // positions any row of the tile sees
-  const int sub_end = (t_end + 15) >> 4;
+  // the partition's positions end at a subtile boundary (partition_size is a
+  // multiple of the block size) or at t_end, so the masks below need no change
+  const int sub_end = ((SPLIT ? min(t_end, t_lo + a.partition_size) : t_end) + 15) >> 4;
+  if (SPLIT && p == 0 && kvh == 0 && (int)threadIdx.x < nq)
+    pp.row_ctx[r0 + q0 + threadIdx.x] = ctx;
 
   // Columns: c = 16 t + g is (row q0 + c / G, head c % G); its causal limit
   // qpos[t] (-1: the column is padding or its row precedes position 0).
@@ -241,14 +258,25 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams pp
     const int col = 16 * t + g;
     const bool emits = qpos[t] >= 0 || (col < QT * G && col / G < nq);
     const int i = col / G;
-    auto emit = [&](int db, f32x4 acc, float L, float) {
+    auto emit = [&](int db, f32x4 acc, float L, float M) {
       if (!emits) return;
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-      f16x4 r;
+      const size_t rh = (size_t)(r0 + q0 + i) * a.Hq + kvh * G + col % G;  // (row, head)
+      if (SPLIT) {
+        f32x4 r;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) r[v] = (f16)(acc[v] * inv);
-      *reinterpret_cast<f16x4*>(a.out + ((size_t)(r0 + q0 + i) * a.Hq + kvh * G + col % G) * D +
-                                16 * db + 4 * quad) = r;
+        for (int v = 0; v < 4; ++v) r[v] = acc[v] * inv;
+        *reinterpret_cast<f32x4*>(a.partial_out + (rh * a.max_partitions + p) * D + 16 * db +
+                                  4 * quad) = r;
+        if (db == 0 && quad == 0)
+          a.partial_lse[rh * a.max_partitions + p] =
+              L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+      } else {
+        f16x4 r;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) r[v] = (f16)(acc[v] * inv);
+        *reinterpret_cast<f16x4*>(a.out + rh * D + 16 * db + 4 * quad) = r;
+      }
     };
     if (NW == 1) {
 #pragma unroll

@@ -225,6 +225,43 @@ def test_prefill_empty_is_noop():
     assert _prefill(lib, maxq=0) == 0
 
 
+def _prefill_split(lib, **kw):
+    a = dict(po=0xA0000, pl=0xB0000, rl=0xC0000, q=B16, k=C16, v=D16, bt=E16, ctx=F16,
+             qs=F16 + 0x1000, B=2, maxq=8, Hq=14, Hkv=2, D=64, bs=16, NB=10, maxb=4, P=32,
+             Pm=2, scale=0.125)
+    a.update(kw)
+    return lib.paged_attention_prefill_split(a["po"], a["pl"], a["rl"], a["q"], a["k"], a["v"],
+                                             a["bt"], a["ctx"], a["qs"], a["B"], a["maxq"],
+                                             a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"],
+                                             a["maxb"], a["P"], a["Pm"], a["scale"], None)
+
+
+PREFILL_SPLIT_BAD = [
+    ("null partials", dict(po=None), -1),
+    ("null row lengths", dict(rl=None), -1),
+    ("misaligned partials", dict(po=0xA0000 + 4), -1),
+    ("misaligned row lengths", dict(rl=0xC0000 + 2), -1),
+    ("null query_start", dict(qs=None), -1),
+    ("partition not a block multiple", dict(P=24), -1),
+    ("partitions do not cover the table", dict(Pm=1), -1),
+    ("negative max_query_len", dict(maxq=-1), -1),
+    ("head dim 96", dict(D=96), -2),
+]
+
+
+@host_only
+@pytest.mark.parametrize("name,kw,code", PREFILL_SPLIT_BAD, ids=[d[0] for d in PREFILL_SPLIT_BAD])
+def test_prefill_split_rejects(name, kw, code):
+    assert _prefill_split(pkv.load_library(), **kw) == code
+
+
+@host_only
+def test_prefill_split_empty_is_noop():
+    lib = pkv.load_library()
+    assert _prefill_split(lib, B=0) == 0
+    assert _prefill_split(lib, maxq=0) == 0
+
+
 def _step(lib, **kw):
     a = dict(out=A16, lse=None, k=C16, v=D16, q=B16, kn=0x70000, vn=0x80000, slots=0x90000,
              bt=E16, ctx=F16, po=0xA0000, pl=0xB0000, cnt=0xC0000, B=2, Hq=14, Hkv=2, D=64,

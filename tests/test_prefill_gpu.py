@@ -155,3 +155,70 @@ def test_prefill_scale_sign_and_zero(scale):
     want = ref.paged_attention_prefill(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens,
                                        c.query_start, c.scale)
     check_fp16(out, want, f"prefill scale {scale}")
+
+
+# ---- split over context partitions + split_reduce ----------------------------
+
+def _prefill_split(c, kp, vp, P, max_q=None):
+    po, pl, rl = pkv.paged_attention_prefill_split(
+        _t(c.q), kp, vp, _t(c.block_tables), _t(c.context_lens), _t(c.query_start), c.scale,
+        c.max_q if max_q is None else max_q, P)
+    return pkv.split_reduce(po, pl, rl, P), po, pl, rl
+
+
+def _row_lens(c):
+    """The length each chunk row carries into the merge: its sequence's
+    context length."""
+    lens = np.zeros(int(c.query_start[-1]), dtype=np.int32)
+    for b in range(len(c.context_lens)):
+        lens[c.query_start[b]:c.query_start[b + 1]] = c.context_lens[b]
+    return lens
+
+
+@pytest.mark.parametrize("name,Hq,Hkv,D,bs,ctx,chunk", CASES, ids=[x[0] for x in CASES])
+def test_prefill_split_matches_oracle(name, Hq, Hkv, D, bs, ctx, chunk):
+    """Split pass + split_reduce against the oracle's prefill, at a partition
+    of two blocks (many partitions, rows that see none of the later ones) and
+    one of 64 blocks; the per-row lengths exactly the sequences'."""
+    c = workloads.prefill_case(name, Hq=Hq, Hkv=Hkv, D=D, block_size=bs, ctx=ctx, chunk=chunk,
+                               seed=410)
+    want = ref.paged_attention_prefill(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens,
+                                       c.query_start, c.scale)
+    for P in (2 * bs, 64 * bs):
+        say(f"prefill split {name} P={P}")
+        out, po, pl, rl = _prefill_split(c, _t(c.k_pool), _t(c.v_pool), P)
+        torch.cuda.synchronize()
+        check_fp16(out, want, f"prefill split {name} P={P}")
+        assert np.array_equal(rl.cpu().numpy(), _row_lens(c))
+
+
+def test_prefill_split_short_chunks_long_context():
+    """The case the split is for: 8 sequences, 64-row chunks ending at
+    position 4095 (q x 4: peaked softmax), partitions of 512 and 1024."""
+    c = workloads.prefill_case("c64", Hq=14, Hkv=2, D=64, block_size=16, ctx=[4096] * 8,
+                               chunk=[64] * 8, seed=411, q_mult=4.0)
+    want = ref.paged_attention_prefill(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens,
+                                       c.query_start, c.scale)
+    for P in (512, 1024):
+        say(f"prefill split 8 x 64 rows at ctx 4096, P={P}")
+        out, _, _, _ = _prefill_split(c, _t(c.k_pool), _t(c.v_pool), P)
+        torch.cuda.synchronize()
+        check_fp16(out, want, f"prefill split c64 P={P}")
+
+
+def test_prefill_split_edge_chunks():
+    """As test_edge_chunks, split: rows before position 0 merge to zeros (lse
+    -inf in every partition), empty chunks write nothing."""
+    c = workloads.prefill_case("edges", Hq=14, Hkv=2, D=64, block_size=16,
+                               ctx=[10, 0, 50, 3, 16], chunk=[0, 0, 7, 9, 16], seed=412)
+    want = ref.paged_attention_prefill(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens,
+                                       c.query_start, c.scale)
+    for max_q in (c.max_q, c.max_q + 40):
+        for P in (16, 32):
+            out, po, pl, rl = _prefill_split(c, _t(c.k_pool), _t(c.v_pool), P, max_q=max_q)
+            torch.cuda.synchronize()
+            check_fp16(out, want, f"split edges max_q={max_q} P={P}")
+            r = int(c.query_start[3])
+            assert int((out[r:r + 6] != 0).sum()) == 0
+            assert bool(torch.isneginf(pl[r:r + 6, :, :1]).all())
+            assert np.array_equal(rl.cpu().numpy(), _row_lens(c))

@@ -184,3 +184,24 @@ def test_split_compact_ragged_and_empty_sequences():
     check_fp16(out, want, "compact ragged")
     _check_lse(lse, want_lse, "compact ragged")
     assert torch.isneginf(pl[0]).all() and torch.isneginf(pl[4]).all()
+
+
+def test_split_reduce_many_rows_few_partitions():
+    """Large batch, few partitions (the library's row-batched merge): B=320 at
+    Hq=14 (4,480 pairs), lengths 1..600 at P=64 and P=512, and the same merge
+    of the split prefill's rows is covered in tests/test_prefill_gpu.py."""
+    rng = np.random.default_rng(130)
+    lens = rng.integers(1, 601, 320).tolist()
+    c = workloads.custom_case("many_rows", B=320, Hq=14, Hkv=2, D=64, block_size=16, lens=lens,
+                              seed=131)
+    g = to_gpu(c)
+    rows = sample_rows(c, 24)
+    want, want_lse = oracle_decode(c, seqs=rows)
+    for P in (64, 512):
+        po, pl = pkv.paged_attention_decode_split(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale,
+                                                  P)
+        out, lse = pkv.split_reduce(po, pl, g.ctx, P, want_lse=True)
+        torch.cuda.synchronize()
+        check_fp16(out, want, f"many rows P={P}", rows=rows)
+        got_lse = host64(lse)[rows]
+        assert float(np.abs(got_lse - want_lse[rows]).max()) <= PARTIAL_ATOL
