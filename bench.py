@@ -349,6 +349,9 @@ def run_headline(args):
     ctx_sum = int(case.context_lens.astype(np.int64).sum())
     step_bytes = alg_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
     app_bytes = append_bytes(B, case.Hkv, case.D)
+    # the library's default tile: 1 subtile for the fused step, 2 for the split
+    # pass at head_dim 64 (an explicit --subtiles applies to both)
+    ns_step = args.subtiles or 1
     ns = args.subtiles or (2 if case.D == 64 else 1)
     nw = args.waves or 4
     depth = args.depth or 2
@@ -357,7 +360,8 @@ def run_headline(args):
         ms_per_step = fused_us * 1e-3
         kern_us = fused_us
         kbytes = step_bytes + app_bytes
-        kname = f"void pkv::attn_kernel<{case.D}, {ns}, {nw}, {depth}, 2, {dual}>(pkv::AttnParams)"
+        kname = (f"void pkv::attn_kernel<{case.D}, {ns_step}, {nw}, {depth}, 2, {dual}>"
+                 "(pkv::AttnParams)")
         step_desc = "paged_decode_step (append + split pass + merge in one launch)"
     else:
         ms_per_step = three_us * 1e-3

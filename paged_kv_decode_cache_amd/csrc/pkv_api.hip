@@ -133,11 +133,23 @@ void launch_compact(const AttnParams& p, int64_t grid, hipStream_t st) {
                        0, st, p);
 }
 
+// The fused step's default tile at head_dim 64 is one subtile, not the split
+// pass's two: its last tile's compute is exposed before the hand-off, and one
+// subtile measured 1-2% faster at B=32 x 4096, B=8 x 4096, B=32 x 2048 and
+// B=128 x 4096 (the split pass alone is not faster with it).  An explicit
+// pkv_set_launch_config subtile count applies as given.
+Shape step_default(Shape s, int head_dim) {
+  if (head_dim == 64 && g_cfg_subtiles[1].load(std::memory_order_relaxed) == 0) s.subtiles = 1;
+  return s;
+}
+
 template <int MODE>
 int launch_attn(const AttnParams& p, int head_dim, int64_t grid, hipStream_t st) {
-  const Shape s = pick_shape(MODE == 0 ? 0 : 1, head_dim);
+  Shape s = pick_shape(MODE == 0 ? 0 : 1, head_dim);
+  if constexpr (MODE == 2) s = step_default(s, head_dim);
   if constexpr (MODE >= 1) {
-    const Shape d = pick_default_shape(1, head_dim);
+    Shape d = pick_default_shape(1, head_dim);
+    if constexpr (MODE == 2) d = step_default(d, head_dim);
     const int mode = g_grid_mode.load(std::memory_order_relaxed);
     const bool same_shape =
         s.waves == d.waves && s.subtiles == d.subtiles && s.depth == d.depth;
