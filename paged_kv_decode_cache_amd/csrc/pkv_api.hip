@@ -717,8 +717,11 @@ int paged_decode_step_q8(void* out, float* lse_out, void* k_codes, void* v_codes
   return head_dim == 64 ? launch_q8<64, 2>(p, grid, st) : launch_q8<128, 2>(p, grid, st);
 }
 
+// The row-batched merge walks a pair's partitions four at a time, one memory
+// round trip per four; the per-pair kernel keeps 16 rows in flight.  So the
+// row-batched form is taken only where it needs at most four round trips.
 constexpr int64_t kRowsMergeAbove = 4096;
-constexpr int32_t kRowsMergeMaxPartitions = 64;
+constexpr int32_t kRowsMergeMaxPartitions = 16;
 
 int split_reduce(void* out, float* lse_out, const float* partial_out, const float* partial_lse,
                  const int32_t* context_lens, int32_t B, int32_t num_q_heads, int32_t head_dim,
