@@ -702,31 +702,23 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
 
   // The block ids of the wave's first DEPTH tiles are requested together with
   // the context length (not after it): any entry of the table row is a valid
-  // read, and ids past the context are masked once the length is known.
-  // Unsplit and split pass: as scalar loads that share the length's round
-  // trip (measured 1.3-1.8% faster than the vector path).  The fused step
-  // keeps the vector path: there the compiler spreads the scalar loads over
-  // more round trips (it is short of scalar registers).
+  // read, and ids past the context are masked once the length is known.  They
+  // are scalar loads that share the length's round trip (measured 1.3-1.8%
+  // faster than vector loads in the split pass, and 1.7-3.8% in the fused
+  // step once its tile is one subtile).
   const int t_begin = SPLIT ? p * a.partition_size : 0;
   const int sub_begin = t_begin >> 4;
   const int s_first = sub_begin + wave * NS;
   ScalarIds<NS> ids0[DEPTH];
   int ids[DEPTH];
-  if constexpr (!STEP) {
 #pragma unroll
-    for (int i = 0; i < DEPTH; ++i)
+  for (int i = 0; i < DEPTH; ++i)
 #pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const int s = s_first + i * TSTEP + j;
-        const int blk = spb_shift >= 0 ? (s >> spb_shift) : (s / spb);
-        ids0[i].v[j] = bt_row[blk < a.max_blocks ? blk : a.max_blocks - 1];
-      }
-  } else {
-    const int sub_cap = a.max_blocks * spb;  // subtiles the table row covers
-#pragma unroll
-    for (int i = 0; i < DEPTH; ++i)
-      ids[i] = load_block_ids<NS>(bt_rs, s_first + i * TSTEP, sub_cap, spb, spb_shift, lane);
-  }
+    for (int j = 0; j < NS; ++j) {
+      const int s = s_first + i * TSTEP + j;
+      const int blk = spb_shift >= 0 ? (s >> spb_shift) : (s / spb);
+      ids0[i].v[j] = bt_row[blk < a.max_blocks ? blk : a.max_blocks - 1];
+    }
 
   // Fused step: the new token's slot, requested before the length so that
   // one round trip brings both (the owner of the new token must not wait for
@@ -823,12 +815,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   KVTile<D, NS> buf[DEPTH];
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) {
-    if constexpr (!STEP)
-      load_kv_tile<D, NS>(buf[i], a, ids0[i], s_first + i * TSTEP, sub_end, t_end, spb,
-                          spb_shift, tok_stride, kvh, lane_off_b, s_new);
-    else
-      load_kv_tile<D, NS>(buf[i], a, ids[i], s_first + i * TSTEP, sub_end, t_end, spb,
-                          spb_shift, tok_stride, kvh, lane_off_b, s_new);
+    load_kv_tile<D, NS>(buf[i], a, ids0[i], s_first + i * TSTEP, sub_end, t_end, spb,
+                        spb_shift, tok_stride, kvh, lane_off_b, s_new);
     ids[i] = load_block_ids<NS>(bt_rs, s_first + (i + DEPTH) * TSTEP, sub_end, spb, spb_shift,
                                 lane);
   }
