@@ -349,3 +349,28 @@ def test_q8_step_in_hip_graph_replays():
         junk = torch.randn(1024, device=g.q.device).sum()
         torch.cuda.synchronize()
         del junk
+
+
+def test_q8_step_ragged_many_partitions():
+    """A ragged batch at a small partition (up to 128 partitions per sequence,
+    most of the grid's workgroups empty): the merge walks many batches of
+    rows.  Sampled sequences against the oracle's 8-bit append + decode; the
+    cache write checked whole."""
+    rng = np.random.default_rng(140)
+    lens = rng.integers(1, 8193, 24).tolist()
+    lens[0], lens[1] = 8192, 1
+    c = workloads.custom_case("q8_ragged", B=24, Hq=14, Hkv=2, D=64, block_size=16, lens=lens,
+                              seed=141)
+    kc, vc, ks, vs = workloads.q8_pools(c)
+    g = to_gpu(c)
+    gq = _gpu_q8(kc, vc, ks, vs)
+    P = 64
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    out = _step_q8(g, gq, c, P, ws, want_lse=False)
+    torch.cuda.synchronize()
+    want_pools = ref.kv_cache_append_q8(kc, vc, ks, vs, c.k_new, c.v_new, c.slot_mapping)
+    _check_pools_q8(gq, want_pools)
+    rows = [0, 1] + rng.choice(np.arange(2, 24), 6, replace=False).tolist()
+    want, _ = _oracle_decode_q8(c, *want_pools, seqs=rows)
+    check_fp16(out, want, "q8 step ragged", rows=rows)
+    _check_workspace_restored(ws)
