@@ -411,8 +411,6 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   for (int i = 0; i < DEPTH; ++i)
     ids[i] = load_block_ids<NS>(bt_rs, s_first + i * TSTEP, sub_cap, spb, spb_shift, lane);
 
-  // Fused step: the new token's slot, requested with the length.
-  const int64_t slot_in = STEP && a.slot_mapping != nullptr ? a.slot_mapping[b] : -1;
   const int cap = a.max_blocks * a.block_size;
   int ctx = a.context_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
@@ -437,7 +435,10 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   // end (the launch never reads its own write).
   const bool owns_new =
       STEP && a.slot_mapping != nullptr && p == (ctx > 0 ? (ctx - 1) / a.partition_size : 0);
-  const int64_t slot = owns_new ? slot_in : -1;
+  // The slot is needed only at the tile holding position ctx-1 and at the
+  // end, so it is requested after the length (the slot pointer comes in a
+  // later batch of argument loads than the length pointer).
+  const int64_t slot = owns_new ? a.slot_mapping[b] : -1;
   int s_new = -1, tok_new = -1, new_off = 0;
   u32x4 kq[DC], vq[DC];
   float ksc = 0.0f, vsc = 0.0f;
