@@ -136,20 +136,36 @@ void launch_compact(const AttnParams& p, int64_t grid, hipStream_t st) {
 // The fused step's default tile at head_dim 64 is one subtile, not the split
 // pass's two: its last tile's compute is exposed before the hand-off, and one
 // subtile measured 1-2% faster at B=32 x 4096, B=8 x 4096, B=32 x 2048 and
-// B=128 x 4096 (the split pass alone is not faster with it).  An explicit
-// pkv_set_launch_config subtile count applies as given.
-Shape step_default(Shape s, int head_dim) {
+// B=128 x 4096 (the split pass alone is not faster with it).
+// With many partitions per (sequence, KV head) and a grid of at most one
+// workgroup per CU, the merging workgroup's walk over the partials is the
+// tail.  When its threads at 4 waves hold more partition rows than one batch
+// of loads (kMergeRowsInFlight), 8 waves (twice the merge threads) shorten
+// it: at head_dim 64, B=1 x 32768 P=512 13.9 vs 16.3 us, B=1 x 131072
+// P=1024 25.3 vs 28.6 us (best P each), B=4 x 32768 P=1024 19.6 vs 20.2 us.
+// With one batch either way 8 waves only add cost (B=1 x 4096 at 16
+// partitions: 8.75 vs 8.54 us), and with more workgroups than CUs 4 waves
+// stay faster (B=4 x 32768 P=512: 24.4 vs 28.9 us).  Explicit
+// pkv_set_launch_config values apply as given.
+constexpr int64_t kStepWideMergeMaxGrid = 256;
+Shape step_default(Shape s, int head_dim, int64_t grid, int max_partitions, int group) {
   if (head_dim == 64 && g_cfg_subtiles[1].load(std::memory_order_relaxed) == 0) s.subtiles = 1;
+  if (head_dim == 64 && g_cfg_waves[1].load(std::memory_order_relaxed) == 0 &&
+      grid <= kStepWideMergeMaxGrid) {
+    const int per_set = group * (64 / 4);  // merge threads per set of partitions (4 dims each)
+    const int sets4 = per_set <= 4 * 64 ? 4 * 64 / per_set : 1;
+    if ((max_partitions + sets4 - 1) / sets4 > pkv::kMergeRowsInFlight) s.waves = 8;
+  }
   return s;
 }
 
 template <int MODE>
 int launch_attn(const AttnParams& p, int head_dim, int64_t grid, hipStream_t st) {
   Shape s = pick_shape(MODE == 0 ? 0 : 1, head_dim);
-  if constexpr (MODE == 2) s = step_default(s, head_dim);
+  if constexpr (MODE == 2) s = step_default(s, head_dim, grid, p.max_partitions, p.G);
   if constexpr (MODE >= 1) {
     Shape d = pick_default_shape(1, head_dim);
-    if constexpr (MODE == 2) d = step_default(d, head_dim);
+    if constexpr (MODE == 2) d = step_default(d, head_dim, grid, p.max_partitions, p.G);
     const int mode = g_grid_mode.load(std::memory_order_relaxed);
     const bool same_shape =
         s.waves == d.waves && s.subtiles == d.subtiles && s.depth == d.depth;

@@ -495,6 +495,7 @@ __device__ __forceinline__ void merge_waves_impl(const SoftmaxState<D>& st, floa
 }
 
 constexpr int kMergeSlots = 512;  // >= 16 heads x 128/4 dims
+constexpr int kMergeRowsInFlight = 8;  // the merge's largest batch of partition rows per thread
 constexpr int kSpinLimit = 1 << 20;
 
 // Streaming LSE merge of one thread's rows (partitions grp, grp + ngroups, ...
@@ -605,7 +606,8 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
     else if (rows <= 4)
       merge_rows<D, 4>(po_rs, pl_rs, Pm, np, p_own, grp, ngroups, hh, cc, own_x, own_l, M, L, acc);
     else
-      merge_rows<D, 8>(po_rs, pl_rs, Pm, np, p_own, grp, ngroups, hh, cc, own_x, own_l, M, L, acc);
+      merge_rows<D, kMergeRowsInFlight>(po_rs, pl_rs, Pm, np, p_own, grp, ngroups, hh, cc, own_x,
+                                        own_l, M, L, acc);
     float* r = msm + 6 * slot;
     r[0] = M;
     r[1] = L;

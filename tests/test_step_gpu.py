@@ -48,7 +48,8 @@ def _check_lse(got, want, rows=None):
 @pytest.mark.parametrize("name,P", [("tiny", 16), ("tiny", 64), ("qwen", 512), ("qwen", 128),
                                     ("sweep:32:4096", 512), ("sweep:1:128", 512),
                                     ("sweep:8:2048", 256), ("long:1:32768", 512),
-                                    ("long:4:32768", 2048)])
+                                    ("long:4:32768", 2048), ("long:4:32768", 1024),
+                                    ("long:4:32768", 512)])
 def test_step_matches_append_then_decode(name, P):
     c = case(name)
     say(f"step {name} P={P}")
