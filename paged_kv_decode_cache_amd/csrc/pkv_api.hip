@@ -148,14 +148,17 @@ void launch_compact(const AttnParams& p, int64_t grid, hipStream_t st) {
 // stay faster (B=4 x 32768 P=512: 24.4 vs 28.9 us).  Explicit
 // pkv_set_launch_config values apply as given.
 constexpr int64_t kStepWideMergeMaxGrid = 256;
+bool step_wide_merge(int head_dim, int64_t grid, int max_partitions, int group) {
+  if (head_dim != 64 || grid > kStepWideMergeMaxGrid) return false;
+  const int per_set = group * (64 / 4);  // merge threads per set of partitions (4 dims each)
+  const int sets4 = per_set <= 4 * 64 ? 4 * 64 / per_set : 1;
+  return (max_partitions + sets4 - 1) / sets4 > pkv::kMergeRowsInFlight;
+}
 Shape step_default(Shape s, int head_dim, int64_t grid, int max_partitions, int group) {
   if (head_dim == 64 && g_cfg_subtiles[1].load(std::memory_order_relaxed) == 0) s.subtiles = 1;
-  if (head_dim == 64 && g_cfg_waves[1].load(std::memory_order_relaxed) == 0 &&
-      grid <= kStepWideMergeMaxGrid) {
-    const int per_set = group * (64 / 4);  // merge threads per set of partitions (4 dims each)
-    const int sets4 = per_set <= 4 * 64 ? 4 * 64 / per_set : 1;
-    if ((max_partitions + sets4 - 1) / sets4 > pkv::kMergeRowsInFlight) s.waves = 8;
-  }
+  if (g_cfg_waves[1].load(std::memory_order_relaxed) == 0 &&
+      step_wide_merge(head_dim, grid, max_partitions, group))
+    s.waves = 8;
   return s;
 }
 
@@ -234,16 +237,28 @@ int launch_prefill(const pkv::PrefillParams& p, int64_t grid, hipStream_t st) {
 // fused step, which takes 1 (as the fp16 step: 15.9 vs 16.8 us at
 // B=32 x 4096, 11.3 vs 11.45 us at B=8 x 4096, 0.6% slower at B=128 x 8192).
 // MODE: 0 unsplit, 1 split pass, 2 fused decode step.
-template <int D, int MODE>
-int launch_q8(const pkv::Q8Params& p, int64_t grid, hipStream_t st) {
+template <int D, int NW, int MODE>
+void launch_q8_nw(const pkv::Q8Params& p, int64_t grid, hipStream_t st) {
   constexpr int NS = (D == 64 && MODE != 2) ? 2 : 1;
-  constexpr int NW = MODE >= 1 ? 4 : 8;
   if (p.a.G <= 8)
     hipLaunchKernelGGL((pkv::attn_q8_kernel<D, NS, NW, 2, MODE, true>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, st, p);
   else
     hipLaunchKernelGGL((pkv::attn_q8_kernel<D, NS, NW, 2, MODE, false>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, st, p);
+}
+
+// The fused step takes 8 waves where the fp16 step does (step_wide_merge).
+template <int D, int MODE>
+int launch_q8(const pkv::Q8Params& p, int64_t grid, hipStream_t st) {
+  if constexpr (MODE == 2 && D == 64) {
+    if (step_wide_merge(D, grid, p.a.max_partitions, p.a.G))
+      launch_q8_nw<D, 8, MODE>(p, grid, st);
+    else
+      launch_q8_nw<D, 4, MODE>(p, grid, st);
+  } else {
+    launch_q8_nw<D, MODE >= 1 ? 4 : 8, MODE>(p, grid, st);
+  }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

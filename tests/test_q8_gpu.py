@@ -223,7 +223,8 @@ def _check_workspace_restored(ws):
 
 @pytest.mark.parametrize("name,P", [("tiny", 16), ("qwen", 256), ("qwen", 1024),
                                     ("sweep:32:4096", 1024), ("sweep:8:2048", 256),
-                                    ("long:1:32768", 1024)])
+                                    ("long:1:32768", 1024), ("long:1:32768", 512),
+                                    ("long:4:32768", 512)])
 def test_q8_step_matches_append_then_decode(name, P):
     """The fused 8-bit step (quantising append + split pass + merge in one
     launch) against the oracle's kv_cache_append_q8 followed by its decode
