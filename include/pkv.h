@@ -96,11 +96,17 @@ int pkv_version(void);
 /*
  * pkv_set_launch_config -- tuning aid: choose the launch shape of an
  * attention pass for later calls in this process.
- *   which              0 = paged_attention_decode, 1 = the split pass.
+ *   which              0 = paged_attention_decode, 1 = the split pass and
+ *                      paged_decode_step.
  *   waves_per_group    wavefronts (64 lanes) per workgroup: 1, 2, 4 or 8.
  *   subtiles_per_tile  16-token subtiles a wave loads per tile: 1, 2 or 4.
  *   tiles_in_flight    tiles of K/V a wave keeps in flight: 2 or 4.
- * 0 in any of the last three restores its default.  Shapes beyond the
+ * 0 in any of the last three restores its default.  At head_dim 64 the
+ * step's defaults differ from the split pass's: one subtile per tile, and 8
+ * waves when the grid is at most 256 workgroups and the merging workgroup's
+ * threads at 4 waves would each hold more than 8 partition rows (the 8-bit
+ * step follows the same wave rule; the 8-bit passes take no other
+ * setting).  Shapes beyond the
  * register budget (more than 8 subtiles in flight at head_dim 64, 4 at
  * head_dim 128) are reduced to fit.  Results do not depend on the shape
  * beyond fp32 summation order.  Not synchronised with concurrent launches (a
