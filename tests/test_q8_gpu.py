@@ -375,3 +375,27 @@ def test_q8_step_ragged_many_partitions():
     want, _ = _oracle_decode_q8(c, *want_pools, seqs=rows)
     check_fp16(out, want, "q8 step ragged", rows=rows)
     _check_workspace_restored(ws)
+
+
+def test_q8_step_wide_merge_large_group():
+    """The 8-bit step with groups of 16 query heads at long contexts with few
+    workgroups, where it takes 8 waves for the merge: against the oracle's
+    8-bit append + decode; the cache write bit-exact."""
+    c = workloads.custom_case("q8_step_wide_g16", B=2, Hq=32, Hkv=2, D=64, block_size=16,
+                              lens=[16384, 9001], seed=151)
+    kc, vc, ks, vs = workloads.q8_pools(c)
+    g = to_gpu(c)
+    gq = _gpu_q8(kc, vc, ks, vs)
+    P = 1024
+    say(f"q8 step wide merge G=16 P={P}")
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    out, lse = _step_q8(g, gq, c, P, ws)
+    torch.cuda.synchronize()
+    want_pools = ref.kv_cache_append_q8(kc, vc, ks, vs, c.k_new, c.v_new, c.slot_mapping)
+    _check_pools_q8(gq, want_pools)
+    want, want_lse = _oracle_decode_q8(c, *want_pools)
+    check_fp16(out, want, "q8 step wide merge G=16")
+    g_lse = host64(lse)
+    fin = np.isfinite(want_lse)
+    assert float(np.abs(g_lse[fin] - want_lse[fin]).max()) <= PARTIAL_ATOL
+

@@ -286,3 +286,30 @@ def test_step_compact_grid_edges_and_churn():
         assert worst <= 2e-3, worst
     finally:
         pkv.set_grid_mode("auto")
+
+
+def test_step_wide_merge_large_group():
+    """Groups of 16 query heads (the kernel variant without the dual-half
+    columns) at long contexts with few workgroups: the step's default launch
+    takes 8 waves for the merge.  Against the oracle's append + decode, and
+    against an explicit 4-wave launch."""
+    c = workloads.custom_case("step_wide_g16", B=2, Hq=32, Hkv=2, D=64, block_size=16,
+                              lens=[16384, 9001], seed=150, q_mult=4.0)
+    P = 1024  # 16 partitions, grid 2 x 2 x 16 = 64
+    say(f"step wide merge G=16 P={P}")
+    g = to_gpu(c)
+    out, lse = _step(g, c, P)
+    torch.cuda.synchronize()
+    want, want_lse, kp, _ = _oracle_step(c)
+    check_fp16(out, want, "step wide merge G=16")
+    _check_lse(lse, want_lse)
+    assert np.array_equal(g.k_pool.cpu().numpy().view(np.uint16), kp.view(np.uint16))
+    g4 = to_gpu(c)
+    pkv.set_launch_config("split", 4, 1, 2)
+    try:
+        out4, _ = _step(g4, c, P)
+        torch.cuda.synchronize()
+    finally:
+        pkv.set_launch_config("split", 0, 0, 0)
+    check_fp16(out4, want, "step G=16 at 4 waves")
+
