@@ -273,8 +273,11 @@ def kv_cache_append(k_pool, v_pool, k_new, v_new, slot_mapping):
     """Write each new token's K/V rows into its slot; returns new pools.
 
     k_new, v_new [N, Hkv, D]; slot_mapping [N] int64 with
-    slot = physical_block * block_size + offset; slot < 0 is skipped.  The
-    inputs are not modified.
+    slot = physical_block * block_size + offset.  A slot that names no row of
+    the pool (slot < 0, or slot >= num_blocks * block_size) is skipped: the
+    reading of the Inference Engineering Day 11 post's per-step cache write
+    taken here (its addressing is not given on the pages).  The inputs are not
+    modified.
     """
     kp = k_pool.copy()
     vp = v_pool.copy()
@@ -282,7 +285,7 @@ def kv_cache_append(k_pool, v_pool, k_new, v_new, slot_mapping):
     flat_k = kp.reshape(nb * bs, *kp.shape[2:])
     flat_v = vp.reshape(nb * bs, *vp.shape[2:])
     slots = np.asarray(slot_mapping, dtype=np.int64)
-    keep = slots >= 0
+    keep = (slots >= 0) & (slots < nb * bs)
     flat_k[slots[keep]] = k_new[keep]
     flat_v[slots[keep]] = v_new[keep]
     return kp, vp

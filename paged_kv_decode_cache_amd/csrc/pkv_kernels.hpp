@@ -271,6 +271,91 @@ __device__ __forceinline__ void load_kv_tile(KVTile<D, NS>& T, const AttnParams&
   T.full = okm == (1 << NS) - 1 && ((s0 + NS) << 4) <= t_end;
 }
 
+// Decode-path K/V loads: whole 128-byte lines per instruction, non-temporal.
+// Eight consecutive lanes (sixteen at head_dim 128) read one token's head row
+// of D halves in 16-byte chunks, so one wave-wide load covers 64 / (D / 8)
+// whole rows (1 KiB).  Measured with a read-only probe of this machine layout
+// (B=32 x 4096 at head_dim 64, random block tables, 64 MiB per launch): 16
+// rows x 64 bytes per instruction -- the MFMA operand layout -- read in
+// 13.5 us; whole rows per instruction with the non-temporal bit in 11.9 us
+// (either change alone: 13.2 and 13.8 us).  The rows are then staged in LDS
+// and read back in the MFMA layouts: K with 16-byte reads, V with the
+// transposing read.  In LDS a row's chunk slot s holds chunk s ^ (row & 7),
+// so the eight rows one 8-lane group of a K read touches hit distinct banks;
+// the swizzle is applied on the load side (each lane loads the chunk its
+// slot holds), which keeps each LDS write a plain 1 KiB contiguous store.
+template <int D>
+struct LineMap {
+  static constexpr int kChunksPerRow = D / 8;          // 16-byte chunks of a head row
+  static constexpr int kRowsPerLoad = 64 / kChunksPerRow;
+  static constexpr int kLoads = D / 32;                // wave loads per 16-row subtile
+  // row (within the subtile) and global chunk of lane's load m
+  static __device__ __forceinline__ int row(int lane, int m) {
+    return kRowsPerLoad * m + lane / kChunksPerRow;
+  }
+  static __device__ __forceinline__ int chunk(int lane, int m) {
+    return (lane % kChunksPerRow) ^ (row(lane, m) & 7);
+  }
+};
+
+template <int D, int NS>
+struct LineSmem {
+  static constexpr int kSubBytes = 16 * D * 2;           // one subtile of K (or V)
+  static constexpr int kStageBytes = 2 * NS * kSubBytes;  // K subtiles, then V subtiles
+  static constexpr int kMergeBytes = ((D / 4) * 64 + 32) * 4;
+  static constexpr int kWaveBytes = kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes;
+};
+
+constexpr int kNonTemporal = 2;  // cache-policy bit of the streaming K/V loads
+
+__device__ __forceinline__ f16x8 load_line16(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(
+      f16x8, __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0,
+                                                                              kNonTemporal)));
+}
+
+// Issue the K/V loads of one tile in the line layout above.  Each subtile's
+// resource starts at its first token's row of head kvh and ends right after
+// the head row of its last attended token, so rows past the context (and
+// every row of a subtile past sub_end or in a block whose id is outside
+// [0, num_blocks)) read as zeros without a memory access: V needs no
+// masking, K's logits are masked by select.  lane_off[m] is the lane's byte
+// offset of load m in a resource.
+template <int D, int NS, typename Ids>
+__device__ __forceinline__ void load_kv_lines(KVTile<D, NS>& T, const AttnParams& a,
+                                              const Ids& ids, int s0, int sub_end, int t_end,
+                                              int spb, int spb_shift, int64_t tok_stride,
+                                              int kvh, const int (&lane_off)[D / 32],
+                                              int s_new) {
+  constexpr int KC = D / 32;
+  T.s0 = s0;
+  int okm = 0;
+  int new_phys = -1;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int phys = block_id_of(ids, j);
+    new_phys = s0 + j == s_new ? phys : new_phys;
+    const bool ok = s0 + j < sub_end && phys >= 0 && phys < a.num_blocks;
+    okm |= (ok ? 1 : 0) << j;
+    const int s = s0 + j;
+    const int sib = spb_shift >= 0 ? (s & (spb - 1)) : (s % spb);
+    const int nvalid = ok ? min(16, t_end - (s << 4)) : 0;  // >= 1 when ok
+    const int bytes = ok ? ((nvalid - 1) * (int)tok_stride + D) * 2 : 0;
+    const int64_t blk_off =
+        ((int64_t)(ok ? phys : 0) * a.block_size + sib * 16) * tok_stride + (int64_t)kvh * D;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(a.k_pool + blk_off, bytes);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(a.v_pool + blk_off, bytes);
+#pragma unroll
+    for (int m = 0; m < KC; ++m) {
+      T.k[j][m] = load_line16(kr, lane_off[m]);
+      T.v[j][m] = load_line16(vr, lane_off[m]);
+    }
+  }
+  T.okmask = okm;
+  T.new_phys = new_phys;
+  T.full = okm == (1 << NS) - 1 && ((s0 + NS) << 4) <= t_end;
+}
+
 // Online-softmax state of one wave: reference maximum (log2 domain) per head
 // column, and the O^T and weight-sum accumulators (MFMA layout: lane
 // (quad, g) holds rows 4*quad + v of column g).
@@ -319,30 +404,53 @@ __device__ __forceinline__ void consume_tile(KVTile<D, NS>& T, SoftmaxState<D>& 
                                              const f16x8 (&vn)[D / 32]) {
   constexpr int KC = D / 32;
   constexpr int NDB = D / 16;
-  constexpr int ROW = D + 4;
   const int g = lane & 15;
   const int quad = lane >> 4;
+  using LM = LineMap<D>;
+  using LS = LineSmem<D, NS>;
   if (SUB && T.new_phys >= 0 && (int64_t)T.new_phys * block_size + new_off == slot) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      const bool mine = T.s0 + j == s_new && (lane & 15) == tok_new;
 #pragma unroll
       for (int m = 0; m < KC; ++m) {
+        const bool mine = T.s0 + j == s_new && LM::row(lane, m) == tok_new;
         T.k[j][m] = mine ? kn[m] : T.k[j][m];
         T.v[j][m] = mine ? vn[m] : T.v[j][m];
       }
     }
   }
 
-  // raw logits S^T[token][column]
+  // K and V of the tile to LDS as loaded: load m of subtile j is 1 KiB of
+  // whole rows, lane l's chunk at byte 16 l.
+  unsigned char* kst = reinterpret_cast<unsigned char*>(stage);
+  unsigned char* vst = kst + NS * LS::kSubBytes;
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+#pragma unroll
+    for (int m = 0; m < KC; ++m) {
+      *reinterpret_cast<f16x8*>(kst + j * LS::kSubBytes + m * 1024 + 16 * lane) = T.k[j][m];
+      *reinterpret_cast<f16x8*>(vst + j * LS::kSubBytes + m * 1024 + 16 * lane) = T.v[j][m];
+    }
+  asm volatile("" ::: "memory");
+
+  // raw logits S^T[token][column]; K in the A layout: lane l holds token
+  // l % 16, dims 8 (l / 16) + 32 m .. + 8 (chunk l / 16 + 4 m, swizzled).
   f32x4 sc[NS];
+  {
+    const int t = lane & 15;
+    const unsigned char* krow = kst + t * (D * 2);
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    f32x4 acc = zero4f();
+    for (int j = 0; j < NS; ++j) {
+      f32x4 acc = zero4f();
 #pragma unroll
-    for (int m = 0; m < KC; ++m)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(T.k[j][m], qb[m], acc, 0, 0, 0);
-    sc[j] = acc;
+      for (int m = 0; m < KC; ++m) {
+        const int ch = ((lane >> 4) + 4 * m) ^ (t & 7);
+        const f16x8 kk =
+            *reinterpret_cast<const f16x8*>(krow + j * LS::kSubBytes + 16 * ch);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kk, qb[m], acc, 0, 0, 0);
+      }
+      sc[j] = acc;
+    }
   }
   if (!T.full) {
 #pragma unroll
@@ -395,29 +503,6 @@ __device__ __forceinline__ void consume_tile(KVTile<D, NS>& T, SoftmaxState<D>& 
     }
   }
 
-  // V subtiles -> LDS, row-major [token][dim]; masked rows as zeros.
-#pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    f16* row = stage + (j * 16 + (lane & 15)) * ROW + 8 * quad;
-    if (T.full) {
-#pragma unroll
-      for (int m = 0; m < KC; ++m) {
-        *reinterpret_cast<f16x4*>(row + 32 * m) = T.v[j][m].lo;
-        *reinterpret_cast<f16x4*>(row + 32 * m + 4) = T.v[j][m].hi;
-      }
-    } else {
-      const int tok = ((T.s0 + j) << 4) + (lane & 15);
-      const bool keep = ((T.okmask >> j) & 1) && tok < t_end;
-#pragma unroll
-      for (int m = 0; m < KC; ++m) {
-        const f16x8 v = keep ? T.v[j][m] : zero8();
-        *reinterpret_cast<f16x4*>(row + 32 * m) = v.lo;
-        *reinterpret_cast<f16x4*>(row + 32 * m + 4) = v.hi;
-      }
-    }
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-
   // V^T operand by transposing LDS reads: within each 16-lane group, lane i
   // of ds_read_b64_tr_b16 receives element (i % 4) of the 8-byte chunks that
   // lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4 point at.  Lane j of quad q points
@@ -425,8 +510,10 @@ __device__ __forceinline__ void consume_tile(KVTile<D, NS>& T, SoftmaxState<D>& 
   // V[4q + k][16 db + i] for k = 0..3: the A operand of the 16x16x16 MFMA.
   // Without DUAL both parts of P go into one 16x16x32 MFMA: its lane (q, i)
   // holds k = 8q .. 8q + 7, taken as the lane's 4 tokens' high parts then
-  // their remainders (B), against the same 4 V values twice (A).
-  const f16* tr = stage + (4 * quad + (g >> 2)) * ROW + 4 * (g & 3);
+  // their remainders (B), against the same 4 V values twice (A).  Rows past
+  // the context were loaded as zeros, so a zero weight never meets a NaN.
+  const int vr = 4 * quad + (g >> 2);
+  const unsigned char* vrow = vst + vr * (D * 2) + 8 * (g & 1);
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const f16x8 pb = __builtin_shufflevector(ph[j], pl[j], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -438,8 +525,9 @@ __device__ __forceinline__ void consume_tile(KVTile<D, NS>& T, SoftmaxState<D>& 
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       typedef short s16x4 __attribute__((ext_vector_type(4)));
+      const int ch = (2 * db + ((g & 3) >> 1)) ^ (vr & 7);
       const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(tr + j * 16 * ROW + 16 * db));
+          (__attribute__((address_space(3))) s16x4*)(vrow + j * LS::kSubBytes + 16 * ch));
       const f16x4 va = __builtin_bit_cast(f16x4, raw);
       if (DUAL)
         st.o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph[j], st.o[db], 0, 0, 0);
@@ -685,7 +773,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   constexpr int NDB = D / 16;  // PV MFMA column blocks (16 dims each)
   constexpr bool SPLIT = MODE >= 1;
   constexpr bool STEP = MODE == 2;
-  using SM = AttnSmem<D, NS>;
+  using SM = LineSmem<D, NS>;
+  using LM = LineMap<D>;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -697,7 +786,10 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   const int spb = a.block_size >> 4;  // subtiles per block
   const int spb_shift = a.spb_shift;
   const int64_t tok_stride = (int64_t)Hkv * D;
-  const int lane_off_b = ((lane & 15) * Hkv * D + 8 * quad) * 2;
+  int lane_off[KC];
+#pragma unroll
+  for (int m = 0; m < KC; ++m)
+    lane_off[m] = (LM::row(lane, m) * (int)tok_stride + 8 * LM::chunk(lane, m)) * 2;
   const int32_t* bt_row = a.block_tables + (size_t)b * a.max_blocks;
   const __amdgpu_buffer_rsrc_t bt_rs = buffer_rsrc(bt_row, a.max_blocks * 4);
   constexpr int TSTEP = NW * NS;  // subtiles between a wave's consecutive tiles
@@ -774,10 +866,11 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
     // A branch around these loads sits before the K/V loop, where it costs
     // the loop's wait counts nothing (loading them through empty resources
     // in every workgroup measured slower).
+    // in the line layout of the K/V loads (load m of this lane)
 #pragma unroll
     for (int m = 0; m < KC; ++m) {
-      kn[m] = *reinterpret_cast<const f16x8*>(a.k_new + new_row + 8 * quad + 32 * m);
-      vn[m] = *reinterpret_cast<const f16x8*>(a.v_new + new_row + 8 * quad + 32 * m);
+      kn[m] = *reinterpret_cast<const f16x8*>(a.k_new + new_row + 8 * LM::chunk(lane, m));
+      vn[m] = *reinterpret_cast<const f16x8*>(a.v_new + new_row + 8 * LM::chunk(lane, m));
     }
   } else {
 #pragma unroll
@@ -826,8 +919,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   KVTile<D, NS> buf[DEPTH];
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) {
-    load_kv_tile<D, NS>(buf[i], a, ids0[i], s_first + i * TSTEP, sub_end, t_end, spb,
-                        spb_shift, tok_stride, kvh, lane_off_b, s_new);
+    load_kv_lines<D, NS>(buf[i], a, ids0[i], s_first + i * TSTEP, sub_end, t_end, spb,
+                         spb_shift, tok_stride, kvh, lane_off, s_new);
     ids[i] = load_block_ids<NS>(bt_rs, s_first + (i + DEPTH) * TSTEP, sub_end, spb, spb_shift,
                                 lane);
   }
@@ -844,8 +937,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
       if (u < n_tiles)
         consume_tile<D, NS, DUAL, STEP>(buf[i], st, qb, stage, c, t_end, lane, ones, rem_mul,
                                         s_new, tok_new, slot, new_off, a.block_size, kn, vn);
-      load_kv_tile<D, NS>(buf[i], a, ids[i], s_first + (u + DEPTH) * TSTEP, sub_end, t_end, spb,
-                          spb_shift, tok_stride, kvh, lane_off_b, s_new);
+      load_kv_lines<D, NS>(buf[i], a, ids[i], s_first + (u + DEPTH) * TSTEP, sub_end, t_end,
+                           spb, spb_shift, tok_stride, kvh, lane_off, s_new);
       ids[i] = load_block_ids<NS>(bt_rs, s_first + (u + 2 * DEPTH) * TSTEP, sub_end, spb,
                                   spb_shift, lane);
     }
@@ -879,14 +972,10 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   // Fused step: the append of the new token's row of this head (after the
   // ticket is read: the wait for it would otherwise include these stores).
   if (owns_new && slot >= 0 && slot < (int64_t)a.num_blocks * a.block_size) {
-    f16* kd = a.k_pool_w + (slot * Hkv + kvh) * D + 8 * quad;
-    f16* vd = a.v_pool_w + (slot * Hkv + kvh) * D + 8 * quad;
-    if (wave == 0 && g == 0) {
-#pragma unroll
-      for (int m = 0; m < KC; ++m) {
-        *reinterpret_cast<f16x8*>(kd + 32 * m) = kn[m];
-        *reinterpret_cast<f16x8*>(vd + 32 * m) = vn[m];
-      }
+    // lanes 0 .. D/8-1 hold the row's chunks 0 .. D/8-1 in load 0 (row 0, no swizzle)
+    if (wave == 0 && lane < LM::kChunksPerRow) {
+      *reinterpret_cast<f16x8*>(a.k_pool_w + (slot * Hkv + kvh) * D + 8 * lane) = kn[0];
+      *reinterpret_cast<f16x8*>(a.v_pool_w + (slot * Hkv + kvh) * D + 8 * lane) = vn[0];
     }
   }
 
@@ -950,7 +1039,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
 // Direct grid: workgroup -> item from its index (B x Hkv x partitions).
 template <int D, int NS, int NW, int DEPTH, int MODE, bool DUAL>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[NW * AttnSmem<D, NS>::kWaveBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NW * LineSmem<D, NS>::kWaveBytes];
   const int kvh = blockIdx.x % a.Hkv;
   const int rest = blockIdx.x / a.Hkv;
   if (MODE >= 1)
@@ -984,7 +1073,7 @@ template <int D, int NS, int NW, int DEPTH, int MODE, bool DUAL>
 __global__ __launch_bounds__(NW * 64) void attn_compact_kernel(const AttnParams a) {
   static_assert(MODE >= 1, "the compact grid is for the partitioned passes");
   constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[NW * AttnSmem<D, NS>::kWaveBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NW * LineSmem<D, NS>::kWaveBytes];
   __shared__ int prefix[kCompactMaxB + 1];
   __shared__ int wave_sum[NW];
   const int t = threadIdx.x;

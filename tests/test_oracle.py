@@ -365,7 +365,8 @@ def test_chunked_prefill_golden():
 
 def pin_append_brute_force():
     """Element loops: written rows equal the inputs, every other byte of the
-    pool is unchanged, negative slots are skipped."""
+    pool is unchanged, and slots naming no row of the pool (negative, or at
+    or past num_blocks * block_size) are skipped."""
     rng = np.random.default_rng(71)
     NB, bs, Hkv, D, N = 6, 16, 2, 64, 9
     kp = rng.standard_normal((NB, bs, Hkv, D)).astype(np.float16)
@@ -374,10 +375,12 @@ def pin_append_brute_force():
     vn = rng.standard_normal((N, Hkv, D)).astype(np.float16)
     slots = rng.choice(NB * bs, size=N, replace=False).astype(np.int64)
     slots[3] = -1
+    slots[5] = NB * bs          # one past the last row
+    slots[7] = NB * bs + 77
     k2, v2 = ref.kv_cache_append(kp, vp, kn, vn, slots)
     written = {}
     for i, s in enumerate(slots):
-        if s >= 0:
+        if 0 <= s < NB * bs:
             written[(int(s) // bs, int(s) % bs)] = i
     for blk in range(NB):
         for off in range(bs):

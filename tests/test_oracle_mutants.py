@@ -93,6 +93,18 @@ def _append_no_skip(k_pool, v_pool, k_new, v_new, slot_mapping):
     return kp, vp
 
 
+def _append_wraps_past_end(k_pool, v_pool, k_new, v_new, slot_mapping):
+    kp, vp = k_pool.copy(), v_pool.copy()
+    nb, bs = kp.shape[:2]
+    for i, s in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if s < 0:
+            continue
+        s = int(s) % (nb * bs)         # a slot past the pool wraps instead of being skipped
+        kp[s // bs, s % bs] = k_new[i]
+        vp[s // bs, s % bs] = v_new[i]
+    return kp, vp
+
+
 def _split_factory(kind):
     orig = ref.paged_attention_decode_split
 
@@ -172,6 +184,7 @@ MUTANTS = {
     "merge_unweighted": ("merge_partitions", _merge_factory("unweighted")),
     "append_transposed_slot": ("kv_cache_append", _append_transposed),
     "append_no_skip": ("kv_cache_append", _append_no_skip),
+    "append_wraps_past_end": ("kv_cache_append", _append_wraps_past_end),
     "split_lse_base2": ("paged_attention_decode_split", _split_factory("lse_log2")),
     "scale_not_fp32": ("fp32_scale", lambda s: float(s) * (1 + 1e-7)),
     "q8_per_tensor_amax": ("quantize_rows_q8", _q8_factory("per_tensor_amax")),
