@@ -283,19 +283,19 @@ def run_headline(args):
     po = torch.empty_like(ws.partial_out)
     pl = torch.empty_like(ws.partial_lse)
     out = torch.empty((B, case.Hq, case.D), dtype=torch.float16, device=device)
-    if args.waves or args.subtiles or args.depth:
-        pkv.set_launch_config("split", args.waves, args.subtiles, args.depth)
+    launch = (dict(waves=args.waves, subtiles=args.subtiles, depth=args.depth)
+              if args.waves or args.subtiles or args.depth else None)
     stream = torch.cuda.current_stream(device)
 
     def fused_step(i):
         r = i % R
         pkv.paged_decode_step(rot.q, rot.k_pool, rot.v_pool, rot.bt[r], rot.ctx, case.scale, P,
                               k_new=rot.k_new, v_new=rot.v_new, slot_mapping=rot.slots[r],
-                              workspace=ws, out=out)
+                              workspace=ws, out=out, launch=launch)
 
     def split_pass(i):
         pkv.paged_attention_decode_split(rot.q, rot.k_pool, rot.v_pool, rot.bt[i % R], rot.ctx,
-                                         case.scale, P, Pm, po, pl)
+                                         case.scale, P, Pm, po, pl, launch=launch)
 
     def three_launch_step(i, ev=None):
         r = i % R
@@ -342,8 +342,6 @@ def run_headline(args):
         rot.q, rot.k_pool, rot.v_pool, rot.bt[r], rot.ctx, case.scale, out=out)
         for r in range(R)])
     unsplit_us = time_graph(g_uns, R, K)
-    if args.waves or args.subtiles or args.depth:
-        pkv.set_launch_config("split", 0, 0, 0)
     probe = probe_read_gbs(rot, case.kv_bytes(), R, K)
 
     ctx_sum = int(case.context_lens.astype(np.int64).sum())

@@ -94,44 +94,41 @@ const char* pkv_status_string(int status);
 int pkv_version(void);
 
 /*
- * pkv_set_launch_config -- tuning aid: choose the launch shape of an
- * attention pass for later calls in this process.
- *   which              0 = paged_attention_decode, 1 = the split pass and
- *                      paged_decode_step.
- *   waves_per_group    wavefronts (64 lanes) per workgroup: 1, 2, 4 or 8.
- *   subtiles_per_tile  16-token subtiles a wave loads per tile: 1, 2 or 4.
- *   tiles_in_flight    tiles of K/V a wave keeps in flight: 2 or 4.
- * 0 in any of the last three restores its default.  At head_dim 64 the
- * step's defaults differ from the split pass's: one subtile per tile, and 8
- * waves when the grid is at most 256 workgroups and the merging workgroup's
- * threads at 4 waves would each hold more than 8 partition rows (the 8-bit
- * step follows the same wave rule; the 8-bit passes take no other
- * setting).  Shapes beyond the
- * register budget (more than 8 subtiles in flight at head_dim 64, 4 at
- * head_dim 128) are reduced to fit.  Results do not depend on the shape
- * beyond fp32 summation order.  Not synchronised with concurrent launches (a
- * launch uses whichever value is current).  Returns PKV_OK or
- * PKV_ERR_INVALID_ARG.
+ * pkv_launch_config -- an explicit launch shape for one call of an attention
+ * pass, taken by the _ex entry points (paged_attention_decode_ex,
+ * paged_attention_decode_split_ex, paged_decode_step_ex); the calls without
+ * _ex use the defaults.  The library keeps no setting between calls.  Every
+ * field 0 means the library's default.
+ *   waves_per_group    wavefronts (64 lanes) per workgroup: 1, 2, 4 or 8;
+ *                      they share the workgroup's context range (a whole
+ *                      sequence unsplit, one partition in the split pass and
+ *                      the fused step).  Defaults: 8 unsplit, 4 split; the
+ *                      fused step takes 4, or 8 when the grid is at most 256
+ *                      workgroups and the merging workgroup's threads would
+ *                      each hold more than 8 partition rows at 4 waves.
+ *   subtiles_per_tile  16-token subtiles a wave loads per tile: 1, 2 or 4
+ *                      (defaults: 2 at head_dim 64 except the fused step's 1;
+ *                      1 at head_dim 128).
+ *   tiles_in_flight    tiles of K/V a wave keeps in flight: 2 or 4 (default 2).
+ *   grid               split pass and fused step: 0 auto (direct up to 8192
+ *                      workgroups, compact above), 1 direct (a workgroup per
+ *                      sequence, KV head and group of partitions, empty ones
+ *                      included), 2 compact (a fixed number of workgroups,
+ *                      each scanning the context lengths and looping over the
+ *                      non-empty groups; B <= 4096).  The compact grid runs
+ *                      the default shape only: a call that sets another
+ *                      shape is launched direct.
+ * Shapes beyond the register budget (more than 8 subtiles in flight at
+ * head_dim 64, 4 at head_dim 128) are reduced to fit.  Results do not
+ * depend on the shape beyond fp32 summation order.  A field outside its set
+ * gives PKV_ERR_INVALID_ARG.  NULL means every default.
  */
-int pkv_set_launch_config(int which, int waves_per_group, int subtiles_per_tile,
-                          int tiles_in_flight);
-
-/*
- * pkv_set_grid_mode -- tuning and test aid: the grid of the partitioned
- * passes (paged_attention_decode_split, paged_decode_step) with the default
- * launch shape.
- *   0  auto (default): direct when B * num_kv_heads * max_partitions is at
- *      most 8192 workgroups, compact above;
- *   1  direct: one workgroup per (sequence, KV head, partition), empty ones
- *      included;
- *   2  compact: a fixed number of workgroups, each scanning the context
- *      lengths and looping over the non-empty (sequence, KV head, partition)
- *      items (B <= 4096; larger batches stay direct).
- * Results do not depend on the mode beyond fp32 summation order; the
- * documented outputs (including -inf partial_lse of empty partitions) are
- * the same.  Returns PKV_OK or PKV_ERR_INVALID_ARG.
- */
-int pkv_set_grid_mode(int mode);
+typedef struct pkv_launch_config {
+  int32_t waves_per_group;
+  int32_t subtiles_per_tile;
+  int32_t tiles_in_flight;
+  int32_t grid;
+} pkv_launch_config;
 
 /*
  * kv_cache_append -- write the K and V rows of new tokens into their slots.
@@ -189,6 +186,18 @@ int paged_attention_decode(void* out, const void* q,
                            int32_t num_blocks, int32_t max_blocks_per_seq,
                            float scale, void* stream);
 
+/* paged_attention_decode with an explicit launch shape (see
+ * pkv_launch_config; NULL = defaults). */
+int paged_attention_decode_ex(void* out, const void* q,
+                              const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables,
+                              const int32_t* context_lens,
+                              int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t max_blocks_per_seq,
+                              float scale, const pkv_launch_config* config,
+                              void* stream);
+
 /*
  * paged_attention_decode_split -- split-context pass of the flash-decoding
  * style arm (nanoserve author's post thread, Day 74).  Partition p of
@@ -222,6 +231,21 @@ int paged_attention_decode_split(float* partial_out, float* partial_lse,
                                  int32_t max_blocks_per_seq,
                                  int32_t partition_size, int32_t max_partitions,
                                  float scale, void* stream);
+
+/* paged_attention_decode_split with an explicit launch shape (see
+ * pkv_launch_config; NULL = defaults). */
+int paged_attention_decode_split_ex(float* partial_out, float* partial_lse,
+                                    const void* q,
+                                    const void* k_pool, const void* v_pool,
+                                    const int32_t* block_tables,
+                                    const int32_t* context_lens,
+                                    int32_t B, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t num_blocks,
+                                    int32_t max_blocks_per_seq,
+                                    int32_t partition_size, int32_t max_partitions,
+                                    float scale, const pkv_launch_config* config,
+                                    void* stream);
 
 /*
  * paged_decode_step -- one whole decode step in a single launch: the cache
@@ -264,9 +288,11 @@ int paged_attention_decode_split(float* partial_out, float* partial_lse,
  * counter early, the holder of the last ticket merges, and it reads the other
  * partitions' rows once none of their words is all ones (device-coherent
  * accesses; the others never wait).  It sets the rows it read back to all
- * ones and the counter back to zero.  A sequence that fits one partition is
- * written directly.  Results equal append + split pass + split_reduce up to
- * fp32 summation order.
+ * ones and the counter back to zero.  Its wait is bounded in time (20 ms): a
+ * workspace that breaks the contract above gives wrong numbers, not a
+ * stalled queue.  A sequence that fits one partition is written directly.
+ * Results equal append + split pass + split_reduce up to fp32 summation
+ * order.
  */
 int paged_decode_step(void* out, float* lse_out,
                       void* k_pool, void* v_pool,
@@ -278,6 +304,20 @@ int paged_decode_step(void* out, float* lse_out,
                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
                       int32_t max_blocks_per_seq, int32_t partition_size,
                       int32_t max_partitions, float scale, void* stream);
+
+/* paged_decode_step with an explicit launch shape (see pkv_launch_config;
+ * NULL = defaults). */
+int paged_decode_step_ex(void* out, float* lse_out,
+                         void* k_pool, void* v_pool,
+                         const void* q, const void* k_new, const void* v_new,
+                         const int64_t* slot_mapping,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         float* partial_out, float* partial_lse, int32_t* counters,
+                         int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         int32_t max_blocks_per_seq, int32_t partition_size,
+                         int32_t max_partitions, float scale,
+                         const pkv_launch_config* config, void* stream);
 
 /*
  * paged_attention_prefill -- attention of a chunk of new tokens per sequence

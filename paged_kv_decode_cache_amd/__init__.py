@@ -4,7 +4,7 @@ The computation lives in libpkv.so (hand-written HIP kernels behind a C ABI,
 ``include/pkv.h``); this package is its thin Python binding.
 """
 from ._binding import (LIB_PATH, HEADER_PATH, load_library, declared_functions,
-                       status_string, set_launch_config, set_grid_mode, kv_cache_append,
+                       status_string, LaunchConfig, kv_cache_append,
                        paged_attention_decode, paged_attention_decode_split,
                        split_reduce, max_partitions_for, paged_decode_step, StepWorkspace,
                        paged_attention_prefill, paged_attention_prefill_split,
@@ -14,7 +14,7 @@ from ._binding import (LIB_PATH, HEADER_PATH, load_library, declared_functions,
                        PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_LAUNCH)
 
 __all__ = ["LIB_PATH", "HEADER_PATH", "load_library", "declared_functions", "status_string",
-           "set_launch_config", "set_grid_mode", "kv_cache_append", "paged_attention_decode",
+           "LaunchConfig", "kv_cache_append", "paged_attention_decode",
            "paged_attention_decode_split", "split_reduce", "max_partitions_for",
            "paged_decode_step", "StepWorkspace", "paged_attention_prefill",
            "paged_attention_prefill_split",

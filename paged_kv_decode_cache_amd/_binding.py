@@ -36,17 +36,20 @@ _F = ctypes.c_float
 _SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_version": (ctypes.c_int, []),
-    "pkv_set_launch_config": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                             ctypes.c_int]),
-    "pkv_set_grid_mode": (ctypes.c_int, [ctypes.c_int]),
     "kv_cache_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "paged_attention_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                               _I, _F, _P]),
+    "paged_attention_decode_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                                 _I, _I, _F, _P, _P]),
     "paged_attention_decode_split": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I,
                                                     _I, _I, _I, _I, _I, _I, _F, _P]),
+    "paged_attention_decode_split_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I,
+                                                       _I, _I, _I, _I, _I, _I, _F, _P, _P]),
     "split_reduce": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "paged_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "paged_decode_step_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                            _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P]),
     "paged_decode_step_q8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                             _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                                             _P]),
@@ -142,19 +145,30 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, device=None
         raise ValueError(f"{name} must be contiguous")
 
 
-def set_grid_mode(mode: str):
-    """Tuning/test aid: grid of the partitioned passes: 'auto', 'direct' or
-    'compact'."""
-    _raise(load_library().pkv_set_grid_mode({"auto": 0, "direct": 1, "compact": 2}[mode]),
-           "pkv_set_grid_mode")
+class LaunchConfig(ctypes.Structure):
+    """pkv_launch_config: an explicit launch shape for one call (0 = default).
+    grid: 0 auto, 1 direct, 2 compact."""
+    _fields_ = [("waves_per_group", ctypes.c_int32), ("subtiles_per_tile", ctypes.c_int32),
+                ("tiles_in_flight", ctypes.c_int32), ("grid", ctypes.c_int32)]
 
 
-def set_launch_config(which: str, waves_per_group: int = 0, subtiles_per_tile: int = 0,
-                      tiles_in_flight: int = 0):
-    """Tuning aid: launch shape of 'decode' or 'split' (0 = library default)."""
-    idx = {"decode": 0, "split": 1}[which]
-    _raise(load_library().pkv_set_launch_config(idx, waves_per_group, subtiles_per_tile,
-                                                tiles_in_flight), "pkv_set_launch_config")
+_GRID = {"auto": 0, "direct": 1, "compact": 2}
+
+
+def _launch(launch):
+    """None, or a LaunchConfig from a dict with keys waves, subtiles, depth,
+    grid ('auto' / 'direct' / 'compact')."""
+    if launch is None:
+        return None
+    if isinstance(launch, LaunchConfig):
+        return launch
+    unknown = set(launch) - {"waves", "subtiles", "depth", "grid"}
+    if unknown:
+        raise ValueError(f"unknown launch keys {sorted(unknown)}")
+    grid = launch.get("grid", 0)
+    return LaunchConfig(int(launch.get("waves", 0)), int(launch.get("subtiles", 0)),
+                        int(launch.get("depth", 0)), _GRID[grid] if isinstance(grid, str)
+                        else int(grid))
 
 
 def kv_cache_append(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
@@ -194,8 +208,9 @@ def _attn_shapes(q, k_pool, v_pool, block_tables, context_lens):
 
 
 def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, scale,
-                           out=None, stream=None):
-    """out [B, Hq, D] fp16 = paged decode attention (one launch)."""
+                           out=None, stream=None, launch=None):
+    """out [B, Hq, D] fp16 = paged decode attention (one launch).  launch: an
+    explicit launch shape (dict: waves, subtiles, depth), else defaults."""
     dev, B, Hq, Hkv, D, bs, NB, maxb = _attn_shapes(q, k_pool, v_pool, block_tables,
                                                     context_lens)
     if out is None:
@@ -203,9 +218,14 @@ def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, scale,
     _need(out, "out", torch.float16, 3, dev)
     if out.shape != (B, Hq, D):
         raise ValueError("out must be [B, Hq, D]")
-    rc = load_library().paged_attention_decode(
-        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
-        B, Hq, Hkv, D, bs, NB, maxb, float(scale), _stream(dev, stream))
+    args = (_ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+            _ptr(context_lens), B, Hq, Hkv, D, bs, NB, maxb, float(scale))
+    cfg = _launch(launch)
+    if cfg is None:
+        rc = load_library().paged_attention_decode(*args, _stream(dev, stream))
+    else:
+        rc = load_library().paged_attention_decode_ex(*args, ctypes.byref(cfg),
+                                                      _stream(dev, stream))
     _raise(rc, "paged_attention_decode")
     return out
 
@@ -377,8 +397,9 @@ def max_partitions_for(max_blocks_per_seq: int, block_size: int, partition_size:
 
 def paged_attention_decode_split(q, k_pool, v_pool, block_tables, context_lens, scale,
                                  partition_size, max_partitions=None, partial_out=None,
-                                 partial_lse=None, stream=None):
-    """Split pass; returns (partial_out [B,Hq,P,D] fp32, partial_lse [B,Hq,P] fp32)."""
+                                 partial_lse=None, stream=None, launch=None):
+    """Split pass; returns (partial_out [B,Hq,P,D] fp32, partial_lse [B,Hq,P] fp32).
+    launch: an explicit launch shape (dict: waves, subtiles, depth, grid)."""
     dev, B, Hq, Hkv, D, bs, NB, maxb = _attn_shapes(q, k_pool, v_pool, block_tables,
                                                     context_lens)
     if max_partitions is None:
@@ -392,10 +413,15 @@ def paged_attention_decode_split(q, k_pool, v_pool, block_tables, context_lens, 
     if partial_out.shape != (B, Hq, max_partitions, D) or \
             partial_lse.shape != (B, Hq, max_partitions):
         raise ValueError("partial_out must be [B, Hq, P, D] and partial_lse [B, Hq, P]")
-    rc = load_library().paged_attention_decode_split(
-        _ptr(partial_out), _ptr(partial_lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
-        _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, bs, NB, maxb,
-        int(partition_size), int(max_partitions), float(scale), _stream(dev, stream))
+    args = (_ptr(partial_out), _ptr(partial_lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+            _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, bs, NB, maxb,
+            int(partition_size), int(max_partitions), float(scale))
+    cfg = _launch(launch)
+    if cfg is None:
+        rc = load_library().paged_attention_decode_split(*args, _stream(dev, stream))
+    else:
+        rc = load_library().paged_attention_decode_split_ex(*args, ctypes.byref(cfg),
+                                                            _stream(dev, stream))
     _raise(rc, "paged_attention_decode_split")
     return partial_out, partial_lse
 
@@ -455,9 +481,10 @@ class StepWorkspace:
 
 def paged_decode_step(q, k_pool, v_pool, block_tables, context_lens, scale, partition_size,
                       k_new=None, v_new=None, slot_mapping=None, workspace=None, out=None,
-                      lse_out=None, want_lse=False, stream=None):
+                      lse_out=None, want_lse=False, stream=None, launch=None):
     """Fused decode step: append (if slot_mapping is given) + split pass +
-    merge in one launch.  Returns out [B, Hq, D] fp16 (and lse [B, Hq])."""
+    merge in one launch.  Returns out [B, Hq, D] fp16 (and lse [B, Hq]).
+    launch: an explicit launch shape (dict: waves, subtiles, depth, grid)."""
     dev, B, Hq, Hkv, D, bs, NB, maxb = _attn_shapes(q, k_pool, v_pool, block_tables,
                                                     context_lens)
     Pm = max_partitions_for(maxb, bs, partition_size)
@@ -485,13 +512,17 @@ def paged_decode_step(q, k_pool, v_pool, block_tables, context_lens, scale, part
         lse_out = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     if lse_out is not None:
         _need(lse_out, "lse_out", torch.float32, 2, dev)
-    rc = load_library().paged_decode_step(
-        _ptr(out), _ptr(lse_out), _ptr(k_pool), _ptr(v_pool), _ptr(q),
-        _ptr(k_new) if slot_mapping is not None else None,
-        _ptr(v_new) if slot_mapping is not None else None, _ptr(slot_mapping),
-        _ptr(block_tables), _ptr(context_lens), _ptr(ws.partial_out), _ptr(ws.partial_lse),
-        _ptr(ws.counters), B, Hq, Hkv, D, bs, NB, maxb, int(partition_size), Pm, float(scale),
-        _stream(dev, stream))
+    args = (_ptr(out), _ptr(lse_out), _ptr(k_pool), _ptr(v_pool), _ptr(q),
+            _ptr(k_new) if slot_mapping is not None else None,
+            _ptr(v_new) if slot_mapping is not None else None, _ptr(slot_mapping),
+            _ptr(block_tables), _ptr(context_lens), _ptr(ws.partial_out), _ptr(ws.partial_lse),
+            _ptr(ws.counters), B, Hq, Hkv, D, bs, NB, maxb, int(partition_size), Pm,
+            float(scale))
+    cfg = _launch(launch)
+    if cfg is None:
+        rc = load_library().paged_decode_step(*args, _stream(dev, stream))
+    else:
+        rc = load_library().paged_decode_step_ex(*args, ctypes.byref(cfg), _stream(dev, stream))
     _raise(rc, "paged_decode_step")
     return (out, lse_out) if lse_out is not None else out
 

@@ -3,7 +3,6 @@
 // synchronisation, no device reads on the host.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -27,35 +26,39 @@ bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
 bool block_size_ok(int32_t bs) { return bs >= 16 && bs <= 256 && bs % 16 == 0; }
 
 // Launch shape: waves per workgroup, 16-token subtiles per tile, tiles in
-// flight per wave; 0 means "library default".  Settable for tuning through
-// pkv_set_launch_config.
-std::atomic<int> g_cfg_waves[2] = {{0}, {0}};
-std::atomic<int> g_cfg_subtiles[2] = {{0}, {0}};
-std::atomic<int> g_cfg_depth[2] = {{0}, {0}};
-
+// flight per wave.  Defaults (measured on MI355X): the unsplit pass has one
+// workgroup per (sequence, KV head) and uses 8 waves; the partitioned passes
+// use 4 (one partition each).  At head_dim 64 the split pass loads 2
+// subtiles per tile and the fused step 1 (its last tile's compute is exposed
+// before the hand-off).  A call may override any of them through a
+// pkv_launch_config (the _ex entry points); nothing is kept between calls.
 struct Shape {
   int waves, subtiles, depth;
 };
 
-Shape pick_default_shape(int which, int head_dim) {
+Shape default_shape(int mode, int head_dim) {
   Shape s;
-  // Defaults (measured on MI355X): the split pass runs one partition per
-  // workgroup with 4 waves; the unsplit pass has one workgroup per
-  // (sequence, KV head) and uses 8.
-  s.waves = which == 0 ? 8 : 4;
-  s.subtiles = head_dim == 64 ? 2 : 1;
+  s.waves = mode == 0 ? 8 : 4;
+  s.subtiles = head_dim == 64 && mode != 2 ? 2 : 1;
   s.depth = 2;
   return s;
 }
 
-Shape pick_shape(int which, int head_dim) {
-  Shape s = pick_default_shape(which, head_dim);
-  const int w = g_cfg_waves[which].load(std::memory_order_relaxed);
-  const int t = g_cfg_subtiles[which].load(std::memory_order_relaxed);
-  const int d = g_cfg_depth[which].load(std::memory_order_relaxed);
-  if (w) s.waves = w;
-  if (t) s.subtiles = t;
-  if (d) s.depth = d;
+bool config_ok(const pkv_launch_config* c) {
+  if (!c) return true;
+  const int w = c->waves_per_group, t = c->subtiles_per_tile, d = c->tiles_in_flight;
+  return (w == 0 || w == 1 || w == 2 || w == 4 || w == 8) &&
+         (t == 0 || t == 1 || t == 2 || t == 4) && (d == 0 || d == 2 || d == 4) &&
+         c->grid >= 0 && c->grid <= 2;
+}
+
+Shape pick_shape(int mode, int head_dim, const pkv_launch_config* c) {
+  Shape s = default_shape(mode, head_dim);
+  if (c) {
+    if (c->waves_per_group) s.waves = c->waves_per_group;
+    if (c->subtiles_per_tile) s.subtiles = c->subtiles_per_tile;
+    if (c->tiles_in_flight) s.depth = c->tiles_in_flight;
+  }
   // register budget: at most 8 subtiles of K/V in flight per wave at
   // head_dim 64 and 4 at head_dim 128
   const int max_inflight = head_dim == 64 ? 8 : 4;
@@ -65,42 +68,58 @@ Shape pick_shape(int which, int head_dim) {
   return s;
 }
 
-// MODE: 0 unsplit decode, 1 split pass, 2 fused decode step.
+// MODE: 0 unsplit decode, 1 split pass, 2 fused decode step.  The grid of
+// the partitioned passes is (Hkv, max_partitions, B); of the unsplit pass
+// (B * Hkv).
+dim3 attn_grid(const AttnParams& p, int mode) {
+  if (mode == 0) return dim3((unsigned)(p.B * p.Hkv));
+  return dim3((unsigned)p.Hkv, (unsigned)p.max_partitions, (unsigned)p.B);
+}
+
 template <int D, int NS, int NW, int DEPTH, int MODE>
-void launch_attn_inst(const AttnParams& p, int64_t grid, hipStream_t st) {
+void launch_attn_inst(const AttnParams& p, hipStream_t st) {
   // Groups of up to 8 query heads put the fp16 remainder of P in the spare
   // MFMA columns (one PV MFMA per 16 dims instead of two).
+  const dim3 grid = attn_grid(p, MODE);
   if (p.G <= 8)
-    hipLaunchKernelGGL((pkv::attn_kernel<D, NS, NW, DEPTH, MODE, true>), dim3((unsigned)grid),
-                       dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((pkv::attn_kernel<D, NS, NW, DEPTH, MODE, true>), grid, dim3(NW * 64), 0,
+                       st, p);
   else
-    hipLaunchKernelGGL((pkv::attn_kernel<D, NS, NW, DEPTH, MODE, false>),
-                       dim3((unsigned)grid), dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((pkv::attn_kernel<D, NS, NW, DEPTH, MODE, false>), grid, dim3(NW * 64),
+                       0, st, p);
 }
 
 template <int D, int NS, int DEPTH, int MODE>
-void launch_attn_nw(const AttnParams& p, int64_t grid, int waves, hipStream_t st) {
+void launch_attn_nw(const AttnParams& p, int waves, hipStream_t st) {
   switch (waves) {
-    case 1: launch_attn_inst<D, NS, 1, DEPTH, MODE>(p, grid, st); break;
-    case 2: launch_attn_inst<D, NS, 2, DEPTH, MODE>(p, grid, st); break;
-    case 4: launch_attn_inst<D, NS, 4, DEPTH, MODE>(p, grid, st); break;
-    default: launch_attn_inst<D, NS, 8, DEPTH, MODE>(p, grid, st); break;
+    case 1: launch_attn_inst<D, NS, 1, DEPTH, MODE>(p, st); break;
+    case 2: launch_attn_inst<D, NS, 2, DEPTH, MODE>(p, st); break;
+    case 4: launch_attn_inst<D, NS, 4, DEPTH, MODE>(p, st); break;
+    default: launch_attn_inst<D, NS, 8, DEPTH, MODE>(p, st); break;
   }
 }
 
 template <int D, int MODE>
-void launch_attn_shape(const AttnParams& p, int64_t grid, Shape s, hipStream_t st) {
+void launch_attn_shape(const AttnParams& p, Shape s, hipStream_t st) {
   const int w = s.waves;
   if (s.depth == 4) {
-    if (s.subtiles == 1) launch_attn_nw<D, 1, 4, MODE>(p, grid, w, st);
-    else if constexpr (D == 64) launch_attn_nw<D, 2, 4, MODE>(p, grid, w, st);
-    else launch_attn_nw<D, 1, 4, MODE>(p, grid, w, st);
+    if (s.subtiles == 1) launch_attn_nw<D, 1, 4, MODE>(p, w, st);
+    else if constexpr (D == 64) launch_attn_nw<D, 2, 4, MODE>(p, w, st);
+    else launch_attn_nw<D, 1, 4, MODE>(p, w, st);
   } else {
-    if (s.subtiles == 1) launch_attn_nw<D, 1, 2, MODE>(p, grid, w, st);
-    else if (s.subtiles == 2) launch_attn_nw<D, 2, 2, MODE>(p, grid, w, st);
-    else if constexpr (D == 64) launch_attn_nw<D, 4, 2, MODE>(p, grid, w, st);
-    else launch_attn_nw<D, 2, 2, MODE>(p, grid, w, st);
+    if (s.subtiles == 1) launch_attn_nw<D, 1, 2, MODE>(p, w, st);
+    else if (s.subtiles == 2) launch_attn_nw<D, 2, 2, MODE>(p, w, st);
+    else if constexpr (D == 64) launch_attn_nw<D, 4, 2, MODE>(p, w, st);
+    else launch_attn_nw<D, 2, 2, MODE>(p, w, st);
   }
+}
+
+// log2(v) when v is a positive power of two, else -1.
+int log2_or_neg(int64_t v) {
+  if (v <= 0 || (v & (v - 1))) return -1;
+  int sh = 0;
+  while ((int64_t(1) << sh) < v) ++sh;
+  return sh;
 }
 
 int spb_shift_of(int32_t block_size) {
@@ -111,20 +130,20 @@ int spb_shift_of(int32_t block_size) {
   return sh;
 }
 
-// Grid of the partitioned passes: direct (one workgroup per sequence x KV
-// head x partition) or compact (a fixed number of workgroups looping over the
-// non-empty items; attn_compact_kernel).  Auto picks compact when the direct
-// grid would exceed kCompactAbove workgroups (ragged batches with a wide
-// table are mostly empty partitions, each a workgroup dispatch); settable for
-// tests and tuning through pkv_set_grid_mode.
+// Grid of the partitioned passes: direct (a workgroup per sequence x KV head
+// x partition) or compact (a fixed number of workgroups looping over the
+// non-empty partitions; attn_compact_kernel).  Auto picks compact when the
+// direct grid would exceed kCompactAbove workgroups (ragged batches with a
+// wide table are mostly empty partitions, each a workgroup dispatch), or
+// when a dimension exceeds the direct grid's limits.  The compact kernel is built for the default shape only; a call
+// with another shape stays direct.
 constexpr int64_t kCompactAbove = 8192;
 constexpr int kCompactGroups = 2048;
-std::atomic<int> g_grid_mode{0};  // 0 auto, 1 direct, 2 compact
+constexpr int64_t kMaxGridYZ = 65535;
 
-template <int D, int MODE>
-void launch_compact(const AttnParams& p, int64_t grid, hipStream_t st) {
-  constexpr int NS = D == 64 ? 2 : 1;
-  const unsigned g = (unsigned)(grid < kCompactGroups ? grid : kCompactGroups);
+template <int D, int NS, int MODE>
+void launch_compact(const AttnParams& p, int64_t wgs, hipStream_t st) {
+  const unsigned g = (unsigned)(wgs < kCompactGroups ? wgs : kCompactGroups);
   if (p.G <= 8)
     hipLaunchKernelGGL((pkv::attn_compact_kernel<D, NS, 4, 2, MODE, true>), dim3(g), dim3(256),
                        0, st, p);
@@ -133,20 +152,14 @@ void launch_compact(const AttnParams& p, int64_t grid, hipStream_t st) {
                        0, st, p);
 }
 
-// The fused step's default tile at head_dim 64 is one subtile, not the split
-// pass's two: its last tile's compute is exposed before the hand-off, and one
-// subtile measured 1-2% faster at B=32 x 4096, B=8 x 4096, B=32 x 2048 and
-// B=128 x 4096 (the split pass alone is not faster with it).
-// With many partitions per (sequence, KV head) and a grid of at most one
-// workgroup per CU, the merging workgroup's walk over the partials is the
-// tail.  When its threads at 4 waves hold more partition rows than one batch
-// of loads (kMergeRowsInFlight), 8 waves (twice the merge threads) shorten
-// it: at head_dim 64, B=1 x 32768 P=512 13.9 vs 16.3 us, B=1 x 131072
-// P=1024 25.3 vs 28.6 us (best P each), B=4 x 32768 P=1024 19.6 vs 20.2 us.
-// With one batch either way 8 waves only add cost (B=1 x 4096 at 16
-// partitions: 8.75 vs 8.54 us), and with more workgroups than CUs 4 waves
-// stay faster (B=4 x 32768 P=512: 24.4 vs 28.9 us).  Explicit
-// pkv_set_launch_config values apply as given.
+// The fused steps (fp16 and 8-bit) take 8 waves with many partitions per
+// (sequence, KV head) and a grid of at most one workgroup per CU: the
+// merging workgroup's walk over the partials is then the tail, and 8 waves
+// (twice the merge threads) shorten it when its threads at 4 waves would
+// hold more partition rows than one batch of loads (measured on the fp16
+// step at head_dim 64: B=1 x 32768 P=512 13.9 vs 16.3 us, B=1 x 131072
+// P=1024 25.3 vs 28.6 us; with one batch either way, or with more
+// workgroups than CUs, 4 waves stay faster).
 constexpr int64_t kStepWideMergeMaxGrid = 256;
 bool step_wide_merge(int head_dim, int64_t grid, int max_partitions, int group) {
   if (head_dim != 64 || grid > kStepWideMergeMaxGrid) return false;
@@ -154,37 +167,39 @@ bool step_wide_merge(int head_dim, int64_t grid, int max_partitions, int group) 
   const int sets4 = per_set <= 4 * 64 ? 4 * 64 / per_set : 1;
   return (max_partitions + sets4 - 1) / sets4 > pkv::kMergeRowsInFlight;
 }
-Shape step_default(Shape s, int head_dim, int64_t grid, int max_partitions, int group) {
-  if (head_dim == 64 && g_cfg_subtiles[1].load(std::memory_order_relaxed) == 0) s.subtiles = 1;
-  if (g_cfg_waves[1].load(std::memory_order_relaxed) == 0 &&
-      step_wide_merge(head_dim, grid, max_partitions, group))
-    s.waves = 8;
-  return s;
-}
 
 template <int MODE>
-int launch_attn(const AttnParams& p, int head_dim, int64_t grid, hipStream_t st) {
-  Shape s = pick_shape(MODE == 0 ? 0 : 1, head_dim);
-  if constexpr (MODE == 2) s = step_default(s, head_dim, grid, p.max_partitions, p.G);
+int launch_attn(const AttnParams& p, int head_dim, const pkv_launch_config* cfg,
+                hipStream_t st) {
+  Shape s = pick_shape(MODE, head_dim, cfg);
   if constexpr (MODE >= 1) {
-    Shape d = pick_default_shape(1, head_dim);
-    if constexpr (MODE == 2) d = step_default(d, head_dim, grid, p.max_partitions, p.G);
-    const int mode = g_grid_mode.load(std::memory_order_relaxed);
+    Shape d = default_shape(MODE, head_dim);
+    if constexpr (MODE == 2) {
+      const int64_t grid = (int64_t)p.B * p.Hkv * p.max_partitions;
+      if (step_wide_merge(head_dim, grid, p.max_partitions, p.G)) {
+        d.waves = 8;
+        if (!cfg || cfg->waves_per_group == 0) s.waves = 8;
+      }
+    }
+    const int64_t wgs = (int64_t)p.B * p.Hkv * p.max_partitions;
+    const int mode = cfg ? cfg->grid : 0;
     const bool same_shape =
         s.waves == d.waves && s.subtiles == d.subtiles && s.depth == d.depth;
+    const bool direct_fits = p.max_partitions <= kMaxGridYZ && p.B <= kMaxGridYZ;
     if (p.B <= pkv::kCompactMaxB && same_shape &&
-        (mode == 2 || (mode == 0 && grid > kCompactAbove))) {
+        (mode == 2 || (mode == 0 && wgs > kCompactAbove) || !direct_fits)) {
       if (head_dim == 64)
-        launch_compact<64, MODE>(p, grid, st);
+        launch_compact<64, MODE == 2 ? 1 : 2, MODE>(p, wgs, st);
       else
-        launch_compact<128, MODE>(p, grid, st);
+        launch_compact<128, 1, MODE>(p, wgs, st);
       return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
     }
+    if (!direct_fits) return PKV_ERR_UNSUPPORTED;
   }
   if (head_dim == 64)
-    launch_attn_shape<64, MODE>(p, grid, s, st);
+    launch_attn_shape<64, MODE>(p, s, st);
   else
-    launch_attn_shape<128, MODE>(p, grid, s, st);
+    launch_attn_shape<128, MODE>(p, s, st);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
@@ -284,6 +299,8 @@ int fill_q8(pkv::Q8Params& p, const void* q, const void* k_codes, const void* v_
   p.a.num_blocks = num_blocks;
   p.a.max_blocks = max_blocks_per_seq;
   p.a.spb_shift = spb_shift_of(block_size);
+  p.a.bs_shift = log2_or_neg(block_size);
+  p.a.part_shift = log2_or_neg(p.a.partition_size);
   p.a.scale_log2 = scale * pkv::kLog2e;
   p.k_codes = static_cast<const int8_t*>(k_codes);
   p.v_codes = static_cast<const int8_t*>(v_codes);
@@ -308,29 +325,6 @@ const char* pkv_status_string(int status) {
 }
 
 int pkv_version(void) { return kVersion; }
-
-int pkv_set_grid_mode(int mode) {
-  if (mode < 0 || mode > 2) return PKV_ERR_INVALID_ARG;
-  g_grid_mode.store(mode, std::memory_order_relaxed);
-  return PKV_OK;
-}
-
-int pkv_set_launch_config(int which, int waves_per_group, int subtiles_per_tile,
-                          int tiles_in_flight) {
-  if (which != 0 && which != 1) return PKV_ERR_INVALID_ARG;
-  if (waves_per_group != 0 && waves_per_group != 1 && waves_per_group != 2 &&
-      waves_per_group != 4 && waves_per_group != 8)
-    return PKV_ERR_INVALID_ARG;
-  if (subtiles_per_tile != 0 && subtiles_per_tile != 1 && subtiles_per_tile != 2 &&
-      subtiles_per_tile != 4)
-    return PKV_ERR_INVALID_ARG;
-  if (tiles_in_flight != 0 && tiles_in_flight != 2 && tiles_in_flight != 4)
-    return PKV_ERR_INVALID_ARG;
-  g_cfg_waves[which].store(waves_per_group, std::memory_order_relaxed);
-  g_cfg_subtiles[which].store(subtiles_per_tile, std::memory_order_relaxed);
-  g_cfg_depth[which].store(tiles_in_flight, std::memory_order_relaxed);
-  return PKV_OK;
-}
 
 int kv_cache_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                     const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
@@ -369,6 +363,18 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                            float scale, void* stream) {
+  return paged_attention_decode_ex(out, q, k_pool, v_pool, block_tables, context_lens, B,
+                                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                   max_blocks_per_seq, scale, nullptr, stream);
+}
+
+int paged_attention_decode_ex(void* out, const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, float scale,
+                              const pkv_launch_config* config, void* stream) {
+  if (!config_ok(config)) return PKV_ERR_INVALID_ARG;
   int rc = check_attn_common(q, k_pool, v_pool, block_tables, context_lens, B, num_q_heads,
                              num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                              scale);
@@ -395,8 +401,10 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
   p.partition_size = max_blocks_per_seq * block_size;
   p.max_partitions = 1;
   p.spb_shift = spb_shift_of(block_size);
+  p.bs_shift = log2_or_neg(block_size);
+  p.part_shift = log2_or_neg(p.partition_size);
   p.scale_log2 = scale * pkv::kLog2e;
-  return launch_attn<0>(p, head_dim, grid, static_cast<hipStream_t>(stream));
+  return launch_attn<0>(p, head_dim, config, static_cast<hipStream_t>(stream));
 }
 
 int paged_attention_decode_split(float* partial_out, float* partial_lse, const void* q,
@@ -406,6 +414,22 @@ int paged_attention_decode_split(float* partial_out, float* partial_lse, const v
                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                  int32_t max_blocks_per_seq, int32_t partition_size,
                                  int32_t max_partitions, float scale, void* stream) {
+  return paged_attention_decode_split_ex(partial_out, partial_lse, q, k_pool, v_pool,
+                                         block_tables, context_lens, B, num_q_heads,
+                                         num_kv_heads, head_dim, block_size, num_blocks,
+                                         max_blocks_per_seq, partition_size, max_partitions,
+                                         scale, nullptr, stream);
+}
+
+int paged_attention_decode_split_ex(float* partial_out, float* partial_lse, const void* q,
+                                    const void* k_pool, const void* v_pool,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    int32_t max_blocks_per_seq, int32_t partition_size,
+                                    int32_t max_partitions, float scale,
+                                    const pkv_launch_config* config, void* stream) {
+  if (!config_ok(config)) return PKV_ERR_INVALID_ARG;
   int rc = check_attn_common(q, k_pool, v_pool, block_tables, context_lens, B, num_q_heads,
                              num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                              scale);
@@ -439,8 +463,10 @@ int paged_attention_decode_split(float* partial_out, float* partial_lse, const v
   p.partition_size = partition_size;
   p.max_partitions = max_partitions;
   p.spb_shift = spb_shift_of(block_size);
+  p.bs_shift = log2_or_neg(block_size);
+  p.part_shift = log2_or_neg(p.partition_size);
   p.scale_log2 = scale * pkv::kLog2e;
-  return launch_attn<1>(p, head_dim, grid, static_cast<hipStream_t>(stream));
+  return launch_attn<1>(p, head_dim, config, static_cast<hipStream_t>(stream));
 }
 
 int paged_decode_step(void* out, float* lse_out, void* k_pool, void* v_pool, const void* q,
@@ -451,6 +477,22 @@ int paged_decode_step(void* out, float* lse_out, void* k_pool, void* v_pool, con
                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                       int32_t partition_size, int32_t max_partitions, float scale,
                       void* stream) {
+  return paged_decode_step_ex(out, lse_out, k_pool, v_pool, q, k_new, v_new, slot_mapping,
+                              block_tables, context_lens, partial_out, partial_lse, counters, B,
+                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                              max_blocks_per_seq, partition_size, max_partitions, scale,
+                              nullptr, stream);
+}
+
+int paged_decode_step_ex(void* out, float* lse_out, void* k_pool, void* v_pool, const void* q,
+                         const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         float* partial_out, float* partial_lse, int32_t* counters, int32_t B,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                         int32_t partition_size, int32_t max_partitions, float scale,
+                         const pkv_launch_config* config, void* stream) {
+  if (!config_ok(config)) return PKV_ERR_INVALID_ARG;
   int rc = check_attn_common(q, k_pool, v_pool, block_tables, context_lens, B, num_q_heads,
                              num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                              scale);
@@ -503,8 +545,10 @@ int paged_decode_step(void* out, float* lse_out, void* k_pool, void* v_pool, con
   p.partition_size = partition_size;
   p.max_partitions = max_partitions;
   p.spb_shift = spb_shift_of(block_size);
+  p.bs_shift = log2_or_neg(block_size);
+  p.part_shift = log2_or_neg(p.partition_size);
   p.scale_log2 = scale * pkv::kLog2e;
-  return launch_attn<2>(p, head_dim, grid, static_cast<hipStream_t>(stream));
+  return launch_attn<2>(p, head_dim, config, static_cast<hipStream_t>(stream));
 }
 
 int paged_attention_prefill(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -541,6 +585,8 @@ int paged_attention_prefill(void* out, const void* q, const void* k_pool, const 
   p.a.num_blocks = num_blocks;
   p.a.max_blocks = max_blocks_per_seq;
   p.a.spb_shift = spb_shift_of(block_size);
+  p.a.bs_shift = log2_or_neg(block_size);
+  p.a.part_shift = log2_or_neg(p.a.partition_size);
   p.a.scale_log2 = scale * pkv::kLog2e;
   p.query_start = query_start;
   p.max_q = max_query_len;
@@ -597,6 +643,8 @@ int paged_attention_prefill_split(float* partial_out, float* partial_lse,
   p.a.partition_size = partition_size;
   p.a.max_partitions = max_partitions;
   p.a.spb_shift = spb_shift_of(block_size);
+  p.a.bs_shift = log2_or_neg(block_size);
+  p.a.part_shift = log2_or_neg(p.a.partition_size);
   p.a.scale_log2 = scale * pkv::kLog2e;
   p.query_start = query_start;
   p.max_q = max_query_len;
@@ -689,6 +737,7 @@ int paged_attention_decode_split_q8(float* partial_out, float* partial_lse, cons
   p.a.partial_out = partial_out;
   p.a.partial_lse = partial_lse;
   p.a.partition_size = partition_size;
+  p.a.part_shift = log2_or_neg(partition_size);
   p.a.max_partitions = max_partitions;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return head_dim == 64 ? launch_q8<64, 1>(p, grid, st) : launch_q8<128, 1>(p, grid, st);
@@ -736,6 +785,7 @@ int paged_decode_step_q8(void* out, float* lse_out, void* k_codes, void* v_codes
   p.a.counters = counters;
   p.a.B = B;
   p.a.partition_size = partition_size;
+  p.a.part_shift = log2_or_neg(partition_size);
   p.a.max_partitions = max_partitions;
   p.a.k_new = static_cast<const pkv::f16*>(k_new);
   p.a.v_new = static_cast<const pkv::f16*>(v_new);

@@ -66,6 +66,8 @@ struct AttnParams {
   int32_t block_size, num_blocks, max_blocks;
   int32_t partition_size, max_partitions;
   int32_t spb_shift;    // log2(block_size / 16) when a power of two, else -1
+  int32_t part_shift;   // log2(partition_size) when a power of two, else -1
+  int32_t bs_shift;     // log2(block_size) when a power of two, else -1
   float scale_log2;     // softmax scale * log2(e)
   // fused decode step only
   f16* k_pool_w;        // the pools, writable (the step's append)
@@ -110,6 +112,25 @@ __device__ __forceinline__ f32x4 zero4f() {
 #pragma unroll
   for (int i = 0; i < 4; ++i) z[i] = 0.0f;
   return z;
+}
+
+// x / d and x % d for x >= 0, with a shift when d is a power of two
+// (sh = log2 d, else -1).
+__device__ __forceinline__ int div_sh(int x, int d, int sh) { return sh >= 0 ? x >> sh : x / d; }
+__device__ __forceinline__ int mod_sh(int x, int d, int sh) {
+  return sh >= 0 ? x & ((1 << sh) - 1) : x % d;
+}
+
+// The value of lane l ^ 8 within each 16-lane row (a DPP row rotation by 8:
+// a VALU move, no LDS round trip).
+__device__ __forceinline__ float row_xor8(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+}
+
+// 1 / x for a positive normal x (v_rcp_f32, within 1 ulp); 0 for x <= 0.
+__device__ __forceinline__ float recip_or_zero(float x) {
+  return x > 0.0f ? __builtin_amdgcn_rcpf(x) : 0.0f;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) {
@@ -302,7 +323,7 @@ template <int D, int NS>
 struct LineSmem {
   static constexpr int kSubBytes = 16 * D * 2;           // one subtile of K (or V)
   static constexpr int kStageBytes = 2 * NS * kSubBytes;  // K subtiles, then V subtiles
-  static constexpr int kMergeBytes = ((D / 4) * 64 + 32) * 4;
+  static constexpr int kMergeBytes = ((D / 4) * 64 + 32) * 4;  // the waves' merge
   static constexpr int kWaveBytes = kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes;
 };
 
@@ -584,7 +605,12 @@ __device__ __forceinline__ void merge_waves_impl(const SoftmaxState<D>& st, floa
 
 constexpr int kMergeSlots = 512;  // >= 16 heads x 128/4 dims
 constexpr int kMergeRowsInFlight = 8;  // the merge's largest batch of partition rows per thread
-constexpr int kSpinLimit = 1 << 20;
+// The merger's wait for the other workgroups' rows is bounded in time: a
+// workspace that breaks its contract (rows reset under a running writer, a
+// stale counter) costs at most this long and gives wrong numbers, never a
+// stalled queue.  Legitimate waits end within microseconds (every writer has
+// started and waits on nothing).  s_memrealtime counts at 100 MHz: 20 ms.
+constexpr long long kSpinTicks = 2000000;
 
 // Streaming LSE merge of one thread's rows (partitions grp, grp + ngroups, ...
 // of head hh, dims 4cc..4cc+3) into (M, L, acc), BATCH rows in flight.
@@ -620,7 +646,9 @@ __device__ __forceinline__ void merge_rows(__amdgpu_buffer_rsrc_t po_rs,
               is_written(x[j][3]) && is_written(l[j]);
       all_ok = all_ok && ok[j];
     }
-    for (int spin = 0; spin < kSpinLimit && !__all(all_ok); ++spin) {
+    const long long t_spin = __all(all_ok) ? 0 : (long long)__builtin_amdgcn_s_memrealtime();
+    while (!__all(all_ok) &&
+           (long long)__builtin_amdgcn_s_memrealtime() - t_spin < kSpinTicks) {
       __builtin_amdgcn_s_sleep(2);
       asm volatile("" ::: "memory");
       all_ok = true;
@@ -696,6 +724,19 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
     else
       merge_rows<D, kMergeRowsInFlight>(po_rs, pl_rs, Pm, np, p_own, grp, ngroups, hh, cc, own_x,
                                         own_l, M, L, acc);
+    // Back to "not written" for the next launch: this thread's data words as
+    // soon as its last slot's rows are read (no load of this call follows
+    // them then, and loads and stores count down one in-order counter); the
+    // lse words, which every thread of a head reads, after the barrier below.
+    if (slot + NT >= nslots) {
+      for (int s2 = t; s2 <= slot; s2 += NT) {
+        const int g2 = s2 / per_group;
+        const int h2 = (s2 % per_group) / TPR;
+        const int c2 = (s2 % per_group) % TPR;
+        for (int q = g2; q < np; q += ngroups)
+          if (q != p_own) store_coherent4(po_rs, ((h2 * Pm + q) * D + 4 * c2) * 4, unwritten4);
+      }
+    }
     float* r = msm + 6 * slot;
     r[0] = M;
     r[1] = L;
@@ -705,6 +746,11 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
     r[5] = acc[3];
   }
   __syncthreads();
+  for (int i = t; i < G * np; i += NT) {
+    const int q = i % np;
+    if (q != p_own)
+      store_coherent1(pl_rs, ((i / np) * Pm + q) * 4, __builtin_bit_cast(float, kUnwritten));
+  }
   for (int hc = t; hc < per_group; hc += NT) {
     float M = -INFINITY;
     for (int gi = 0; gi < ngroups; ++gi) M = fmaxf(M, msm[6 * (gi * per_group + hc)]);
@@ -722,30 +768,13 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
     }
     const int h = kvh * a.G + hc / TPR;
     const int cc = hc % TPR;
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const float inv = recip_or_zero(L);
     f16x4 o;
 #pragma unroll
     for (int v = 0; v < 4; ++v) o[v] = (f16)(acc[v] * inv);
     *reinterpret_cast<f16x4*>(a.out + ((size_t)b * a.Hq + h) * D + 4 * cc) = o;
     if (a.lse_out != nullptr && cc == 0)
       a.lse_out[(size_t)b * a.Hq + h] = L > 0.0f ? M + logf(L) : -INFINITY;
-  }
-  // Back to "not written" for the next launch, last: a store issued between
-  // two batches of loads holds up the next batch (loads and stores count down
-  // one in-order counter), and one pending before the combine above made it
-  // wait for the write-through of every reset.  Data words: each thread's own
-  // rows; lse words: read by every thread of a head, so after the barrier.
-  for (int slot = t; slot < nslots; slot += NT) {
-    const int grp = slot / per_group;
-    const int hh = (slot % per_group) / TPR;
-    const int cc = (slot % per_group) % TPR;
-    for (int q = grp; q < np; q += ngroups)
-      if (q != p_own) store_coherent4(po_rs, ((hh * Pm + q) * D + 4 * cc) * 4, unwritten4);
-  }
-  for (int i = t; i < G * np; i += NT) {
-    const int q = i % np;
-    if (q != p_own)
-      store_coherent1(pl_rs, ((i / np) * Pm + q) * 4, __builtin_bit_cast(float, kUnwritten));
   }
 }
 
@@ -842,7 +871,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
     t_end = min(ctx, t_begin + a.partition_size);
   }
   const int sub_end = (t_end + 15) >> 4;
-  const int n_parts = STEP ? (ctx + a.partition_size - 1) / a.partition_size : 1;
+  const int n_parts =
+      STEP ? div_sh(ctx + a.partition_size - 1, a.partition_size, a.part_shift) : 1;
 
   // Fused step: the workgroup owning position ctx-1 (partition 0 if ctx = 0)
   // writes the new token's K/V row of its head into the pool (at the end of
@@ -850,8 +880,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   // the pool when the slot is the position's slot in the block table (so the
   // launch never reads its own write).  That block id comes with the tile
   // that holds the position; nothing here waits for a load after the length.
-  const bool owns_new =
-      STEP && a.slot_mapping != nullptr && p == (ctx > 0 ? (ctx - 1) / a.partition_size : 0);
+  const bool owns_new = STEP && a.slot_mapping != nullptr &&
+                        p == (ctx > 0 ? div_sh(ctx - 1, a.partition_size, a.part_shift) : 0);
   const int64_t slot = owns_new ? slot_in : -1;
   int s_new = -1, tok_new = -1, new_off = 0;
   f16x8 kn[KC], vn[KC];
@@ -859,7 +889,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   if (owns_new) {
     if (ctx > 0) {
       const int pos = ctx - 1;
-      new_off = pos % a.block_size;
+      new_off = mod_sh(pos, a.block_size, a.bs_shift);
       s_new = pos >> 4;
       tok_new = pos & 15;
     }
@@ -949,11 +979,12 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) st.o[db][v] += __shfl_xor(st.o[db][v], 8);
-    st.lsum[0] += __shfl_xor(st.lsum[0], 8);
+      for (int v = 0; v < 4; ++v) st.o[db][v] += row_xor8(st.o[db][v]);
+    st.lsum[0] += row_xor8(st.lsum[0]);
   }
-  // Weight sum of this lane's column: row 0, held by the quad-0 lane.
-  const float l_tot = __shfl(st.lsum[0], g);
+  // Weight sum of this lane's column: row 0, held by the quad-0 lane (the
+  // wave merge reads it from those lanes only).
+  const float l_tot = NW == 1 ? __shfl(st.lsum[0], g) : st.lsum[0];
 
   // Fused step: publish whether this workgroup merges (its ticket is the
   // pair's last), before the barriers of the wave merge; the merger resets
@@ -984,7 +1015,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   auto emit = [&](int db, f32x4 acc, float L, float M) {
     if (!emits) return;
     const int h = kvh * a.G + head_col;
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const float inv = recip_or_zero(L);
     const int d0 = 16 * db + 4 * quad;
     if (SPLIT && !(STEP && n_parts <= 1)) {
       f32x4 r;
@@ -1036,17 +1067,16 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   merge_step_partitions<D, NW>(a, b, kvh, n_parts, p, own, msm);
 }
 
-// Direct grid: workgroup -> item from its index (B x Hkv x partitions).
+// Direct grid.  Unsplit decode: one workgroup per (sequence, KV head),
+// blockIdx.x = b * Hkv + kvh.  Partitioned passes: a 3-D grid (KV head,
+// partition, sequence), so the item needs no division.
 template <int D, int NS, int NW, int DEPTH, int MODE, bool DUAL>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnParams a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[NW * LineSmem<D, NS>::kWaveBytes];
-  const int kvh = blockIdx.x % a.Hkv;
-  const int rest = blockIdx.x / a.Hkv;
-  if (MODE >= 1)
-    attn_item<D, NS, NW, DEPTH, MODE, DUAL>(a, rest / a.max_partitions, kvh,
-                                            rest % a.max_partitions, smem);
+  if constexpr (MODE >= 1)
+    attn_item<D, NS, NW, DEPTH, MODE, DUAL>(a, blockIdx.z, blockIdx.x, blockIdx.y, smem);
   else
-    attn_item<D, NS, NW, DEPTH, MODE, DUAL>(a, rest, kvh, 0, smem);
+    attn_item<D, NS, NW, DEPTH, MODE, DUAL>(a, blockIdx.x / a.Hkv, blockIdx.x % a.Hkv, 0, smem);
 }
 
 // Compact grid for the split pass and the fused step when most of the

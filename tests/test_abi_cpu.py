@@ -20,6 +20,13 @@ C16 = 0x30000
 D16 = 0x40000
 E16 = 0x50000
 F16 = 0x60000
+G16 = 0x70000
+H16 = 0x80000
+I16 = 0x90000
+J16 = 0xA0000
+K16 = 0xB0000
+L16 = 0xC0000
+M16 = 0xD0000
 
 
 def test_library_exports_every_declared_symbol():
@@ -43,22 +50,27 @@ def test_status_strings_and_version():
     assert lib.pkv_version() >= 100
 
 
+@host_only
 def test_launch_config_validation():
+    """A launch shape outside its set is an argument error, decided before
+    any HIP call (so it is checkable here); NULL and in-set shapes pass."""
     lib = pkv.load_library()
-    assert lib.pkv_set_launch_config(2, 4, 4, 2) == -1
-    assert lib.pkv_set_launch_config(0, 3, 4, 2) == -1
-    assert lib.pkv_set_launch_config(1, 4, 3, 2) == -1
-    assert lib.pkv_set_launch_config(1, 4, 2, 3) == -1
-    assert lib.pkv_set_launch_config(0, 0, 0, 0) == 0
-    assert lib.pkv_set_launch_config(1, 0, 0, 0) == 0
-
-
-def test_grid_mode_validation():
-    lib = pkv.load_library()
-    assert lib.pkv_set_grid_mode(3) == -1
-    assert lib.pkv_set_grid_mode(-1) == -1
-    for mode in (2, 1, 0):
-        assert lib.pkv_set_grid_mode(mode) == 0
+    args = (A16, B16, C16, D16, E16, F16, 2, 14, 2, 64, 16, 10, 4, 0.125)
+    for bad in ((3, 0, 0, 0), (16, 0, 0, 0), (0, 3, 0, 0), (0, 0, 3, 0), (0, 0, 1, 0),
+                (0, 0, 0, 3), (0, 0, 0, -1)):
+        cfg = pkv.LaunchConfig(*bad)
+        assert lib.paged_attention_decode_ex(*args, ctypes.byref(cfg), None) == -1, bad
+        assert lib.paged_attention_decode_split_ex(
+            A16, B16, C16, D16, E16, F16, G16, 2, 14, 2, 64, 16, 10, 4, 64, 1, 0.125,
+            ctypes.byref(cfg), None) == -1, bad
+        assert lib.paged_decode_step_ex(
+            A16, B16, C16, D16, E16, F16, G16, H16, I16, J16, K16, L16, M16, 2, 14, 2, 64, 16,
+            10, 4, 64, 1, 0.125, ctypes.byref(cfg), None) == -1, bad
+    empty = (A16, B16, C16, D16, E16, F16, 0, 14, 2, 64, 16, 10, 4, 0.125)
+    for good in ((0, 0, 0, 0), (1, 1, 2, 1), (8, 4, 4, 2), (2, 2, 0, 0)):
+        cfg = pkv.LaunchConfig(*good)
+        assert lib.paged_attention_decode_ex(*empty, ctypes.byref(cfg), None) == 0, good
+    assert lib.paged_attention_decode_ex(*empty, None, None) == 0
 
 
 def _decode(lib, **kw):

@@ -16,8 +16,9 @@ SWEEP = [f"sweep:{B}:{ctx}" for B in workloads.SWEEP_B for ctx in workloads.SWEE
 FULL_ORACLE = ["tiny", "qwen"] + SWEEP + ["long:1:32768", "long:1:131072", "long:4:32768"]
 
 
-def _decode(g, c):
-    return pkv.paged_attention_decode(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale)
+def _decode(g, c, launch=None):
+    return pkv.paged_attention_decode(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale,
+                                      launch=launch)
 
 
 @pytest.mark.parametrize("name", FULL_ORACLE)
@@ -186,21 +187,18 @@ def test_peaked_softmax_large_outputs():
 @pytest.mark.parametrize("subtiles", [1, 2, 4])
 @pytest.mark.parametrize("depth", [2, 4])
 def test_decode_every_launch_shape(waves, subtiles, depth):
-    try:
-        pkv.set_launch_config("decode", waves, subtiles, depth)
-        for name, D in (("qwen", 64), ("d128", 128)):
-            if name == "qwen":
-                c = case("qwen")
-            else:
-                c = workloads.custom_case("d128", B=3, Hq=32, Hkv=8, D=128, block_size=16,
-                                          lens=[1, 300, 1111], seed=96)
-            g = to_gpu(c)
-            out = _decode(g, c)
-            torch.cuda.synchronize()
-            want, _ = oracle_decode(c)
-            check_fp16(out, want, f"{name} NW={waves} NS={subtiles} DEPTH={depth}")
-    finally:
-        pkv.set_launch_config("decode", 0, 0, 0)
+    launch = dict(waves=waves, subtiles=subtiles, depth=depth)
+    for name, D in (("qwen", 64), ("d128", 128)):
+        if name == "qwen":
+            c = case("qwen")
+        else:
+            c = workloads.custom_case("d128", B=3, Hq=32, Hkv=8, D=128, block_size=16,
+                                      lens=[1, 300, 1111], seed=96)
+        g = to_gpu(c)
+        out = _decode(g, c, launch=launch)
+        torch.cuda.synchronize()
+        want, _ = oracle_decode(c)
+        check_fp16(out, want, f"{name} NW={waves} NS={subtiles} DEPTH={depth}")
 
 
 def test_out_of_range_block_ids_are_ignored():

@@ -13,9 +13,9 @@ from gpu_common import (PARTIAL_ATOL, case, check_fp16, host64, needs_gpu, oracl
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
 
-def _split_reduce(g, c, P, Pm=None):
+def _split_reduce(g, c, P, Pm=None, launch=None):
     po, pl = pkv.paged_attention_decode_split(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale,
-                                              P, max_partitions=Pm)
+                                              P, max_partitions=Pm, launch=launch)
     out, lse = pkv.split_reduce(po, pl, g.ctx, P, want_lse=True)
     return po, pl, out, lse
 
@@ -122,25 +122,22 @@ def test_split_ctx0():
 @pytest.mark.parametrize("subtiles", [1, 2, 4])
 @pytest.mark.parametrize("depth", [2, 4])
 def test_split_every_launch_shape(waves, subtiles, depth):
-    try:
-        pkv.set_launch_config("split", waves, subtiles, depth)
-        c = case("qwen")
-        g = to_gpu(c)
-        po, pl, out, lse = _split_reduce(g, c, 256)
-        torch.cuda.synchronize()
-        want, want_lse = oracle_decode(c)
-        check_fp16(out, want, f"split NW={waves} NS={subtiles} DEPTH={depth}")
-        _check_lse(lse, want_lse, "split shapes")
-        # head_dim 128, group 16 (both parts of P in one 16x16x32 MFMA), block size 32
-        c2 = workloads.custom_case("split_d128_g16", B=3, Hq=16, Hkv=1, D=128, block_size=32,
-                                   lens=[33, 700, 1500], seed=100)
-        g2 = to_gpu(c2)
-        po, pl, out2, lse2 = _split_reduce(g2, c2, 256)
-        torch.cuda.synchronize()
-        want2, want_lse2 = oracle_decode(c2)
-        check_fp16(out2, want2, f"split d128 g16 NW={waves} NS={subtiles} DEPTH={depth}")
-    finally:
-        pkv.set_launch_config("split", 0, 0, 0)
+    launch = dict(waves=waves, subtiles=subtiles, depth=depth)
+    c = case("qwen")
+    g = to_gpu(c)
+    po, pl, out, lse = _split_reduce(g, c, 256, launch=launch)
+    torch.cuda.synchronize()
+    want, want_lse = oracle_decode(c)
+    check_fp16(out, want, f"split NW={waves} NS={subtiles} DEPTH={depth}")
+    _check_lse(lse, want_lse, "split shapes")
+    # head_dim 128, group 16 (both parts of P in one 16x16x32 MFMA), block size 32
+    c2 = workloads.custom_case("split_d128_g16", B=3, Hq=16, Hkv=1, D=128, block_size=32,
+                               lens=[33, 700, 1500], seed=100)
+    g2 = to_gpu(c2)
+    po, pl, out2, lse2 = _split_reduce(g2, c2, 256, launch=launch)
+    torch.cuda.synchronize()
+    want2, want_lse2 = oracle_decode(c2)
+    check_fp16(out2, want2, f"split d128 g16 NW={waves} NS={subtiles} DEPTH={depth}")
 
 
 @pytest.mark.parametrize("name,P", [("tiny", 16), ("qwen", 256), ("sweep:8:1024", 64),
@@ -152,12 +149,8 @@ def test_split_compact_grid_matches_oracle(name, P):
     say(f"split compact {name}: P={P}")
     g = to_gpu(c)
     Pm = c.max_partitions(P) + 2
-    try:
-        pkv.set_grid_mode("compact")
-        po, pl, out, lse = _split_reduce(g, c, P, Pm)
-        torch.cuda.synchronize()
-    finally:
-        pkv.set_grid_mode("auto")
+    po, pl, out, lse = _split_reduce(g, c, P, Pm, launch=dict(grid="compact"))
+    torch.cuda.synchronize()
     wpo, wpl = ref.paged_attention_decode_split(c.q, c.k_pool, c.v_pool, c.block_tables,
                                                 c.context_lens, c.scale, P, Pm)
     gpl = host64(pl)
@@ -174,12 +167,8 @@ def test_split_compact_ragged_and_empty_sequences():
     c = workloads.custom_case("compact_ragged", B=7, Hq=14, Hkv=2, D=64, block_size=16,
                               lens=[0, 1, 700, 16, 0, 2049, 33], seed=102, max_blocks=160)
     g = to_gpu(c)
-    try:
-        pkv.set_grid_mode("compact")
-        po, pl, out, lse = _split_reduce(g, c, 64)
-        torch.cuda.synchronize()
-    finally:
-        pkv.set_grid_mode("auto")
+    po, pl, out, lse = _split_reduce(g, c, 64, launch=dict(grid="compact"))
+    torch.cuda.synchronize()
     want, want_lse = oracle_decode(c)
     check_fp16(out, want, "compact ragged")
     _check_lse(lse, want_lse, "compact ragged")

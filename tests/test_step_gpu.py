@@ -13,10 +13,10 @@ from gpu_common import (PARTIAL_ATOL, case, check_fp16, host64, needs_gpu, oracl
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
 
-def _step(g, c, P, ws=None, append=True, want_lse=True):
+def _step(g, c, P, ws=None, append=True, want_lse=True, launch=None):
     kw = dict(k_new=g.k_new, v_new=g.v_new, slot_mapping=g.slots) if append else {}
     return pkv.paged_decode_step(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale, P, workspace=ws,
-                                 want_lse=want_lse, **kw)
+                                 want_lse=want_lse, launch=launch, **kw)
 
 
 def _oracle_step(c, seqs=None):
@@ -205,17 +205,14 @@ def test_step_in_hip_graph_replays():
 @pytest.mark.parametrize("waves,subtiles,depth", [(1, 1, 2), (2, 2, 4), (4, 2, 2), (8, 4, 2),
                                                   (4, 1, 4)])
 def test_step_launch_shapes(waves, subtiles, depth):
-    try:
-        pkv.set_launch_config("split", waves, subtiles, depth)
-        for name in ("qwen", "tiny"):
-            c = case(name)
-            g = to_gpu(c)
-            out = _step(g, c, 64 if name == "tiny" else 256, want_lse=False)
-            torch.cuda.synchronize()
-            want, _, _, _ = _oracle_step(c)
-            check_fp16(out, want, f"step {name} NW={waves} NS={subtiles} DEPTH={depth}")
-    finally:
-        pkv.set_launch_config("split", 0, 0, 0)
+    launch = dict(waves=waves, subtiles=subtiles, depth=depth)
+    for name in ("qwen", "tiny"):
+        c = case(name)
+        g = to_gpu(c)
+        out = _step(g, c, 64 if name == "tiny" else 256, want_lse=False, launch=launch)
+        torch.cuda.synchronize()
+        want, _, _, _ = _oracle_step(c)
+        check_fp16(out, want, f"step {name} NW={waves} NS={subtiles} DEPTH={depth}")
 
 
 def test_step_merge_stress_against_three_launch_path():
@@ -257,11 +254,11 @@ def test_step_compact_grid_edges_and_churn():
                               lens=[0, 1, 16, 17, 511, 1300], seed=112, q_mult=4.0,
                               max_blocks=96)
     P = 64
-    try:
-        pkv.set_grid_mode("compact")
+    compact = dict(grid="compact")
+    if True:
         g = to_gpu(c)
         ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
-        out, lse = _step(g, c, P, ws)
+        out, lse = _step(g, c, P, ws, launch=compact)
         torch.cuda.synchronize()
         want, want_lse, kp, _ = _oracle_step(c)
         check_fp16(out, want, "compact step edges")
@@ -276,7 +273,7 @@ def test_step_compact_grid_edges_and_churn():
             g.q = torch.randn(g.q.shape, generator=gen, device=g.q.device).to(torch.float16)
             g.ctx = torch.randint(0, 96 * 16 + 1, (c.B,), generator=cpu_gen,
                                   dtype=torch.int32).to(g.q.device)
-            fused = _step(g, c, P, ws, append=False, want_lse=False)
+            fused = _step(g, c, P, ws, append=False, want_lse=False, launch=compact)
             po, pl = pkv.paged_attention_decode_split(g.q, g.k_pool, g.v_pool, g.bt, g.ctx,
                                                       c.scale, P)
             ref3 = pkv.split_reduce(po, pl, g.ctx, P)
@@ -284,8 +281,6 @@ def test_step_compact_grid_edges_and_churn():
             worst = max(worst, (fused.float() - ref3.float()).abs().max().item())
             _check_workspace_restored(ws)
         assert worst <= 2e-3, worst
-    finally:
-        pkv.set_grid_mode("auto")
 
 
 def test_step_wide_merge_large_group():
@@ -305,11 +300,7 @@ def test_step_wide_merge_large_group():
     _check_lse(lse, want_lse)
     assert np.array_equal(g.k_pool.cpu().numpy().view(np.uint16), kp.view(np.uint16))
     g4 = to_gpu(c)
-    pkv.set_launch_config("split", 4, 1, 2)
-    try:
-        out4, _ = _step(g4, c, P)
-        torch.cuda.synchronize()
-    finally:
-        pkv.set_launch_config("split", 0, 0, 0)
+    out4, _ = _step(g4, c, P, launch=dict(waves=8, subtiles=1, depth=2))
+    torch.cuda.synchronize()
     check_fp16(out4, want, "step G=16 at 4 waves")
 
