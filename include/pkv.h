@@ -269,9 +269,10 @@ int paged_attention_decode_split_ex(float* partial_out, float* partial_lse,
  *                     whether this step's attention sees the new value there
  *                     is undefined.
  *   partial_out       [B, num_q_heads, max_partitions, head_dim] fp32 and
- *   partial_lse       [B, num_q_heads, max_partitions] fp32 workspace, every
- *                     32-bit word all ones (0xFFFFFFFF) before the first call;
- *                     every call leaves them so.  num_q_heads / num_kv_heads *
+ *   partial_lse       [B, num_q_heads, max_partitions] fp32 workspace, all
+ *                     zero before the first call; every call leaves them so
+ *                     (rows in flight are stored bit-inverted, so a zero word
+ *                     means "not written").  num_q_heads / num_kv_heads *
  *                     max_partitions * head_dim * 4 must be below 2^30
  *                     (else PKV_ERR_UNSUPPORTED).  Not to be shared with
  *                     paged_attention_decode_split, which leaves values there.
@@ -286,9 +287,9 @@ int paged_attention_decode_split_ex(float* partial_out, float* partial_lse,
  * Each (sequence, KV head) with more than one non-empty partition is merged
  * in the launch by one of its workgroups: each takes a ticket from the pair's
  * counter early, the holder of the last ticket merges, and it reads the other
- * partitions' rows once none of their words is all ones (device-coherent
- * accesses; the others never wait).  It sets the rows it read back to all
- * ones and the counter back to zero.  Its wait is bounded in time (20 ms): a
+ * partitions' rows once none of their words is zero (device-coherent
+ * accesses; the others never wait).  It sets the rows it read back to zero
+ * and the counter back to zero.  Its wait is bounded in time (20 ms): a
  * workspace that breaks the contract above gives wrong numbers, not a
  * stalled queue.  A sequence that fits one partition is written directly.
  * Results equal append + split pass + split_reduce up to fp32 summation

@@ -456,11 +456,11 @@ COUNTER_STRIDE = 32  # int32 words per ticket counter (one 128-byte line)
 
 
 class StepWorkspace:
-    """Device workspace of paged_decode_step: split partials, every word all
-    ones (0xFFFFFFFF, "not written"), and the per-(sequence, KV head) ticket
-    counters, zero.  Set up here once; every call leaves it in that state.
-    Allocated with torch by the caller's code, never by the library.  reset()
-    restores the state (after an aborted call)."""
+    """Device workspace of paged_decode_step: split partials and the
+    per-(sequence, KV head) ticket counters, all zero ("not written").  Set up
+    here once; every call leaves it in that state.  Allocated with torch by
+    the caller's code, never by the library.  reset() restores the state
+    (after an aborted call)."""
 
     def __init__(self, B, num_q_heads, num_kv_heads, head_dim, max_partitions, device):
         self.partial_out = torch.empty((B, num_q_heads, max_partitions, head_dim),
@@ -474,8 +474,8 @@ class StepWorkspace:
         self.reset()
 
     def reset(self):
-        self.partial_out.view(torch.int32).fill_(-1)
-        self.partial_lse.view(torch.int32).fill_(-1)
+        self.partial_out.zero_()
+        self.partial_lse.zero_()
         self.counters.zero_()
 
 

@@ -309,6 +309,79 @@ int fill_q8(pkv::Q8Params& p, const void* q, const void* k_codes, const void* v_
   return PKV_OK;
 }
 
+// Argument checks of the fused step that do not involve its workspace
+// (decided on the host, before any HIP call).
+int check_step(const void* out, const float* lse_out, const void* q, const void* k_pool,
+               const void* v_pool, const void* k_new, const void* v_new,
+               const int64_t* slot_mapping, const int32_t* block_tables,
+               const int32_t* context_lens, int32_t B, int32_t num_q_heads,
+               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+               int32_t max_blocks_per_seq, int32_t partition_size, int32_t max_partitions,
+               float scale) {
+  int rc = check_attn_common(q, k_pool, v_pool, block_tables, context_lens, B, num_q_heads,
+                             num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                             scale);
+  if (rc != PKV_OK) return rc;
+  if (partition_size <= 0 || max_partitions <= 0 || partition_size % block_size != 0)
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_partitions * partition_size < (int64_t)max_blocks_per_seq * block_size)
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_partitions * partition_size > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  if (!out || !aligned(out, 16) || (lse_out && !aligned(lse_out, 4))) return PKV_ERR_INVALID_ARG;
+  if (slot_mapping) {
+    if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+        !aligned(slot_mapping, 8))
+      return PKV_ERR_INVALID_ARG;
+  }
+  const int64_t cells = (int64_t)B * num_kv_heads * max_partitions;
+  if (cells > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  // one buffer resource spans a pair's partials; its byte offsets, and the
+  // out-of-range offset the merge uses for rows it skips (2^30), must not meet
+  if ((int64_t)(num_q_heads / num_kv_heads) * max_partitions * head_dim * 4 >= (1 << 30))
+    return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+int launch_step(void* out, float* lse_out, void* k_pool, void* v_pool, const void* q,
+                const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                const int32_t* block_tables, const int32_t* context_lens, float* partial_out,
+                float* partial_lse, int32_t* counters, int32_t B, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                int32_t max_blocks_per_seq, int32_t partition_size, int32_t max_partitions,
+                float scale, const pkv_launch_config* config, hipStream_t st) {
+  AttnParams p = {};
+  p.q = static_cast<const pkv::f16*>(q);
+  p.k_pool = static_cast<const pkv::f16*>(k_pool);
+  p.v_pool = static_cast<const pkv::f16*>(v_pool);
+  p.k_pool_w = static_cast<pkv::f16*>(k_pool);
+  p.v_pool_w = static_cast<pkv::f16*>(v_pool);
+  p.k_new = static_cast<const pkv::f16*>(k_new);
+  p.v_new = static_cast<const pkv::f16*>(v_new);
+  p.slot_mapping = slot_mapping;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = static_cast<pkv::f16*>(out);
+  p.lse_out = lse_out;
+  p.partial_out = partial_out;
+  p.partial_lse = partial_lse;
+  p.counters = counters;
+  p.B = B;
+  p.Hq = num_q_heads;
+  p.Hkv = num_kv_heads;
+  p.G = num_q_heads / num_kv_heads;
+  p.block_size = block_size;
+  p.num_blocks = num_blocks;
+  p.max_blocks = max_blocks_per_seq;
+  p.partition_size = partition_size;
+  p.max_partitions = max_partitions;
+  p.spb_shift = spb_shift_of(block_size);
+  p.bs_shift = log2_or_neg(block_size);
+  p.part_shift = log2_or_neg(partition_size);
+  p.scale_log2 = scale * pkv::kLog2e;
+  return launch_attn<2>(p, head_dim, config, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -493,62 +566,18 @@ int paged_decode_step_ex(void* out, float* lse_out, void* k_pool, void* v_pool, 
                          int32_t partition_size, int32_t max_partitions, float scale,
                          const pkv_launch_config* config, void* stream) {
   if (!config_ok(config)) return PKV_ERR_INVALID_ARG;
-  int rc = check_attn_common(q, k_pool, v_pool, block_tables, context_lens, B, num_q_heads,
-                             num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
-                             scale);
-  if (rc != PKV_OK) return rc;
-  if (partition_size <= 0 || max_partitions <= 0 || partition_size % block_size != 0)
+  int rc = check_step(out, lse_out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_tables,
+                      context_lens, B, num_q_heads, num_kv_heads, head_dim, block_size,
+                      num_blocks, max_blocks_per_seq, partition_size, max_partitions, scale);
+  if (rc != PKV_OK || B == 0) return rc;
+  if (!partial_out || !partial_lse || !counters) return PKV_ERR_INVALID_ARG;
+  if (!aligned(partial_out, 16) || !aligned(partial_lse, 4) || !aligned(counters, 4))
     return PKV_ERR_INVALID_ARG;
-  if ((int64_t)max_partitions * partition_size < (int64_t)max_blocks_per_seq * block_size)
-    return PKV_ERR_INVALID_ARG;
-  if ((int64_t)max_partitions * partition_size > INT32_MAX) return PKV_ERR_INVALID_ARG;
-  if (B == 0) return PKV_OK;
-  if (!out || !partial_out || !partial_lse || !counters) return PKV_ERR_INVALID_ARG;
-  if (!aligned(out, 16) || !aligned(partial_out, 16) || !aligned(partial_lse, 4) ||
-      !aligned(counters, 4) || (lse_out && !aligned(lse_out, 4)))
-    return PKV_ERR_INVALID_ARG;
-  if (slot_mapping) {
-    if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16) ||
-        !aligned(slot_mapping, 8))
-      return PKV_ERR_INVALID_ARG;
-  }
-  const int64_t grid = (int64_t)B * num_kv_heads * max_partitions;
-  if (grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
-  // one buffer resource spans a pair's partials; its byte offsets, and the
-  // out-of-range offset the merge uses for rows it skips (2^30), must not meet
-  if ((int64_t)(num_q_heads / num_kv_heads) * max_partitions * head_dim * 4 >= (1 << 30))
-    return PKV_ERR_UNSUPPORTED;
-
-  AttnParams p = {};
-  p.q = static_cast<const pkv::f16*>(q);
-  p.k_pool = static_cast<const pkv::f16*>(k_pool);
-  p.v_pool = static_cast<const pkv::f16*>(v_pool);
-  p.k_pool_w = static_cast<pkv::f16*>(k_pool);
-  p.v_pool_w = static_cast<pkv::f16*>(v_pool);
-  p.k_new = static_cast<const pkv::f16*>(k_new);
-  p.v_new = static_cast<const pkv::f16*>(v_new);
-  p.slot_mapping = slot_mapping;
-  p.block_tables = block_tables;
-  p.context_lens = context_lens;
-  p.out = static_cast<pkv::f16*>(out);
-  p.lse_out = lse_out;
-  p.partial_out = partial_out;
-  p.partial_lse = partial_lse;
-  p.counters = counters;
-  p.B = B;
-  p.Hq = num_q_heads;
-  p.Hkv = num_kv_heads;
-  p.G = num_q_heads / num_kv_heads;
-  p.block_size = block_size;
-  p.num_blocks = num_blocks;
-  p.max_blocks = max_blocks_per_seq;
-  p.partition_size = partition_size;
-  p.max_partitions = max_partitions;
-  p.spb_shift = spb_shift_of(block_size);
-  p.bs_shift = log2_or_neg(block_size);
-  p.part_shift = log2_or_neg(p.partition_size);
-  p.scale_log2 = scale * pkv::kLog2e;
-  return launch_attn<2>(p, head_dim, config, static_cast<hipStream_t>(stream));
+  return launch_step(out, lse_out, k_pool, v_pool, q, k_new, v_new, slot_mapping, block_tables,
+                     context_lens, partial_out, partial_lse, counters, B, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                     partition_size, max_partitions, scale, config,
+                     static_cast<hipStream_t>(stream));
 }
 
 int paged_attention_prefill(void* out, const void* q, const void* k_pool, const void* v_pool,

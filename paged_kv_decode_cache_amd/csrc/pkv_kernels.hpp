@@ -143,9 +143,16 @@ __device__ __forceinline__ float fast_exp2(float x) {
 // cache-policy bit, which write through to, and read from, the device's
 // coherence point.  Buffer accesses are also range-checked by the hardware:
 // reads past the resource's end return 0, writes past it are dropped.
+//
+// Hand-off encoding.  A partial word is stored bit-inverted, and an all-zero
+// word means "not written yet": the workspace rests at zero between calls
+// (a zeroed buffer is ready to use), and a stored word is zero only for the
+// all-ones pattern, which no computed value has (NaNs from fp16 inputs or
+// from invalid operations carry other payloads; it is mapped to a quiet NaN
+// anyway).  32-bit words are single-copy atomic, so a row some of whose
+// words are still zero is seen as not written.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kCoherent = 16;                 // sc1
-constexpr unsigned kUnwritten = 0xFFFFFFFFu;  // a partial word not written yet
+constexpr int kCoherent = 16;  // sc1
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
@@ -165,14 +172,18 @@ __device__ __forceinline__ f32x4 load_coherent4(__amdgpu_buffer_rsrc_t rs, int o
 __device__ __forceinline__ float load_coherent1(__amdgpu_buffer_rsrc_t rs, int off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kCoherent));
 }
-__device__ __forceinline__ bool is_written(float x) {
-  return __builtin_bit_cast(unsigned, x) != kUnwritten;
+// Encode a value for the hand-off (never the all-zero word), and back.
+__device__ __forceinline__ float encode_partial(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  return __builtin_bit_cast(float, u == 0xFFFFFFFFu ? ~0x7FC00000u : ~u);
 }
-// A computed value never has the all-ones pattern (NaNs from fp16 inputs or
-// from invalid operations have other payloads); mapped to a quiet NaN anyway,
-// so a written word can never read as unwritten.
-__device__ __forceinline__ float as_written(float x) {
-  return is_written(x) ? x : __builtin_bit_cast(float, 0x7FC00000u);
+__device__ __forceinline__ float decode_partial(float w) {
+  return __builtin_bit_cast(float, ~__builtin_bit_cast(unsigned, w));
+}
+__device__ __forceinline__ bool is_written(float w) { return __builtin_bit_cast(unsigned, w) != 0u; }
+__device__ __forceinline__ bool row_written(f32x4 x, float l) {
+  return is_written(x[0]) && is_written(x[1]) && is_written(x[2]) && is_written(x[3]) &&
+         is_written(l);
 }
 
 // Streaming loads through buffer resources.  A load past the resource's
@@ -629,21 +640,20 @@ __device__ __forceinline__ void merge_rows(__amdgpu_buffer_rsrc_t po_rs,
     int xo[BATCH], lo[BATCH];
     f32x4 x[BATCH];
     float l[BATCH];
-    bool ok[BATCH];
+    bool ok[BATCH], other[BATCH];
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
       const int q = q0 + j * ngroups;
-      const bool other = q < np && q != p_own;
-      xo[j] = other ? ((hh * Pm + q) * D + 4 * cc) * 4 : kOutOfRange;
-      lo[j] = other ? (hh * Pm + q) * 4 : kOutOfRange;
+      other[j] = q < np && q != p_own;
+      xo[j] = other[j] ? ((hh * Pm + q) * D + 4 * cc) * 4 : kOutOfRange;
+      lo[j] = other[j] ? (hh * Pm + q) * 4 : kOutOfRange;
       x[j] = load_coherent4(po_rs, xo[j]);
       l[j] = load_coherent1(pl_rs, lo[j]);
     }
     bool all_ok = true;
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
-      ok[j] = is_written(x[j][0]) && is_written(x[j][1]) && is_written(x[j][2]) &&
-              is_written(x[j][3]) && is_written(l[j]);
+      ok[j] = !other[j] || row_written(x[j], l[j]);
       all_ok = all_ok && ok[j];
     }
     const long long t_spin = __all(all_ok) ? 0 : (long long)__builtin_amdgcn_s_memrealtime();
@@ -658,8 +668,7 @@ __device__ __forceinline__ void merge_rows(__amdgpu_buffer_rsrc_t po_rs,
         const float nl = load_coherent1(pl_rs, ok[j] ? kOutOfRange : lo[j]);
         x[j] = ok[j] ? x[j] : nx;
         l[j] = ok[j] ? l[j] : nl;
-        ok[j] = is_written(x[j][0]) && is_written(x[j][1]) && is_written(x[j][2]) &&
-                is_written(x[j][3]) && is_written(l[j]);
+        ok[j] = !other[j] || row_written(x[j], l[j]);
         all_ok = all_ok && ok[j];
       }
     }
@@ -667,8 +676,11 @@ __device__ __forceinline__ void merge_rows(__amdgpu_buffer_rsrc_t po_rs,
     for (int j = 0; j < BATCH; ++j) {
       const int q = q0 + j * ngroups;
       const bool mine = q == p_own;
-      const float lq = q < np ? (mine ? own_l : l[j]) : -INFINITY;
-      const f32x4 xq = mine ? own_x : x[j];
+      f32x4 xd;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) xd[v] = decode_partial(x[j][v]);
+      const float lq = q < np ? (mine ? own_l : decode_partial(l[j])) : -INFINITY;
+      const f32x4 xq = mine ? own_x : (other[j] ? xd : zero4f());
       const float Mn = fmaxf(M, lq);
       const float mu = Mn == -INFINITY ? 0.0f : Mn;
       const float sa = fast_exp2((M - mu) * kLog2e);  // 1 while M holds; 0 from -inf
@@ -703,9 +715,7 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
   const size_t head0 = (size_t)b * a.Hq + kvh * G;
   const __amdgpu_buffer_rsrc_t po_rs = buffer_rsrc(a.partial_out + head0 * Pm * D, G * Pm * D * 4);
   const __amdgpu_buffer_rsrc_t pl_rs = buffer_rsrc(a.partial_lse + head0 * Pm, G * Pm * 4);
-  f32x4 unwritten4;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) unwritten4[v] = __builtin_bit_cast(float, kUnwritten);
+  const f32x4 unwritten4 = zero4f();
   for (int slot = t; slot < nslots; slot += NT) {
     const int grp = slot / per_group;
     const int hc = slot % per_group;
@@ -749,7 +759,7 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
   for (int i = t; i < G * np; i += NT) {
     const int q = i % np;
     if (q != p_own)
-      store_coherent1(pl_rs, ((i / np) * Pm + q) * 4, __builtin_bit_cast(float, kUnwritten));
+      store_coherent1(pl_rs, ((i / np) * Pm + q) * 4, 0.0f);
   }
   for (int hc = t; hc < per_group; hc += NT) {
     float M = -INFINITY;
@@ -789,9 +799,9 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
 // under the K/V stream); the one holding the last ticket merges.  The others
 // store their partials with device-coherent stores and exit without waiting.
 // The merger keeps its own partial in LDS and polls the others' rows, which
-// hold an all-ones word until written (the merger sets them back after
-// reading, and resets the counter), so no store->flag->load round trips sit
-// on the kernel's tail.
+// hold a zero word until written (the merger sets them back after reading,
+// and resets the counter), so no store->flag->load round trips sit on the
+// kernel's tail.
 // One work item -- (sequence b, KV head kvh, partition p; p = 0 unsplit) --
 // of the attention kernels.  Every thread of the workgroup calls it with the
 // same item; smem is the workgroup's NW * AttnSmem<D, NS>::kWaveBytes bytes.
@@ -1034,10 +1044,10 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
           const __amdgpu_buffer_rsrc_t pl_rs =
               buffer_rsrc(a.partial_lse + head0 * Pm, a.G * Pm * 4);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) r[v] = as_written(r[v]);
+          for (int v = 0; v < 4; ++v) r[v] = encode_partial(r[v]);
           store_coherent4(po_rs, ((head_col * Pm + p) * D + d0) * 4, r);
           if (db == 0 && quad == 0)
-            store_coherent1(pl_rs, (head_col * Pm + p) * 4, as_written(lse_v));
+            store_coherent1(pl_rs, (head_col * Pm + p) * 4, encode_partial(lse_v));
         }
       } else {
         float* dst = a.partial_out + (((size_t)b * a.Hq + h) * a.max_partitions + p) * D + d0;

@@ -579,10 +579,10 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
           const __amdgpu_buffer_rsrc_t pl_rs =
               buffer_rsrc(a.partial_lse + head0 * Pm, a.G * Pm * 4);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) r[v] = as_written(r[v]);
+          for (int v = 0; v < 4; ++v) r[v] = encode_partial(r[v]);
           store_coherent4(po_rs, ((head_col * Pm + p) * D + d0) * 4, r);
           if (db == 0 && quad == 0)
-            store_coherent1(pl_rs, (head_col * Pm + p) * 4, as_written(lse_v));
+            store_coherent1(pl_rs, (head_col * Pm + p) * 4, encode_partial(lse_v));
         }
       } else {
         *reinterpret_cast<f32x4*>(a.partial_out +

@@ -356,3 +356,4 @@ def test_binding_rejects_wrong_dtype():
     ctx = torch.ones(1, dtype=torch.int32)
     with pytest.raises(TypeError):
         pkv.paged_attention_decode(q, kp, kp, bt, ctx, 0.125)
+

@@ -217,8 +217,8 @@ def _check_pools_q8(gq, want):
 
 def _check_workspace_restored(ws):
     assert int(ws.counters.abs().sum()) == 0
-    assert bool((ws.partial_out.view(torch.int32) == -1).all())
-    assert bool((ws.partial_lse.view(torch.int32) == -1).all())
+    assert bool((ws.partial_out.view(torch.int32) == 0).all())
+    assert bool((ws.partial_lse.view(torch.int32) == 0).all())
 
 
 @pytest.mark.parametrize("name,P", [("tiny", 16), ("qwen", 256), ("qwen", 1024),

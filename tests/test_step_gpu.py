@@ -27,11 +27,11 @@ def _oracle_step(c, seqs=None):
 
 
 def _check_workspace_restored(ws):
-    """Every call leaves the partials all ones ("not written") and the
-    counters zero, ready for the next call."""
+    """Every call leaves the partials and the counters zero ("not
+    written"), ready for the next call."""
     assert int(ws.counters.abs().sum()) == 0
-    assert bool((ws.partial_out.view(torch.int32) == -1).all())
-    assert bool((ws.partial_lse.view(torch.int32) == -1).all())
+    assert bool((ws.partial_out.view(torch.int32) == 0).all())
+    assert bool((ws.partial_lse.view(torch.int32) == 0).all())
 
 
 def _check_lse(got, want, rows=None):
