@@ -83,8 +83,10 @@ enum {
   PKV_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, ...   */
   PKV_ERR_UNSUPPORTED = -2, /* head_dim / block_size / group not compiled  */
   PKV_ERR_LAUNCH = -3,      /* HIP reported an error for the launch        */
-  PKV_ERR_NO_SPACE = -4     /* allocator: not enough free blocks, or a
+  PKV_ERR_NO_SPACE = -4,    /* allocator: not enough free blocks, or a
                                sequence would pass max_blocks_per_seq      */
+  PKV_ERR_SCRATCH = -5      /* paged_decode_step_noalloc: the call needs more
+                               than its static scratch holds               */
 };
 
 /* Static, human-readable name of a status code. */
@@ -319,6 +321,42 @@ int paged_decode_step_ex(void* out, float* lse_out,
                          int32_t max_blocks_per_seq, int32_t partition_size,
                          int32_t max_partitions, float scale,
                          const pkv_launch_config* config, void* stream);
+
+/*
+ * paged_decode_step_noalloc -- paged_decode_step with no workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * step's workspace (partials, their lse, ticket counters) lives in a static
+ * device array of the library, 16 MiB per GPU, held by each GPU the library
+ * runs on until the process ends; a call needs
+ *   round256(B * num_q_heads * max_partitions * head_dim * 4)
+ *   + round256(B * num_q_heads * max_partitions * 4)
+ *   + round256(B * num_kv_heads * 128)
+ * bytes of it (round256 = rounded up to a multiple of 256), and returns
+ * PKV_ERR_SCRATCH, before any HIP call, when that is more than 16 MiB (at
+ * head_dim 64 with 14 query heads: about 4,600 sequence-partitions, e.g.
+ * B=32 at up to 144 partitions each).
+ *
+ * The call allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine.  Its first call on a device (the current device, which must be
+ * the stream's) resolves the array's address there and clears it once with
+ * a fill kernel on `stream`.  Every call on a GPU shares that GPU's array
+ * and leaves it all zero, as the workspace contract of paged_decode_step
+ * asks; calls that overlap on one GPU (on different streams without an
+ * ordering between them, or from several host threads) race on it and give
+ * undefined results, and a call that faults or is aborted leaves it
+ * undefined.  Arguments, outputs, results and errors are otherwise those of
+ * paged_decode_step.
+ */
+int paged_decode_step_noalloc(void* out, float* lse_out,
+                              void* k_pool, void* v_pool,
+                              const void* q, const void* k_new, const void* v_new,
+                              const int64_t* slot_mapping,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t partition_size,
+                              int32_t max_partitions, float scale, void* stream);
 
 /*
  * paged_attention_prefill -- attention of a chunk of new tokens per sequence

@@ -24,6 +24,7 @@ PKV_ERR_INVALID_ARG = -1
 PKV_ERR_UNSUPPORTED = -2
 PKV_ERR_LAUNCH = -3
 PKV_ERR_NO_SPACE = -4
+PKV_ERR_SCRATCH = -5
 
 
 class NoSpaceError(RuntimeError):
@@ -50,6 +51,8 @@ _SIGNATURES = {
                                          _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "paged_decode_step_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                             _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P]),
+    "paged_decode_step_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I,
+                                                 _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "paged_decode_step_q8": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                             _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                                             _P]),
@@ -524,6 +527,42 @@ def paged_decode_step(q, k_pool, v_pool, block_tables, context_lens, scale, part
     else:
         rc = load_library().paged_decode_step_ex(*args, ctypes.byref(cfg), _stream(dev, stream))
     _raise(rc, "paged_decode_step")
+    return (out, lse_out) if lse_out is not None else out
+
+
+def paged_decode_step_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale,
+                              partition_size, k_new=None, v_new=None, slot_mapping=None,
+                              out=None, lse_out=None, want_lse=False, stream=None):
+    """paged_decode_step on the library's static scratch (no workspace; the C
+    call allocates nothing).  Returns out [B, Hq, D] fp16 (and lse [B, Hq]).
+    Raises ValueError when the call needs more scratch than the library holds
+    (PKV_ERR_SCRATCH)."""
+    dev, B, Hq, Hkv, D, bs, NB, maxb = _attn_shapes(q, k_pool, v_pool, block_tables,
+                                                    context_lens)
+    Pm = max_partitions_for(maxb, bs, partition_size)
+    if slot_mapping is not None:
+        _need(k_new, "k_new", torch.float16, 3, dev)
+        _need(v_new, "v_new", torch.float16, 3, dev)
+        _need(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+        if k_new.shape != (B, Hkv, D) or v_new.shape != (B, Hkv, D) or \
+                slot_mapping.shape != (B,):
+            raise ValueError("k_new/v_new must be [B, Hkv, D] and slot_mapping [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    _need(out, "out", torch.float16, 3, dev)
+    if want_lse and lse_out is None:
+        lse_out = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, 2, dev)
+    rc = load_library().paged_decode_step_noalloc(
+        _ptr(out), _ptr(lse_out), _ptr(k_pool), _ptr(v_pool), _ptr(q),
+        _ptr(k_new) if slot_mapping is not None else None,
+        _ptr(v_new) if slot_mapping is not None else None, _ptr(slot_mapping),
+        _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, bs, NB, maxb,
+        int(partition_size), Pm, float(scale), _stream(dev, stream))
+    if rc == PKV_ERR_SCRATCH:
+        raise ValueError(f"paged_decode_step_noalloc: {status_string(rc)} (status {rc})")
+    _raise(rc, "paged_decode_step_noalloc")
     return (out, lse_out) if lse_out is not None else out
 
 

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "pkv.h"
 #include "pkv_kernels.hpp"
@@ -382,6 +383,67 @@ int launch_step(void* out, float* lse_out, void* k_pool, void* v_pool, const voi
   return launch_attn<2>(p, head_dim, config, st);
 }
 
+// ---- paged_decode_step_noalloc: the fused step on a static scratch -------
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops, harnesses that forbid hipMalloc): the step's workspace
+// (partials, their lse, ticket counters) lives in this file-scope device
+// array instead of a caller buffer.  Each GPU the library runs on holds its
+// own copy until the process ends.  Its rest state is all zero, which every
+// call leaves (as the workspace contract of paged_decode_step).
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+struct ScratchLayout {
+  size_t partial_out, partial_lse, counters;
+};
+
+size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Byte offsets of the workspace parts in the scratch; false if they do not fit.
+bool scratch_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t Pm,
+                    ScratchLayout* L) {
+  const size_t po = round256((size_t)B * Hq * Pm * D * 4);
+  const size_t pl = round256((size_t)B * Hq * Pm * 4);
+  const size_t ct = round256((size_t)B * Hkv * pkv::kCounterStride * 4);
+  L->partial_out = 0;
+  L->partial_lse = po;
+  L->counters = po + pl;
+  return po + pl + ct <= kScratchBytes;
+}
+
+__global__ __launch_bounds__(256) void zero_scratch_kernel(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The scratch's device address on the current device (the array's name is a
+// host-side stand-in, never passed to a kernel).  Resolved once per device
+// with that device current, and cleared once there by a fill kernel on the
+// caller's stream (ordered before the caller's step; a memset node is never
+// recorded into a graph the caller may be capturing).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch[kMaxDevices] = {};
+
+int device_scratch(unsigned char** out, hipStream_t st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return PKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return PKV_ERR_LAUNCH;
+    hipLaunchKernelGGL(zero_scratch_kernel, dim3(1024), dim3(256), 0, st,
+                       static_cast<uint4*>(ptr), kScratchBytes / 16);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_LAUNCH;
+    g_scratch[dev] = static_cast<unsigned char*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -393,6 +455,8 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported shape";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     case PKV_ERR_NO_SPACE: return "no space: not enough free cache blocks";
+    case PKV_ERR_SCRATCH:
+      return "the call needs more than paged_decode_step_noalloc's static scratch holds";
     default: return "unknown status";
   }
 }
@@ -578,6 +642,33 @@ int paged_decode_step_ex(void* out, float* lse_out, void* k_pool, void* v_pool, 
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                      partition_size, max_partitions, scale, config,
                      static_cast<hipStream_t>(stream));
+}
+
+int paged_decode_step_noalloc(void* out, float* lse_out, void* k_pool, void* v_pool,
+                              const void* q, const void* k_new, const void* v_new,
+                              const int64_t* slot_mapping, const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t B, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t max_blocks_per_seq,
+                              int32_t partition_size, int32_t max_partitions, float scale,
+                              void* stream) {
+  int rc = check_step(out, lse_out, q, k_pool, v_pool, k_new, v_new, slot_mapping, block_tables,
+                      context_lens, B, num_q_heads, num_kv_heads, head_dim, block_size,
+                      num_blocks, max_blocks_per_seq, partition_size, max_partitions, scale);
+  if (rc != PKV_OK || B == 0) return rc;
+  ScratchLayout L;
+  if (!scratch_layout(B, num_q_heads, num_kv_heads, head_dim, max_partitions, &L))
+    return PKV_ERR_SCRATCH;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  unsigned char* base = nullptr;
+  rc = device_scratch(&base, st);
+  if (rc != PKV_OK) return rc;
+  return launch_step(out, lse_out, k_pool, v_pool, q, k_new, v_new, slot_mapping, block_tables,
+                     context_lens, reinterpret_cast<float*>(base + L.partial_out),
+                     reinterpret_cast<float*>(base + L.partial_lse),
+                     reinterpret_cast<int32_t*>(base + L.counters), B, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                     partition_size, max_partitions, scale, nullptr, st);
 }
 
 int paged_attention_prefill(void* out, const void* q, const void* k_pool, const void* v_pool,

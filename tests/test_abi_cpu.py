@@ -357,3 +357,28 @@ def test_binding_rejects_wrong_dtype():
     with pytest.raises(TypeError):
         pkv.paged_attention_decode(q, kp, kp, bt, ctx, 0.125)
 
+
+@host_only
+def test_step_noalloc_rejects_oversize_and_bad_args():
+    """paged_decode_step_noalloc: argument errors as paged_decode_step, and a
+    workspace larger than its static scratch gives PKV_ERR_SCRATCH, all
+    decided before any HIP call."""
+    lib = pkv.load_library()
+    base = dict(out=A16, lse=None, k=B16, v=C16, q=D16, kn=None, vn=None, slots=None, bt=E16,
+                ctx=F16, B=2, Hq=14, Hkv=2, D=64, bs=16, NB=10, maxb=4, P=64, Pm=1, scale=0.125)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return lib.paged_decode_step_noalloc(
+            a["out"], a["lse"], a["k"], a["v"], a["q"], a["kn"], a["vn"], a["slots"], a["bt"],
+            a["ctx"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["maxb"], a["P"],
+            a["Pm"], a["scale"], None)
+    assert call(B=0) == 0
+    assert call(out=None) == -1
+    assert call(P=24) == -1                      # not a multiple of block_size
+    assert call(Pm=0) == -1
+    assert call(D=96) == -2
+    # 4096 x 32 x 256 partitions x 128 dims x 4 bytes = 17 GB of partials
+    assert call(B=4096, Hq=32, Hkv=8, D=128, maxb=2048, P=256, Pm=128) == pkv.PKV_ERR_SCRATCH
+    assert "scratch" in pkv.status_string(pkv.PKV_ERR_SCRATCH)
