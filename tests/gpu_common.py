@@ -82,11 +82,16 @@ def oracle_decode(c, seqs=None):
                                       c.scale, return_lse=True, seqs=seqs)
 
 
-def sample_rows(c, k: int = 24, seed: int = 0):
-    """Sequences to check where the oracle cannot do the whole batch quickly:
-    the longest, the shortest and a seeded random selection."""
-    lens = c.context_lens
-    rng = np.random.default_rng(seed)
-    picks = {int(np.argmax(lens)), int(np.argmin(lens))}
-    picks.update(int(i) for i in rng.choice(c.B, size=min(k, c.B), replace=False))
-    return sorted(picks)[:max(k, 2)]
+@functools.lru_cache(maxsize=None)
+def oracle_full(name: str, appended: bool = False):
+    """(out, lse) of the fp64 oracle over every sequence of a named workload,
+    over its pools as generated or after the step's append of each
+    sequence's new token; cached, since several tests compare the whole
+    skewed batch (1.77 GB of K/V) against it."""
+    c = case(name)
+    if appended:
+        kp, vp = ref.kv_cache_append(c.k_pool, c.v_pool, c.k_new, c.v_new, c.slot_mapping)
+    else:
+        kp, vp = c.k_pool, c.v_pool
+    return ref.paged_attention_decode(c.q, kp, vp, c.block_tables, c.context_lens, c.scale,
+                                      return_lse=True)

@@ -7,7 +7,7 @@ import torch
 import paged_kv_decode_cache_amd as pkv
 import workloads
 from oracle import paged_ref as ref
-from gpu_common import (DEV, case, check_fp16, needs_gpu, oracle_decode, sample_rows, say,
+from gpu_common import (DEV, case, check_fp16, needs_gpu, oracle_decode, oracle_full, say,
                         to_gpu)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
@@ -34,16 +34,15 @@ def test_decode_matches_oracle(name):
 
 
 @pytest.mark.parametrize("name", ["skewed", "long:4:131072"])
-def test_decode_matches_oracle_sampled(name):
-    """Full-size launch; the oracle checks a sample of sequences one by one."""
+def test_decode_matches_oracle_full_size(name):
+    """Full-size launch, every sequence against the oracle."""
     c = case(name)
-    rows = sample_rows(c, k=16 if name == "skewed" else 4)
-    say(f"decode {name} (sampled rows {rows})")
+    say(f"decode {name} (all {c.B} sequences)")
     g = to_gpu(c)
     out = _decode(g, c)
     torch.cuda.synchronize()
-    want, _ = oracle_decode(c, seqs=rows)
-    check_fp16(out, want, name, rows=rows)
+    want, _ = oracle_full(name)
+    check_fp16(out, want, name)
     assert torch.isfinite(out.float()).all()
 
 

@@ -355,7 +355,7 @@ def test_q8_step_in_hip_graph_replays():
 def test_q8_step_ragged_many_partitions():
     """A ragged batch at a small partition (up to 128 partitions per sequence,
     most of the grid's workgroups empty): the merge walks many batches of
-    rows.  Sampled sequences against the oracle's 8-bit append + decode; the
+    rows.  Every sequence against the oracle's 8-bit append + decode; the
     cache write checked whole."""
     rng = np.random.default_rng(140)
     lens = rng.integers(1, 8193, 24).tolist()
@@ -371,9 +371,8 @@ def test_q8_step_ragged_many_partitions():
     torch.cuda.synchronize()
     want_pools = ref.kv_cache_append_q8(kc, vc, ks, vs, c.k_new, c.v_new, c.slot_mapping)
     _check_pools_q8(gq, want_pools)
-    rows = [0, 1] + rng.choice(np.arange(2, 24), 6, replace=False).tolist()
-    want, _ = _oracle_decode_q8(c, *want_pools, seqs=rows)
-    check_fp16(out, want, "q8 step ragged", rows=rows)
+    want, _ = _oracle_decode_q8(c, *want_pools)
+    check_fp16(out, want, "q8 step ragged")
     _check_workspace_restored(ws)
 
 

@@ -8,7 +8,7 @@ import paged_kv_decode_cache_amd as pkv
 import workloads
 from oracle import paged_ref as ref
 from gpu_common import (PARTIAL_ATOL, case, check_fp16, host64, needs_gpu, oracle_decode,
-                        sample_rows, say, to_gpu)
+                        oracle_full, say, to_gpu)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -65,19 +65,41 @@ def test_step_matches_append_then_decode(name, P):
     _check_workspace_restored(ws)
 
 
-@pytest.mark.parametrize("name", ["skewed", "long:4:131072"])
-def test_step_full_size_sampled(name):
+@pytest.mark.parametrize("name,grid", [("skewed", "auto"), ("skewed", "compact"),
+                                       ("long:4:131072", "auto")])
+def test_step_full_size(name, grid):
+    """Full-size launches, every sequence against the oracle's append +
+    decode."""
     c = case(name)
     P = 512
-    rows = sample_rows(c, k=16 if name == "skewed" else 4)
-    say(f"step {name} sampled {rows}")
+    say(f"step {name} grid={grid} (all {c.B} sequences)")
     g = to_gpu(c)
     ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
-    out, lse = _step(g, c, P, ws)
+    out, lse = _step(g, c, P, ws, launch=dict(grid=grid))
     torch.cuda.synchronize()
-    want, want_lse, _, _ = _oracle_step(c, seqs=rows)
-    check_fp16(out, want, f"step {name}", rows=rows)
-    _check_lse(lse, want_lse, rows=rows)
+    want, want_lse = oracle_full(name, appended=True)
+    check_fp16(out, want, f"step {name} {grid}")
+    _check_lse(lse, want_lse)
+    _check_workspace_restored(ws)
+
+
+def test_step_compact_grid_large_ragged_batch():
+    """The fused step on the compact grid with 300 ragged sequences (empty
+    ones write zeros), every sequence against the oracle's append + decode."""
+    rng = np.random.default_rng(134)
+    lens = rng.integers(0, 2001, 300).tolist()
+    lens[0], lens[1], lens[299] = 0, 2000, 1
+    c = workloads.custom_case("step_compact_300", B=300, Hq=14, Hkv=2, D=64, block_size=16,
+                              lens=lens, seed=135)
+    g = to_gpu(c)
+    P = 128
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    out, lse = _step(g, c, P, ws, launch=dict(grid="compact"))
+    torch.cuda.synchronize()
+    want, want_lse, kp, vp = _oracle_step(c)
+    check_fp16(out, want, "step compact B=300")
+    _check_lse(lse, want_lse)
+    assert np.array_equal(g.k_pool.cpu().numpy().view(np.uint16), kp.view(np.uint16))
     _check_workspace_restored(ws)
 
 
