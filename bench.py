@@ -9,20 +9,28 @@ split_reduce) is timed beside it.  The default workload is the batch x context
 sweep point B=32, ctx=4096 (Hq=14, Hkv=2, D=64, block_size=16, fp16).
 
 Timing protocol
+  * Kernel gate first: a child process runs 32 fused steps and 32
+    three-launch steps under rocprofv3 --kernel-trace, and the line records
+    whether the library launched exactly the expected kernels, by name, one
+    fused kernel per step (three kernels per three-launch step), and their
+    traced average durations.
   * R rotation sets: disjoint block ranges of one large pool, each with its own
     block tables and new tokens, R chosen so the K/V bytes of all sets exceed
     4x the 256 MB Infinity Cache; step i uses set i % R, so every call reads
     its K/V from HBM.
   * W untimed warm-up steps and at least 200 ms of warm-up (clock ramp).
-  * R consecutive steps (one per set) are captured in one HIP graph and
-    replayed until K steps have run; HIP events on the replay stream bracket
-    the timed replays (after torch.cuda.synchronize()).  The split pass alone
-    is timed the same way (R back-to-back launches per replay) for the
-    roofline figure.  Eager (per-call Python) timings are reported beside.
-  * A streaming-read probe over the same bytes per launch gives the
-    achievable read bandwidth.
-  * The fp64 oracle runs on a bounded sample of the same workload on the host
-    (one thread) for the CPU baseline.
+  * Steps are launched from HIP graphs (no host launch cost).  The value of
+    record: 15 trials, each of at least max(K, 100) steps (graph replays of
+    the R consecutive steps), HIP events on the replay stream around each
+    trial; p10 / p50 / p90 of the per-step time, value and % of peak from the
+    p50.  Exactly K steps (a graph of K steps, replayed once between two
+    synchronizations) are timed too and reported beside it.
+  * Two read probes over the same bytes per launch: a contiguous streaming
+    read (8-16 loads in flight per lane, best grid) and the decode's own K/V
+    access pattern with no arithmetic.
+  * The fp64 oracle runs on a bounded sample of the same workload on the
+    host, with every core of the process's affinity as BLAS threads and with
+    one thread, for the CPU baseline.
 
 Prints one JSON line.  --sweep writes per-point lines for the whole
 batch x context sweep (unsplit and split) to a file instead.
@@ -74,6 +82,9 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 20 plain device copies of MIB MiB (a known-size "
                          "reference for HBM traffic counters)")
+    ap.add_argument("--trials", type=int, default=15, help="timed trials (p10/p50/p90)")
+    ap.add_argument("--no-gate", action="store_true", help="skip the rocprofv3 kernel gate")
+    ap.add_argument("--gate-child", action="store_true", help=argparse.SUPPRESS)
     return ap.parse_args()
 
 
@@ -118,29 +129,61 @@ class Rotation:
         self.v_new = t(case.v_new)
 
 
-def time_cpu_oracle(case, seconds):
-    """fp64 oracle on a bounded sample of the batch; returns (GB/s, sample)."""
+def host_info():
+    """Cores of this process's affinity, the CPU model and numpy's BLAS."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:  # threadpoolctl missing or unable to inspect
+        pass
+    return cores, model, blas
+
+
+def time_cpu_oracle(case, seconds, threads):
+    """fp64 oracle on a bounded sample of the batch with `threads` BLAS
+    threads; returns (GB/s, description of the sample)."""
     from threadpoolctl import threadpool_limits
     from oracle import paged_ref as ref
     nseq = max(1, min(case.B, 4))
     seqs = list(range(nseq))
     done = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
+        t0 = time.perf_counter()
         while True:
             ref.paged_attention_decode(case.q, case.k_pool, case.v_pool, case.block_tables,
                                        case.context_lens, case.scale, seqs=seqs)
             done += 1
             if time.perf_counter() - t0 >= seconds:
                 break
-    dt = time.perf_counter() - t0
+        dt = time.perf_counter() - t0
     ctx_sample = int(case.context_lens[:nseq].astype(np.int64).sum())
     sample_bytes = alg_bytes(nseq, ctx_sample, case.Hq, case.Hkv, case.D)
     gbs = sample_bytes * done / dt / 1e9
     sample = (f"oracle paged_attention_decode on {nseq} of {case.B} sequences "
               f"({ctx_sample} positions, all {case.Hkv} KV heads) x {done} repeats in "
-              f"{dt:.1f} s, fp64, one thread; rate scaled by algorithmic bytes")
+              f"{dt:.1f} s, fp64, {threads} BLAS thread(s); rate scaled by algorithmic bytes")
     return gbs, sample
+
+
+def cpu_baseline(case, seconds):
+    cores, model, blas = host_info()
+    gbs, sample = time_cpu_oracle(case, seconds, cores)
+    gbs1, sample1 = time_cpu_oracle(case, seconds, 1)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": sample, "one_thread": {"value": round(gbs1, 4), "sample": sample1},
+            "cpu_model": model, "blas": blas}
 
 
 def capture(fns):
@@ -161,6 +204,34 @@ def capture(fns):
     return g
 
 
+def time_trials(g, per_replay, K, trials):
+    """µs per captured unit over `trials` trials of >= max(K, 100) units
+    each (graph replays), HIP events on the replay stream around each trial.
+    Returns the sorted per-trial times."""
+    import torch
+    reps = max(1, math.ceil(max(K, 100) / per_replay))
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    out = []
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3 / (reps * per_replay))
+    return sorted(out)
+
+
+def pct(sorted_vals, q):
+    """Nearest-rank percentile of sorted values."""
+    i = min(len(sorted_vals) - 1, max(0, math.ceil(q / 100 * len(sorted_vals)) - 1))
+    return sorted_vals[i]
+
+
 def time_graph(g, per_replay, K):
     """Average µs per captured unit over >= K units of graph replays."""
     import torch
@@ -178,38 +249,79 @@ def time_graph(g, per_replay, K):
     return e0.elapsed_time(e1) * 1e3 / (reps * per_replay)
 
 
-def probe_read_gbs(rot, nbytes, R, K):
-    """Streaming-read probe over the same byte count per launch, rotating
-    through the K/V pool (so reads are cold like the kernel's); best grid."""
+def _probe_lib():
     import ctypes
-    import torch
     lib_path = os.path.join(ROOT, "paged_kv_decode_cache_amd", "libpkv_probe.so")
     if not os.path.exists(lib_path):
         return None
     lib = ctypes.CDLL(lib_path)
-    lib.pkv_probe_stream_read.restype = ctypes.c_int
-    lib.pkv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                          ctypes.c_int, ctypes.c_void_p]
+    P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.pkv_probe_stream_read.restype = I
+    lib.pkv_probe_stream_read.argtypes = [P, L, P, I, I, P]
+    lib.pkv_probe_paged_read.restype = I
+    lib.pkv_probe_paged_read.argtypes = [P, P, P, I, I, I, I, I, I, P, P]
+    return lib
+
+
+def probe_read_gbs(rot, nbytes, R, K):
+    """Contiguous streaming read of the same byte count per launch, rotating
+    through the K/V pool (cold like the kernel's reads); best grid and loads
+    in flight.  Returns (GB/s, grid, loads in flight)."""
+    import ctypes
+    import torch
+    lib = _probe_lib()
+    if lib is None:
+        return None, None, None
     flat = rot.k_pool.view(-1)
     total = flat.numel() * 2
     per = (min(nbytes, total) // 16) * 16     # never past the end of the pool
     sink = torch.zeros(4, dtype=torch.int32, device=flat.device)
-    best = 0.0
-    for grid in (1024, 2048, 4096, 8192):
-        def launch(r, grid=grid):
-            off = (r * per) % (total - per) if total > per else 0
-            off -= off % 16
-            assert off + per <= total
-            st = torch.cuda.current_stream().cuda_stream
-            rc = lib.pkv_probe_stream_read(ctypes.c_void_p(flat.data_ptr() + off), per,
-                                           ctypes.c_void_p(sink.data_ptr()), grid,
-                                           ctypes.c_void_p(st))
-            if rc != 0:
-                raise RuntimeError(f"probe launch failed: {rc}")
-        g = capture([lambda r=r: launch(r) for r in range(R)])
-        us = time_graph(g, R, K)
-        best = max(best, per / (us * 1e-6) / 1e9)
+    best = (0.0, None, None)
+    for grid in (256, 512, 1024, 4096):
+        for u in (8, 16):
+            def launch(r, grid=grid, u=u):
+                off = (r * per) % (total - per) if total > per else 0
+                off -= off % 16
+                assert off + per <= total
+                st = torch.cuda.current_stream().cuda_stream
+                rc = lib.pkv_probe_stream_read(ctypes.c_void_p(flat.data_ptr() + off), per,
+                                               ctypes.c_void_p(sink.data_ptr()), grid, u,
+                                               ctypes.c_void_p(st))
+                if rc != 0:
+                    raise RuntimeError(f"probe launch failed: {rc}")
+            g = capture([lambda r=r: launch(r) for r in range(R)])
+            us = time_graph(g, R, K)
+            gbs = per / (us * 1e-6) / 1e9
+            if gbs > best[0]:
+                best = (gbs, grid, u)
     return best
+
+
+def probe_paged_gbs(rot, case, P, R, K):
+    """The decode's own K/V reads (block tables, one head per workgroup,
+    whole-line non-temporal loads, two subtiles in flight per wave) with no
+    arithmetic, over the same rotation; GB/s on the K/V bytes."""
+    import ctypes
+    import torch
+    lib = _probe_lib()
+    if lib is None or case.D != 64 or case.block_size != 16:
+        return None
+    ctx = int(case.context_lens.max())
+    if int(case.context_lens.min()) != ctx:
+        return None
+    sink = torch.zeros(4, dtype=torch.int32, device=rot.q.device)
+
+    def launch(r):
+        st = torch.cuda.current_stream().cuda_stream
+        rc = lib.pkv_probe_paged_read(ctypes.c_void_p(rot.k_pool.data_ptr()),
+                                      ctypes.c_void_p(rot.v_pool.data_ptr()),
+                                      ctypes.c_void_p(rot.bt[r].data_ptr()), case.B, case.Hkv,
+                                      ctx, rot.k_pool.shape[0], rot.bt[r].shape[1], P,
+                                      ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st))
+        if rc != 0:
+            raise RuntimeError(f"paged probe launch failed: {rc}")
+    us = time_graph(capture([lambda r=r: launch(r) for r in range(R)]), R, K)
+    return case.kv_bytes() / (us * 1e-6) / 1e9
 
 
 KERNEL_SOURCES = ("paged_kv_decode_cache_amd/csrc/pkv_kernels.hpp",
@@ -259,7 +371,7 @@ def copy_calibration(args, device):
     del src, dst
 
 
-def run_headline(args):
+def run_headline(args, gate=None):
     import torch
     import paged_kv_decode_cache_amd as pkv
     import workloads
@@ -323,11 +435,31 @@ def run_headline(args):
     K = args.steps
 
     # Graph-launched steps: R consecutive steps (one per rotation set) are
-    # captured once and replayed; HIP events on the replay stream bracket the
-    # timed replays.  This is the timing of record (no host launch overhead).
-    fused_us = time_graph(capture([lambda r=r: fused_step(r) for r in range(R)]), R, K)
-    three_us = time_graph(capture([lambda r=r: three_launch_step(r) for r in range(R)]), R, K)
-    split_us = time_graph(capture([lambda r=r: split_pass(r) for r in range(R)]), R, K)
+    # captured once and replayed; HIP events on the replay stream bracket each
+    # trial.  This is the timing of record (no host launch overhead).
+    trials = max(1, args.trials)
+    g_fused = capture([lambda r=r: fused_step(r) for r in range(R)])
+    g_three = capture([lambda r=r: three_launch_step(r) for r in range(R)])
+    g_split = capture([lambda r=r: split_pass(r) for r in range(R)])
+    fused_t = time_trials(g_fused, R, K, trials)
+    three_t = time_trials(g_three, R, K, trials)
+    split_t = time_trials(g_split, R, K, trials)
+    fused_us, three_us, split_us = pct(fused_t, 50), pct(three_t, 50), pct(split_t, 50)
+    step_t = fused_t if fused else three_t
+
+    # Exactly K steps: one graph of K consecutive steps (rotating through the
+    # sets), replayed once between two synchronizations.
+    g_k = capture([lambda i=i: (fused_step if fused else three_launch_step)(i)
+                   for i in range(K)])
+    g_k.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g_k.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    k_region_us = e0.elapsed_time(e1) * 1e3 / K
+    del g_k
 
     # Eager launches (Python binding per call), for context.
     torch.cuda.synchronize()
@@ -342,7 +474,8 @@ def run_headline(args):
         rot.q, rot.k_pool, rot.v_pool, rot.bt[r], rot.ctx, case.scale, out=out)
         for r in range(R)])
     unsplit_us = time_graph(g_uns, R, K)
-    probe = probe_read_gbs(rot, case.kv_bytes(), R, K)
+    probe, probe_grid, probe_loads = probe_read_gbs(rot, case.kv_bytes(), R, K)
+    paged_probe = probe_paged_gbs(rot, case, P, R, K)
 
     ctx_sum = int(case.context_lens.astype(np.int64).sum())
     step_bytes = alg_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
@@ -409,10 +542,27 @@ def run_headline(args):
             "traffic": traffic,
             "traffic_source": tprof if traffic else None,
             "kernel_us": round(kern_us, 3),
-            "kernel_timing": "HIP events around graph replays of R back-to-back launches",
+            "kernel_timing": (f"p50 of {trials} trials, each >= max(K, 100) launches as graph "
+                              "replays of R back-to-back launches, HIP events on the replay "
+                              "stream"),
             "algorithmic_bytes_per_launch": kbytes,
-            "probe_read_gbs": round(probe, 1),
+            "probe_read_gbs": round(probe, 1) if probe else None,
+            "probe_read_shape": (f"contiguous grid-stride read, {probe_grid} workgroups x 256 "
+                                 f"lanes, {probe_loads} non-temporal 16-byte loads in flight "
+                                 "per lane") if probe else None,
             "frac_of_probe": round(achieved / probe, 4) if probe else None,
+            "probe_paged_gbs": round(paged_probe, 1) if paged_probe else None,
+            "frac_of_paged_probe": round(achieved / paged_probe, 4) if paged_probe else None,
+        },
+        "timing": {
+            "trials": trials,
+            "steps_per_trial": R * max(1, math.ceil(max(K, 100) / R)),
+            "us_per_step_p10": round(pct(step_t, 10), 3),
+            "us_per_step_p50": round(pct(step_t, 50), 3),
+            "us_per_step_p90": round(pct(step_t, 90), 3),
+            "exactly_K_steps_us_per_step": round(k_region_us, 3),
+            "exactly_K_steps": "one graph of K consecutive steps, replayed once between two "
+                               "synchronizations, HIP events around the replay",
         },
         "eager_us_per_step": round(eager_step_us, 3),
         "three_launch_step_us": round(three_us, 3),
@@ -423,10 +573,12 @@ def run_headline(args):
         "unsplit_decode_us": round(unsplit_us, 3),
         "unsplit_decode_gbs": round(step_bytes / (unsplit_us * 1e-6) / 1e9, 1),
     }
+    if gate is not None:
+        res["kernel_gate"] = gate
+        if fused and gate.get("fused_kernel_traced_avg_us"):
+            res["roofline"]["kernel_traced_avg_us"] = gate["fused_kernel_traced_avg_us"]
     if not args.no_cpu:
-        gbs, sample = time_cpu_oracle(case, args.cpu_seconds)
-        res["cpu_baseline"] = {"value": round(gbs, 4), "unit": "GB/s", "cores": 1,
-                               "kind": "oracle", "sample": sample}
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     return res
 
 
@@ -837,16 +989,148 @@ def run_sweep(args):
             f.write(json.dumps(ln) + "\n")
 
 
+GATE_STEPS = 32
+
+
+def gate_expected(D, G, args):
+    """Kernel names one fused step and one three-launch step must launch, at
+    the library's default shapes (or the explicit ones)."""
+    dual = "true" if G <= 8 else "false"
+    ns_step = args.subtiles or 1
+    ns = args.subtiles or (2 if D == 64 else 1)
+    nw, depth = args.waves or 4, args.depth or 2
+    return {
+        "fused": [f"void pkv::attn_kernel<{D}, {ns_step}, {nw}, {depth}, 2, {dual}>"
+                  "(pkv::AttnParams)"],
+        "three_launch": ["pkv::append_kernel(pkv::AppendParams)",
+                         f"void pkv::attn_kernel<{D}, {ns}, {nw}, {depth}, 1, {dual}>"
+                         "(pkv::AttnParams)",
+                         f"void pkv::split_reduce_kernel<{D}>(pkv::ReduceParams)|"
+                         f"void pkv::split_reduce_rows_kernel<{D}>(pkv::ReduceParams)"],
+    }
+
+
+def run_gate_child(args):
+    """Under rocprofv3: GATE_STEPS fused steps, then GATE_STEPS three-launch
+    steps, eager, rotating over the headline's sets (so the traced durations
+    are of cold reads, as in the timed run)."""
+    import torch
+    import paged_kv_decode_cache_amd as pkv
+    import workloads
+    device = torch.device("cuda:0")
+    B, ctx, P = args.batch, args.ctx, args.partition
+    case = (workloads.sweep_case(B, ctx) if B in workloads.SWEEP_B and ctx in workloads.SWEEP_CTX
+            else workloads.sweep_case(B, ctx, seed=3999))
+    R = args.sets or max(2, math.ceil(4 * LLC_BYTES / case.kv_bytes()))
+    rot = Rotation(case, R, device)
+    q, kp, vp, cl, kn, vn = rot.q, rot.k_pool, rot.v_pool, rot.ctx, rot.k_new, rot.v_new
+    Pm = case.max_partitions(P)
+    ws = pkv.StepWorkspace(B, case.Hq, case.Hkv, case.D, Pm, device)
+    po = torch.empty_like(ws.partial_out)
+    pl = torch.empty_like(ws.partial_lse)
+    out = torch.empty((B, case.Hq, case.D), dtype=torch.float16, device=device)
+    launch = (dict(waves=args.waves, subtiles=args.subtiles, depth=args.depth)
+              if args.waves or args.subtiles or args.depth else None)
+    torch.cuda.synchronize()
+    for i in range(GATE_STEPS):
+        pkv.paged_decode_step(q, kp, vp, rot.bt[i % R], cl, case.scale, P, k_new=kn, v_new=vn,
+                              slot_mapping=rot.slots[i % R], workspace=ws, out=out,
+                              launch=launch)
+    for i in range(GATE_STEPS):
+        pkv.kv_cache_append(kp, vp, kn, vn, rot.slots[i % R])
+        pkv.paged_attention_decode_split(q, kp, vp, rot.bt[i % R], cl, case.scale, P, Pm, po, pl,
+                                         launch=launch)
+        pkv.split_reduce(po, pl, cl, P, out=out)
+    torch.cuda.synchronize()
+
+
+def run_kernel_gate(args):
+    """Run the gate child under rocprofv3 --kernel-trace --stats (before this
+    process touches the GPU) and check the library's kernels by name and
+    count: exactly GATE_STEPS launches of the fused kernel, GATE_STEPS of
+    each three-launch kernel, and no other kernel of the library."""
+    import csv
+    import shutil
+    import subprocess
+    import tempfile
+    prof = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
+    if args.no_gate or not os.path.exists(prof):
+        return {"status": "skipped", "reason": "--no-gate" if args.no_gate else
+                "rocprofv3 not found"}
+    base = os.path.join(ROOT, "gpurun_out")
+    out_dir = tempfile.mkdtemp(prefix="gate_", dir=base if os.path.isdir(base) else None)
+    cmd = [prof, "--kernel-trace", "--stats", "--output-format", "csv", "-d", out_dir, "-o",
+           "gate", "--", sys.executable, os.path.abspath(__file__), "--gate-child",
+           "--batch", str(args.batch), "--ctx", str(args.ctx), "--partition",
+           str(args.partition), "--waves", str(args.waves), "--subtiles", str(args.subtiles),
+           "--depth", str(args.depth), "--sets", str(args.sets)]
+    env = dict(os.environ, TMPDIR="/tmp")
+    try:
+        r = subprocess.run(cmd, cwd="/tmp", env=env, capture_output=True, text=True,
+                           timeout=240)
+        rc = r.returncode
+    except subprocess.TimeoutExpired:
+        return {"status": "fail", "reason": "rocprofv3 run timed out", "command": " ".join(cmd)}
+    stats = os.path.join(out_dir, "gate_kernel_stats.csv")
+    # rocprofv3 itself can end with a segmentation fault after the traced
+    # program has finished and its results are whole
+    if not os.path.exists(stats) or rc not in (0, -11, 139):
+        return {"status": "fail", "reason": f"rocprofv3 exit {rc}, stats present: "
+                                            f"{os.path.exists(stats)}",
+                "stderr_tail": (r.stderr or "")[-400:]}
+    observed = {}
+    for row in csv.DictReader(open(stats)):
+        observed[row["Name"]] = {"calls": int(row["Calls"]),
+                                 "average_us": round(float(row["AverageNs"]) / 1e3, 3)}
+    import workloads
+    case = workloads.sweep_case(args.batch, args.ctx) if (
+        args.batch in workloads.SWEEP_B and args.ctx in workloads.SWEEP_CTX) else None
+    Hq, Hkv, D = (case.Hq, case.Hkv, case.D) if case else (14, 2, 64)
+    want = gate_expected(D, Hq // Hkv, args)
+    problems = []
+    matched = set()
+    for path, names in want.items():
+        for alts in names:
+            hit = [n for n in alts.split("|") if n in observed]
+            calls = sum(observed[n]["calls"] for n in hit)
+            matched.update(hit)
+            if calls != GATE_STEPS:
+                problems.append(f"{path}: {alts} launched {calls} times, expected {GATE_STEPS}")
+    extra = [n for n in observed if n not in matched and ("pkv::" in n)]
+    if extra:
+        problems.append(f"unexpected library kernels: {extra}")
+    fused_name = want["fused"][0]
+    three = [n for alts in want["three_launch"] for n in alts.split("|") if n in observed]
+    return {
+        "status": "pass" if not problems else "fail",
+        "problems": problems,
+        "steps": GATE_STEPS,
+        "expected_per_step": {"fused": want["fused"], "three_launch": want["three_launch"]},
+        "observed": {n: v for n, v in observed.items() if "pkv::" in n},
+        "fused_kernel_traced_avg_us": observed.get(fused_name, {}).get("average_us"),
+        "three_launch_kernels_traced_sum_us": round(sum(observed[n]["average_us"]
+                                                        for n in three), 3),
+        "trace": "rocprofv3 --kernel-trace --stats of a child process, eager launches rotating "
+                 "over the same sets as the timed run",
+    }
+
+
 def main():
     args = parse()
+    if args.gate_child:
+        run_gate_child(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path "
-                                   "needs no collective, see DESIGN.md for how it would shard",
+                                   "shards with no collective, by sequence or KV head, one process per GPU",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.allocator:
         print(json.dumps(run_allocator(args)), flush=True)
         return
+    # the gate runs its child before this process initialises the GPU
+    headline = not (args.sweep or args.q8 or args.prefill)
+    gate = run_kernel_gate(args) if headline else None
     import torch
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
@@ -862,7 +1146,7 @@ def main():
             args.batch = 8
         print(json.dumps(run_prefill(args)), flush=True)
         return
-    print(json.dumps(run_headline(args)), flush=True)
+    print(json.dumps(run_headline(args, gate)), flush=True)
 
 
 if __name__ == "__main__":

@@ -55,7 +55,7 @@ What it computes, and where that comes from
   Its value is code * scale.  Attention over an 8-bit cache is the plain
   definition above applied to those values.
 
-Readings where the pages are silent (all listed in the design doc):
+Readings where the pages are silent:
 * GQA: query head h uses KV head ``h // (Hq // Hkv)`` (contiguous groups).
 * ``context_lens`` counts the attended positions, including the token the
   same step appended.

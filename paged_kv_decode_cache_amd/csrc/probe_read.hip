@@ -1,128 +1,130 @@
-// Streaming-read probe: reads a buffer once with 16-byte loads and writes
-// nothing (unless an XOR of everything it read hits one fixed pattern), so its
-// time measures the achievable HBM read bandwidth for a given byte count.  A
-// measurement aid for the benchmark, not part of the decode path.
+// Read-bandwidth probes for the benchmark: kernels that only read memory and
+// write nothing (unless an XOR of everything they read hits one fixed
+// pattern), so their time measures what a launch reading that many bytes can
+// achieve.  Measurement aids, not part of the decode path.
+//
+//   pkv_probe_stream_read   a contiguous buffer, grid-stride, U 16-byte
+//                           non-temporal loads in flight per lane: the plain
+//                           streaming-read ceiling for a byte count.
+//   pkv_probe_paged_read    the decode's own K/V access pattern with no
+//                           arithmetic: a workgroup per (sequence, KV head,
+//                           partition) of 4 waves, each wave reading its
+//                           16-token subtiles round-robin through the block
+//                           table, two subtiles in flight, whole 128-byte
+//                           head rows per 8 lanes, non-temporal.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace {
 
-__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* src, int64_t n16,
-                                                          uint4* sink) {
-  uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int U>
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src,
+                                                          int64_t n16, u32x4* sink) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc.x ^= a.x ^ b.x ^ c.x ^ d.x;
-    acc.y ^= a.y ^ b.y ^ c.y ^ d.y;
-    acc.z ^= a.z ^ b.z ^ c.z ^ d.z;
-    acc.w ^= a.w ^ b.w ^ c.w ^ d.w;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u];
   }
-  for (; i < n16; i += stride) {
-    const uint4 a = src[i];
-    acc.x ^= a.x;
-    acc.y ^= a.y;
-    acc.z ^= a.z;
-    acc.w ^= a.w;
-  }
-  if (acc.x == 0x9E3779B9u && acc.y == 0x7F4A7C15u && acc.z == 0x85EBCA6Bu &&
-      acc.w == 0xC2B2AE35u)
+  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+  if (acc[0] == 0x9E3779B9u && acc[1] == 0x7F4A7C15u && acc[2] == 0x85EBCA6Bu &&
+      acc[3] == 0xC2B2AE35u)
     sink[0] = acc;
 }
 
-// Paged-pattern read: the buffer is a pool of 128-byte head rows with two
-// heads interleaved (row r of head h at (2r + h) * 128 B), read in 16-row
-// subtiles of one head.
-//   mode 1: lane l reads row l % 16, bytes 16*(l/16) + 64m (the MFMA
-//           A-operand layout); adjacent waves of a workgroup read the two
-//           heads of the same rows.
-//   mode 2: as 1 but lane l reads row l / 8 + 8m, bytes 16*(l%8) (each
-//           128-byte row by 8 adjacent lanes).
-//   mode 3: as 1 but the two heads of a row go to adjacent workgroups (which
-//           the dispatcher places on different XCDs), like one workgroup per
-//           (sequence, KV head).
-//   mode +4: the same with non-temporal loads.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-template <bool NT>
-__device__ __forceinline__ uint4 ld16(const unsigned char* p) {
-  if (NT) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_uint4(v[0], v[1], v[2], v[3]);
-  }
-  return *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
-template <bool NT>
-__global__ __launch_bounds__(256) void paged_read_kernel(const unsigned char* src,
-                                                         int64_t n_subtiles, int mode,
-                                                         uint4* sink) {
-  const int lane = threadIdx.x & 63;
-  uint4 acc = make_uint4(0u, 0u, 0u, 0u);
-  int64_t wave, nwaves;
-  if (mode == 3) {
-    // workgroup pair (2k, 2k+1) reads rows of pair k, one head each
-    const int64_t pair = blockIdx.x >> 1;
-    const int64_t npairs = gridDim.x >> 1;
-    wave = pair * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    nwaves = npairs * (blockDim.x >> 6);
-  } else {
-    wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
-  }
-  const int64_t n_groups = n_subtiles >> 1;  // 16-row groups, both heads
-  for (int64_t s = wave; s < (mode == 3 ? n_groups : n_subtiles); s += nwaves) {
-    const int64_t h = mode == 3 ? (int64_t)(blockIdx.x & 1) : (s & 1);
-    const int64_t row0 = (mode == 3 ? s : (s >> 1)) * 16;
-    uint4 x[2];
+// head_dim 64, block_size 16: a subtile is one block's 16 rows of one head
+// (128 bytes each, rows Hkv * 128 bytes apart); lane l reads row 8m + l/8,
+// chunk l%8 of load m (m = 0, 1), as the decode kernels do.
+constexpr int kWaves = 4;
+
+__global__ __launch_bounds__(kWaves * 64) void paged_read_kernel(
+    const unsigned char* __restrict__ kp, const unsigned char* __restrict__ vp,
+    const int* __restrict__ bt, int max_blocks, int num_blocks, int Hkv, int ctx,
+    int partition_size, u32x4* sink) {
+  const int kvh = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = p * partition_size;
+  const int t1 = min(ctx, t0 + partition_size);
+  const int s_begin = t0 >> 4, s_end = (t1 + 15) >> 4;
+  const int row_bytes = Hkv * 128;
+  const int loff = (lane >> 3) * row_bytes + kvh * 128 + (lane & 7) * 16;
+  const int* row = bt + (size_t)b * max_blocks;
+  // the wave's block ids in one vector load (lane i: its i-th subtile), as
+  // the decode kernels request them ahead of the K/V
+  const int mine = s_begin + wave + kWaves * lane;
+  const int ids = mine < s_end ? row[mine] : 0;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int i0 = 0; s_begin + wave + kWaves * i0 < s_end; i0 += 2) {
+    u32x4 x[2][4];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      int64_t row, col;
-      if (mode == 2) {
-        row = row0 + (lane >> 3) + 8 * m;
-        col = 16 * (lane & 7);
-      } else {
-        row = row0 + (lane & 15);
-        col = 16 * (lane >> 4) + 64 * m;
+    for (int d = 0; d < 2; ++d) {
+      const int s = s_begin + wave + kWaves * (i0 + d);
+      const int blk = __builtin_amdgcn_readlane(ids, (i0 + d) & 63);
+      const bool ok = s < s_end && blk >= 0 && blk < num_blocks;
+      const auto kr = rsrc(kp + (size_t)(ok ? blk : 0) * 16 * row_bytes, ok ? 16 * row_bytes : 0);
+      const auto vr = rsrc(vp + (size_t)(ok ? blk : 0) * 16 * row_bytes, ok ? 16 * row_bytes : 0);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        x[d][m] = __builtin_amdgcn_raw_buffer_load_b128(kr, loff + m * 8 * row_bytes, 0, 2);
+        x[d][2 + m] = __builtin_amdgcn_raw_buffer_load_b128(vr, loff + m * 8 * row_bytes, 0, 2);
       }
-      x[m] = ld16<NT>(src + (2 * row + h) * 128 + col);
     }
-    acc.x ^= x[0].x ^ x[1].x;
-    acc.y ^= x[0].y ^ x[1].y;
-    acc.z ^= x[0].z ^ x[1].z;
-    acc.w ^= x[0].w ^ x[1].w;
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc ^= x[d][m];
   }
-  if (acc.x == 0x9E3779B9u && acc.y == 0x7F4A7C15u && acc.z == 0x85EBCA6Bu &&
-      acc.w == 0xC2B2AE35u)
+  if (acc[0] == 0x9E3779B9u && acc[1] == 0x7F4A7C15u && acc[2] == 0x85EBCA6Bu &&
+      acc[3] == 0xC2B2AE35u)
     sink[0] = acc;
 }
 
 }  // namespace
 
-// Reads `bytes` (a multiple of 4096) of src in the paged pattern `mode`.
-extern "C" int pkv_probe_paged_read(const void* src, int64_t bytes, void* sink, int grid,
-                                    int mode, void* stream) {
-  const int base_mode = mode & 3;
-  if (!src || !sink || bytes <= 0 || bytes % 4096 != 0 || grid <= 0 || grid % 2 != 0 ||
-      base_mode == 0 || mode > 7)
-    return -1;
-  if (mode & 4)
-    hipLaunchKernelGGL(paged_read_kernel<true>, dim3(grid), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const unsigned char*>(src),
-                       bytes / 2048, base_mode, static_cast<uint4*>(sink));
-  else
-    hipLaunchKernelGGL(paged_read_kernel<false>, dim3(grid), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const unsigned char*>(src),
-                       bytes / 2048, base_mode, static_cast<uint4*>(sink));
+// Reads `bytes` (a multiple of 16) of src: grid workgroups of 256 lanes,
+// loads_in_flight (4, 8 or 16) loads per lane.
+extern "C" int pkv_probe_stream_read(const void* src, int64_t bytes, void* sink, int grid,
+                                     int loads_in_flight, void* stream) {
+  if (!src || !sink || bytes <= 0 || bytes % 16 != 0 || grid <= 0) return -1;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const u32x4* s = static_cast<const u32x4*>(src);
+  u32x4* k = static_cast<u32x4*>(sink);
+  switch (loads_in_flight) {
+    case 4: hipLaunchKernelGGL(stream_read_kernel<4>, dim3(grid), dim3(256), 0, st, s, bytes / 16, k); break;
+    case 8: hipLaunchKernelGGL(stream_read_kernel<8>, dim3(grid), dim3(256), 0, st, s, bytes / 16, k); break;
+    case 16: hipLaunchKernelGGL(stream_read_kernel<16>, dim3(grid), dim3(256), 0, st, s, bytes / 16, k); break;
+    default: return -1;
+  }
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-extern "C" int pkv_probe_stream_read(const void* src, int64_t bytes, void* sink, int grid,
-                                     void* stream) {
-  if (!src || !sink || bytes <= 0 || bytes % 16 != 0 || grid <= 0) return -1;
-  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(src), bytes / 16,
-                     static_cast<uint4*>(sink));
+// The K/V read of a split pass over B sequences of ctx positions each (fp16
+// pools [num_blocks, 16, Hkv, 64], tables [B, max_blocks]), no arithmetic.
+extern "C" int pkv_probe_paged_read(const void* k_pool, const void* v_pool,
+                                    const int32_t* block_tables, int B, int Hkv, int ctx,
+                                    int num_blocks, int max_blocks, int partition_size,
+                                    void* sink, void* stream) {
+  if (!k_pool || !v_pool || !block_tables || !sink || B <= 0 || B > 65535 || Hkv <= 0 ||
+      ctx <= 0 || num_blocks <= 0 || max_blocks <= 0 || ctx > max_blocks * 16 ||
+      partition_size <= 0 || partition_size % 16 != 0 || partition_size > 16 * 64 * kWaves ||
+      (int64_t)16 * Hkv * 128 > INT32_MAX)
+    return -1;
+  const int parts = (ctx + partition_size - 1) / partition_size;
+  if (parts > 65535) return -1;
+  hipLaunchKernelGGL(paged_read_kernel, dim3(Hkv, parts, B), dim3(kWaves * 64), 0,
+                     static_cast<hipStream_t>(stream),
+                     static_cast<const unsigned char*>(k_pool),
+                     static_cast<const unsigned char*>(v_pool), block_tables, max_blocks,
+                     num_blocks, Hkv, ctx, partition_size, static_cast<u32x4*>(sink));
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }

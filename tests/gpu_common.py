@@ -34,18 +34,21 @@ def say(msg: str):
 @functools.lru_cache(maxsize=None)
 def case(name: str):
     """Cached generator call by name: 'tiny', 'qwen', 'sweep:B:ctx', 'skewed',
-    'long:B:ctx'."""
-    parts = name.split(":")
+    'long:B:ctx'; a '+fp32' suffix ('qwen+fp32', 'sweep:32:4096+fp32',
+    'long:1:32768+fp32') draws the values as fp32 normals rounded to fp16,
+    tails uncut."""
+    untr = name.endswith("+fp32")
+    parts = name[:-5].split(":") if untr else name.split(":")
     if parts[0] == "tiny":
         return workloads.tiny_case()
     if parts[0] == "qwen":
-        return workloads.qwen_case()
+        return workloads.qwen_case(untruncated=untr)
     if parts[0] == "sweep":
-        return workloads.sweep_case(int(parts[1]), int(parts[2]))
+        return workloads.sweep_case(int(parts[1]), int(parts[2]), untruncated=untr)
     if parts[0] == "skewed":
         return workloads.skewed_case()
     if parts[0] == "long":
-        return workloads.long_case(int(parts[1]), int(parts[2]))
+        return workloads.long_case(int(parts[1]), int(parts[2]), untruncated=untr)
     raise KeyError(name)
 
 

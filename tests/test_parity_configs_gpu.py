@@ -15,7 +15,9 @@ pytestmark = [pytest.mark.gpu, needs_gpu]
 
 CONFIGS = (["tiny", "qwen"]
            + [f"sweep:{B}:{c}" for B in workloads.SWEEP_B for c in workloads.SWEEP_CTX]
-           + ["skewed"] + [f"long:{B}:{c}" for B, c in workloads.LONG_POINTS])
+           + ["skewed"] + [f"long:{B}:{c}" for B, c in workloads.LONG_POINTS]
+           # values drawn as fp32 normals rounded to fp16, tails uncut
+           + ["qwen+fp32", "sweep:32:4096+fp32", "long:1:32768+fp32"])
 
 
 @pytest.mark.parametrize("name", CONFIGS)

@@ -4,7 +4,7 @@ This module only draws inputs: context lengths, block tables, fp16 K/V pools,
 queries, the new tokens' K/V and their slot mapping.  It holds none of the
 attention arithmetic; the oracle and the HIP path both consume what it returns.
 
-Recipe ("Input recipe"):
+Recipe:
 * ``numpy.random.default_rng(seed)`` (PCG64).  Draw order: lengths, block
   tables, K pool, V pool, q, k_new, v_new.
 * Values are N(0,1) in fp16, drawn by inverse-CDF sampling: each raw 64-bit
@@ -146,19 +146,29 @@ def _poison_unattended(pool, lens, bt, block_size):
     view[~used] = NAN16
 
 
+def _normal16_fp32(rng: np.random.Generator, shape) -> np.ndarray:
+    """N(0,1) fp16 values as fp32 standard normals rounded to fp16 (nearest
+    even): no cut on the tails, slower on the host than _normal16."""
+    return rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
+
+
 def make_case(name, *, B, Hq, Hkv, D, block_size, lens, num_blocks, seed, rng,
               scale=None, q_mult=1.0, partition_size=None, max_blocks=None,
-              poison=True) -> DecodeCase:
+              poison=True, untruncated=False) -> DecodeCase:
+    """untruncated: draw values as fp32 normals rounded to fp16 instead of
+    the inverse-CDF table (whose tails stop at |x| = 4.33)."""
+    draw = (lambda shape: _normal16_fp32(rng, shape)) if untruncated else \
+        (lambda shape: _normal16(rng, shape))
     lens = np.asarray(lens, dtype=np.int32)
     bt = _tables(rng, lens, block_size, num_blocks, max_blocks)
     shape = (num_blocks, block_size, Hkv, D)
-    k_pool = _normal16(rng, shape)
-    v_pool = _normal16(rng, shape)
-    q = _normal16(rng, (B, Hq, D))
+    k_pool = draw(shape)
+    v_pool = draw(shape)
+    q = draw((B, Hq, D))
     if q_mult != 1.0:
         q = (q.astype(np.float32) * np.float32(q_mult)).astype(np.float16)
-    k_new = _normal16(rng, (B, Hkv, D))
-    v_new = _normal16(rng, (B, Hkv, D))
+    k_new = draw((B, Hkv, D))
+    v_new = draw((B, Hkv, D))
     if poison:
         _poison_unattended(k_pool, lens, bt, block_size)
         _poison_unattended(v_pool, lens, bt, block_size)
@@ -187,14 +197,14 @@ def tiny_case(seed: int = 1000) -> DecodeCase:
                      max_blocks=4, partition_size=16)
 
 
-def qwen_case(seed: int = 2000) -> DecodeCase:
+def qwen_case(seed: int = 2000, untruncated: bool = False) -> DecodeCase:
     """Qwen2.5-0.5B attention shape: B=8, Hq=14, Hkv=2, D=64, bs=16,
     ctx ~ U{512..4096}, 4096-block pool."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(512, 4097, size=8).astype(np.int32)
     return make_case("qwen", B=8, Hq=14, Hkv=2, D=64, block_size=16, lens=lens,
                      num_blocks=4096, seed=seed, rng=rng, max_blocks=256,
-                     partition_size=512)
+                     partition_size=512, untruncated=untruncated)
 
 
 SWEEP_B = (1, 8, 32)
@@ -205,7 +215,7 @@ EXTRA_POINTS = ((64, 4096), (128, 4096), (32, 8192), (64, 8192), (128, 8192), (3
 
 
 def sweep_case(B: int, ctx: int, seed: Optional[int] = None,
-               partition_size: int = 512) -> DecodeCase:
+               partition_size: int = 512, untruncated: bool = False) -> DecodeCase:
     """Batch x context sweep point: Hq=14, Hkv=2, D=64, bs=16, equal lengths."""
     if seed is None:
         seed = 3000 + 5 * SWEEP_B.index(B) + SWEEP_CTX.index(ctx)
@@ -214,7 +224,7 @@ def sweep_case(B: int, ctx: int, seed: Optional[int] = None,
     nb = B * (-(-ctx // 16))
     return make_case(f"sweep_B{B}_ctx{ctx}", B=B, Hq=14, Hkv=2, D=64,
                      block_size=16, lens=lens, num_blocks=nb, seed=seed, rng=rng,
-                     partition_size=partition_size)
+                     partition_size=partition_size, untruncated=untruncated)
 
 
 def extra_case(B: int, ctx: int, partition_size: int = 512) -> DecodeCase:
@@ -244,7 +254,7 @@ LONG_POINTS = ((1, 32768), (1, 131072), (4, 32768), (4, 131072))
 
 
 def long_case(B: int, ctx: int, seed: Optional[int] = None,
-              partition_size: int = 512) -> DecodeCase:
+              partition_size: int = 512, untruncated: bool = False) -> DecodeCase:
     """Long-context split-K point: Hq=14, Hkv=2, D=64, bs=32, q x4."""
     if seed is None:
         seed = 5000 + LONG_POINTS.index((B, ctx))
@@ -253,7 +263,7 @@ def long_case(B: int, ctx: int, seed: Optional[int] = None,
     nb = B * (-(-ctx // 32))
     return make_case(f"long_B{B}_ctx{ctx}", B=B, Hq=14, Hkv=2, D=64,
                      block_size=32, lens=lens, num_blocks=nb, seed=seed, rng=rng,
-                     q_mult=4.0, partition_size=partition_size)
+                     q_mult=4.0, partition_size=partition_size, untruncated=untruncated)
 
 
 def custom_case(name, *, B, Hq, Hkv, D, block_size, lens, seed, num_blocks=None,
