@@ -659,15 +659,24 @@ __device__ __forceinline__ void merge_rows(__amdgpu_buffer_rsrc_t po_rs,
     const long long t_spin = __all(all_ok) ? 0 : (long long)__builtin_amdgcn_s_memrealtime();
     while (!__all(all_ok) &&
            (long long)__builtin_amdgcn_s_memrealtime() - t_spin < kSpinTicks) {
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);
       asm volatile("" ::: "memory");
+      // Every re-request is issued before any is waited for (one memory
+      // round trip per poll, not one per row); rows already seen go through
+      // the out-of-range offset.
+      f32x4 nx[BATCH];
+      float nl[BATCH];
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        nx[j] = load_coherent4(po_rs, ok[j] ? kOutOfRange : xo[j]);
+        nl[j] = load_coherent1(pl_rs, ok[j] ? kOutOfRange : lo[j]);
+      }
       all_ok = true;
 #pragma unroll
       for (int j = 0; j < BATCH; ++j) {
-        const f32x4 nx = load_coherent4(po_rs, ok[j] ? kOutOfRange : xo[j]);
-        const float nl = load_coherent1(pl_rs, ok[j] ? kOutOfRange : lo[j]);
-        x[j] = ok[j] ? x[j] : nx;
-        l[j] = ok[j] ? l[j] : nl;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x[j][v] = ok[j] ? x[j][v] : nx[j][v];
+        l[j] = ok[j] ? l[j] : nl[j];
         ok[j] = !other[j] || row_written(x[j], l[j]);
         all_ok = all_ok && ok[j];
       }
