@@ -278,24 +278,28 @@ int paged_attention_decode_split_ex(float* partial_out, float* partial_lse,
  *                     max_partitions * head_dim * 4 must be below 2^30
  *                     (else PKV_ERR_UNSUPPORTED).  Not to be shared with
  *                     paged_attention_decode_split, which leaves values there.
- *   counters          [B, num_kv_heads, 32] int32 workspace (one 128-byte
- *                     line per sequence and KV head, so tickets of different
- *                     pairs never contend for a line): must be zero before
- *                     the first call; every call leaves it zero.
+ *   counters          [B, num_kv_heads, 32] int32 workspace, 8-byte aligned
+ *                     (one 128-byte line per sequence and KV head, so
+ *                     tickets of different pairs never contend for a line):
+ *                     must be zero before the first call; every call leaves
+ *                     it zero.
  * Calls that share a workspace must be ordered by a stream; a call that
  * faults or is aborted leaves it undefined (initialise it again).
  * Other arguments as for paged_attention_decode_split.
  *
  * Each (sequence, KV head) with more than one non-empty partition is merged
- * in the launch by one of its workgroups: each takes a ticket from the pair's
- * counter early, the holder of the last ticket merges, and it reads the other
- * partitions' rows once none of their words is zero (device-coherent
- * accesses; the others never wait).  It sets the rows it read back to zero
- * and the counter back to zero.  Its wait is bounded in time (20 ms): a
- * workspace that breaks the contract above gives wrong numbers, not a
- * stalled queue.  A sequence that fits one partition is written directly.
- * Results equal append + split pass + split_reduce up to fp32 summation
- * order.
+ * in the launch by its workgroups: each takes a ticket from the pair's
+ * counter line early, and the holder of the last ticket merges, reading the
+ * other partitions' rows once none of their words is zero (device-coherent
+ * accesses; the others never wait).  Past 16 partitions the merge has two
+ * levels: the partitions form groups of about 8, the last ticket of each
+ * group merges the group into its own row, and the pair's last ticket
+ * merges the group results.  Mergers set the rows and words they read back
+ * to zero.  Their waits are bounded in time (20 ms): a workspace that breaks
+ * the contract above gives wrong numbers, not a stalled queue.  A sequence
+ * that fits one partition is written directly.  Results equal append +
+ * split pass + split_reduce up to fp32 summation order, and do not depend
+ * on which workgroups merge.
  */
 int paged_decode_step(void* out, float* lse_out,
                       void* k_pool, void* v_pool,

@@ -69,7 +69,7 @@ Shape pick_shape(int mode, int head_dim, const pkv_launch_config* c) {
   return s;
 }
 
-// MODE: 0 unsplit decode, 1 split pass, 2 fused decode step.  The grid of
+// MODE: 0 unsplit decode, 1 split pass, 2 and 3 fused decode step.  The grid of
 // the partitioned passes is (Hkv, max_partitions, B); of the unsplit pass
 // (B * Hkv).
 dim3 attn_grid(const AttnParams& p, int mode) {
@@ -153,29 +153,35 @@ void launch_compact(const AttnParams& p, int64_t wgs, hipStream_t st) {
                        0, st, p);
 }
 
-// The fused steps (fp16 and 8-bit) take 8 waves with many partitions per
-// (sequence, KV head) and a grid of at most one workgroup per CU: the
-// merging workgroup's walk over the partials is then the tail, and 8 waves
-// (twice the merge threads) shorten it when its threads at 4 waves would
-// hold more partition rows than one batch of loads (measured on the fp16
-// step at head_dim 64: B=1 x 32768 P=512 13.9 vs 16.3 us, B=1 x 131072
-// P=1024 25.3 vs 28.6 us; with one batch either way, or with more
-// workgroups than CUs, 4 waves stay faster).
+// The fused steps (fp16 and 8-bit) take 8 waves when the grid is at most
+// one workgroup per CU and either a pair has more than 16 partitions (few
+// workgroups stream long contexts, and the merges are large) or the merging
+// workgroup's threads at 4 waves would hold more partition rows than one
+// batch of loads (groups of 16 query heads).  With 16 partitions or fewer
+// and one batch, or with more workgroups than CUs, 4 waves stay faster.
 constexpr int64_t kStepWideMergeMaxGrid = 256;
 bool step_wide_merge(int head_dim, int64_t grid, int max_partitions, int group) {
-  if (head_dim != 64 || grid > kStepWideMergeMaxGrid) return false;
+  if (head_dim != 64 || grid > kStepWideMergeMaxGrid || max_partitions < 2) return false;
+  if (max_partitions > 16) return true;
   const int per_set = group * (64 / 4);  // merge threads per set of partitions (4 dims each)
   const int sets4 = per_set <= 4 * 64 ? 4 * 64 / per_set : 1;
   return (max_partitions + sets4 - 1) / sets4 > pkv::kMergeRowsInFlight;
 }
 
+// MODE: 0 unsplit, 1 split pass, 2 fused step; the fused step's launches
+// with more than kFlatMerge partitions per pair take MODE 3 (the two-level
+// merge), the others keep the one-level code.
 template <int MODE>
 int launch_attn(const AttnParams& p, int head_dim, const pkv_launch_config* cfg,
                 hipStream_t st) {
-  Shape s = pick_shape(MODE, head_dim, cfg);
+  if constexpr (MODE == 2) {
+    if (p.max_partitions > pkv::kFlatMerge) return launch_attn<3>(p, head_dim, cfg, st);
+  }
+  constexpr int SHAPE_MODE = MODE == 3 ? 2 : MODE;
+  Shape s = pick_shape(SHAPE_MODE, head_dim, cfg);
   if constexpr (MODE >= 1) {
-    Shape d = default_shape(MODE, head_dim);
-    if constexpr (MODE == 2) {
+    Shape d = default_shape(SHAPE_MODE, head_dim);
+    if constexpr (MODE >= 2) {
       const int64_t grid = (int64_t)p.B * p.Hkv * p.max_partitions;
       if (step_wide_merge(head_dim, grid, p.max_partitions, p.G)) {
         d.waves = 8;
@@ -190,7 +196,7 @@ int launch_attn(const AttnParams& p, int head_dim, const pkv_launch_config* cfg,
     if (p.B <= pkv::kCompactMaxB && same_shape &&
         (mode == 2 || (mode == 0 && wgs > kCompactAbove) || !direct_fits)) {
       if (head_dim == 64)
-        launch_compact<64, MODE == 2 ? 1 : 2, MODE>(p, wgs, st);
+        launch_compact<64, MODE >= 2 ? 1 : 2, MODE>(p, wgs, st);
       else
         launch_compact<128, 1, MODE>(p, wgs, st);
       return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
@@ -252,10 +258,11 @@ int launch_prefill(const pkv::PrefillParams& p, int64_t grid, hipStream_t st) {
 // tiles in flight; 2 subtiles per tile at head_dim 64 (1 at 128), except the
 // fused step, which takes 1 (as the fp16 step: 15.9 vs 16.8 us at
 // B=32 x 4096, 11.3 vs 11.45 us at B=8 x 4096, 0.6% slower at B=128 x 8192).
-// MODE: 0 unsplit, 1 split pass, 2 fused decode step.
+// MODE: 0 unsplit, 1 split pass, 2 fused decode step (3 with the two-level
+// merge).
 template <int D, int NW, int MODE>
 void launch_q8_nw(const pkv::Q8Params& p, int64_t grid, hipStream_t st) {
-  constexpr int NS = (D == 64 && MODE != 2) ? 2 : 1;
+  constexpr int NS = (D == 64 && MODE < 2) ? 2 : 1;
   if (p.a.G <= 8)
     hipLaunchKernelGGL((pkv::attn_q8_kernel<D, NS, NW, 2, MODE, true>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, st, p);
@@ -267,7 +274,10 @@ void launch_q8_nw(const pkv::Q8Params& p, int64_t grid, hipStream_t st) {
 // The fused step takes 8 waves where the fp16 step does (step_wide_merge).
 template <int D, int MODE>
 int launch_q8(const pkv::Q8Params& p, int64_t grid, hipStream_t st) {
-  if constexpr (MODE == 2 && D == 64) {
+  if constexpr (MODE == 2) {
+    if (p.a.max_partitions > pkv::kFlatMerge) return launch_q8<D, 3>(p, grid, st);
+  }
+  if constexpr (MODE >= 2 && D == 64) {
     if (step_wide_merge(D, grid, p.a.max_partitions, p.a.G))
       launch_q8_nw<D, 8, MODE>(p, grid, st);
     else
@@ -635,7 +645,7 @@ int paged_decode_step_ex(void* out, float* lse_out, void* k_pool, void* v_pool, 
                       num_blocks, max_blocks_per_seq, partition_size, max_partitions, scale);
   if (rc != PKV_OK || B == 0) return rc;
   if (!partial_out || !partial_lse || !counters) return PKV_ERR_INVALID_ARG;
-  if (!aligned(partial_out, 16) || !aligned(partial_lse, 4) || !aligned(counters, 4))
+  if (!aligned(partial_out, 16) || !aligned(partial_lse, 4) || !aligned(counters, 8))
     return PKV_ERR_INVALID_ARG;
   return launch_step(out, lse_out, k_pool, v_pool, q, k_new, v_new, slot_mapping, block_tables,
                      context_lens, partial_out, partial_lse, counters, B, num_q_heads,
@@ -885,7 +895,7 @@ int paged_decode_step_q8(void* out, float* lse_out, void* k_codes, void* v_codes
   if (B == 0) return PKV_OK;
   if (!out || !partial_out || !partial_lse || !counters) return PKV_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(partial_out, 16) || !aligned(partial_lse, 4) ||
-      !aligned(counters, 4) || (lse_out && !aligned(lse_out, 4)))
+      !aligned(counters, 8) || (lse_out && !aligned(lse_out, 4)))
     return PKV_ERR_INVALID_ARG;
   if (slot_mapping) {
     if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16) ||

@@ -53,6 +53,37 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kCounterStride = 32;
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// Merge groups of the fused step.  In the launches with more than
+// kFlatMerge partitions per (sequence, KV head), a pair with more than that
+// many merges in two levels: its np partitions form ng
+// groups of gs consecutive partitions (the last may be smaller); the last
+// workgroup of a group to take its ticket merges the group and stores the
+// result in its own partition's row, and the last workgroup of all merges
+// the group results.  Words 0-1 of the pair's counter line are one 64-bit
+// ticket word holding a w-bit count per group, so a single atomic tells a
+// workgroup both whether it closes its group and whether it closes the pair.
+// Word kGroupRowWord + k carries group k's result row (partition + 1) from
+// its merger to the pair's.  About 8 partitions per group, at most 16 groups
+// (fewer when the counts would not fit 64 bits).
+constexpr int kFlatMerge = 32;
+constexpr int kMaxMergeGroups = 16;
+constexpr int kGroupRowWord = 2;
+struct MergeGroups {
+  int ng;  // groups
+  int gs;  // partitions per group (the last group: np - (ng - 1) * gs)
+  int w;   // bits per group count in the ticket word
+};
+__host__ __device__ inline MergeGroups merge_groups(int np) {
+  if (np <= kFlatMerge) return MergeGroups{1, np, 32 - __builtin_clz((unsigned)(np | 1))};
+  int ng = (np + 7) / 8 < kMaxMergeGroups ? (np + 7) / 8 : kMaxMergeGroups;
+  for (;; --ng) {
+    const int gs = (np + ng - 1) / ng;
+    const int n = (np + gs - 1) / gs;  // groups in use (none empty)
+    const int w = 32 - __builtin_clz((unsigned)gs);  // counts 0 .. gs
+    if (n * w <= 64 || n == 1) return MergeGroups{n, gs, w};
+  }
+}
+
 struct AttnParams {
   const f16* q;
   const f16* k_pool;
@@ -75,8 +106,8 @@ struct AttnParams {
   const f16* k_new;     // [B, Hkv, D] the step's new token per sequence
   const f16* v_new;
   const int64_t* slot_mapping;  // [B] or null (no append)
-  int32_t* counters;    // [B, Hkv, kCounterStride] ticket counters (word 0 used), zero
-                        // between calls
+  int32_t* counters;    // [B, Hkv, kCounterStride] ticket words and group rows (8-byte
+                        // aligned), zero between calls
   float* lse_out;       // [B, Hq] or null
 };
 
@@ -623,20 +654,23 @@ constexpr int kMergeRowsInFlight = 8;  // the merge's largest batch of partition
 // started and waits on nothing).  s_memrealtime counts at 100 MHz: 20 ms.
 constexpr long long kSpinTicks = 2000000;
 
-// Streaming LSE merge of one thread's rows (partitions grp, grp + ngroups, ...
-// of head hh, dims 4cc..4cc+3) into (M, L, acc), BATCH rows in flight.
+// Streaming LSE merge of one thread's items (grp, grp + ngroups, ... of the
+// n items; item q is partial row rowtbl[q], or row0 + q without the table)
+// for head hh, dims 4cc..4cc+3, into (M, L, acc), BATCH rows in flight.
+// Item q_own is the merging workgroup's own partial (own_x, own_l), not read.
 template <int D, int BATCH>
 __device__ __forceinline__ void merge_rows(__amdgpu_buffer_rsrc_t po_rs,
-                                           __amdgpu_buffer_rsrc_t pl_rs, int Pm, int np,
-                                           int p_own, int grp, int ngroups, int hh, int cc,
-                                           f32x4 own_x, float own_l, float& M, float& L,
-                                           f32x4& acc) {
-  for (int q0 = grp; q0 < np; q0 += BATCH * ngroups) {
+                                           __amdgpu_buffer_rsrc_t pl_rs, int Pm, int n,
+                                           int q_own, const int* rowtbl, bool use_tbl, int row0,
+                                           int grp, int ngroups, int hh, int cc, f32x4 own_x,
+                                           float own_l, float& M, float& L, f32x4& acc) {
+  for (int q0 = grp; q0 < n; q0 += BATCH * ngroups) {
     // Straight-line code for the common case: every row of the batch is
-    // requested at once (rows past np, and the merger's own, through an
-    // out-of-range offset: zeros, no memory access), checked with one
-    // vector test, and merged with selects.  Rows not written yet are
-    // requested again in a wave-uniform loop, the only branch.
+    // requested at once (items past n, the merger's own, and rows outside
+    // [0, Pm) through an out-of-range offset: zeros, no memory access),
+    // checked with one vector test, and merged with selects.  Rows not
+    // written yet are requested again in a wave-uniform loop, the only
+    // branch.
     int xo[BATCH], lo[BATCH];
     f32x4 x[BATCH];
     float l[BATCH];
@@ -644,9 +678,13 @@ __device__ __forceinline__ void merge_rows(__amdgpu_buffer_rsrc_t po_rs,
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
       const int q = q0 + j * ngroups;
-      other[j] = q < np && q != p_own;
-      xo[j] = other[j] ? ((hh * Pm + q) * D + 4 * cc) * 4 : kOutOfRange;
-      lo[j] = other[j] ? (hh * Pm + q) * 4 : kOutOfRange;
+      other[j] = q < n && q != q_own;
+      // rows of the table come from other workgroups (checked); the others
+      // are partitions of this launch
+      const int r = use_tbl ? rowtbl[other[j] ? q : 0] : row0 + q;
+      const bool in = other[j] && (!use_tbl || (r >= 0 && r < Pm));
+      xo[j] = in ? ((hh * Pm + r) * D + 4 * cc) * 4 : kOutOfRange;
+      lo[j] = in ? (hh * Pm + r) * 4 : kOutOfRange;
       x[j] = load_coherent4(po_rs, xo[j]);
       l[j] = load_coherent1(pl_rs, lo[j]);
     }
@@ -684,16 +722,16 @@ __device__ __forceinline__ void merge_rows(__amdgpu_buffer_rsrc_t po_rs,
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
       const int q = q0 + j * ngroups;
-      const bool mine = q == p_own;
+      const bool mine = q == q_own;
       f32x4 xd;
 #pragma unroll
       for (int v = 0; v < 4; ++v) xd[v] = decode_partial(x[j][v]);
-      const float lq = q < np ? (mine ? own_l : decode_partial(l[j])) : -INFINITY;
+      const float lq = q < n ? (mine ? own_l : decode_partial(l[j])) : -INFINITY;
       const f32x4 xq = mine ? own_x : (other[j] ? xd : zero4f());
       const float Mn = fmaxf(M, lq);
       const float mu = Mn == -INFINITY ? 0.0f : Mn;
       const float sa = fast_exp2((M - mu) * kLog2e);  // 1 while M holds; 0 from -inf
-      const float sb = fast_exp2((lq - mu) * kLog2e);  // 0 for rows past np
+      const float sb = fast_exp2((lq - mu) * kLog2e);  // 0 for items past n
       acc = acc * sa + xq * sb;
       L = L * sa + sb;
       M = Mn;
@@ -701,99 +739,230 @@ __device__ __forceinline__ void merge_rows(__amdgpu_buffer_rsrc_t po_rs,
   }
 }
 
-// Cross-workgroup merge of the fused step, run by the merging workgroup of
-// (b, kvh) once its own partition (p_own, held in LDS at `own`) is final.
-// Threads cover (head, 4 dims) x partition groups with a streaming LSE merge,
-// and the groups combine through LDS.  Every other partition's row is polled
-// until none of its words is still unwritten, and set back to unwritten for
-// the next launch once the output is stored.
-// The wait ends: the other workgroups of the pair took their tickets before
-// this one took the last, so they are running and wait on nothing.
-template <int D, int NW>
-__device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int np, int p_own,
-                                      const float* own /* [16][D] o, then [16] lse */,
-                                      float* msm /* 6 * kMergeSlots floats */) {
+// The ticket word of (b, kvh) (words 0-1 of its counter line).
+__device__ __forceinline__ unsigned long long* step_ticket_word(const AttnParams& a, int b,
+                                                                int kvh) {
+  return reinterpret_cast<unsigned long long*>(a.counters +
+                                               ((size_t)b * a.Hkv + kvh) * kCounterStride);
+}
+// Partition p's ticket: the ticket word before its own count is added.
+// The groups are worked out here and again once the ticket is back, so that
+// nothing of them stays live across the K/V loop.
+// Launches with one level count in the word's low half only.
+template <bool TWO>
+__device__ __forceinline__ unsigned long long take_step_ticket(const AttnParams& a, int b,
+                                                               int kvh, int np, int p) {
+  if (!TWO)
+    return __hip_atomic_fetch_add(reinterpret_cast<unsigned*>(step_ticket_word(a, b, kvh)), 1u,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const MergeGroups mg = merge_groups(np);
+  return __hip_atomic_fetch_add(step_ticket_word(a, b, kvh), 1ull << (mg.w * (p / mg.gs)),
+                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// What partition p does once its ticket is back (thread 0): 0 stores its
+// partial; 1 merges its group and stores the result in its own row (whose
+// index it then publishes); 2 merges its group and then the pair (the pair's
+// last ticket: the ticket word goes back to zero at once, every ticket of
+// this launch being taken).
+template <bool TWO>
+__device__ __forceinline__ int step_merge_role(const AttnParams& a, int b, int kvh, int np,
+                                               int p, unsigned long long ticket) {
+  if (!TWO) {
+    if ((unsigned)ticket != (unsigned)(np - 1)) return 0;
+    __hip_atomic_store(reinterpret_cast<unsigned*>(step_ticket_word(a, b, kvh)), 0u,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return 2;
+  }
+  asm volatile("" : "+s"(np));  // recomputed, not kept from the ticket's request
+  const MergeGroups mg = merge_groups(np);
+  const int k = p / mg.gs;
+  const int gk = min(mg.gs, np - k * mg.gs);
+  const unsigned long long mask = (1ull << mg.w) - 1;
+  if ((int)((ticket >> (mg.w * k)) & mask) != gk - 1) return 0;
+  unsigned long long full = 0;
+  for (int j = 0; j < mg.ng; ++j)
+    full += (unsigned long long)min(mg.gs, np - j * mg.gs) << (mg.w * j);
+  if (ticket + (1ull << (mg.w * k)) == full) {
+    __hip_atomic_store(step_ticket_word(a, b, kvh), 0ull, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    return 2;
+  }
+  __hip_atomic_store(a.counters + ((size_t)b * a.Hkv + kvh) * kCounterStride + kGroupRowWord + k,
+                     p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return 1;
+}
+
+// The merges of the fused step by partition p of (b, kvh), whose role (1 or
+// 2, step_merge_role) says which: its group's, and for role 2 then the
+// pair's, over the group results (the group mergers' rows, polled from the
+// counter line; its own group's result stays in LDS).  With one group the
+// group's merge is the pair's.
+// Each merge covers n items (item q_own is the workgroup's own partial, in
+// LDS at `own`), every other item's row polled until none of its words is
+// still unwritten and set back to unwritten for the next launch once read.
+// Threads cover (head, 4 dims) x item groups with a streaming LSE merge, and
+// the item groups combine through LDS.  Results do not depend on which
+// workgroups merge: items are merged in partition, then group, order.
+// The waits end: the workgroups whose rows are read took their tickets
+// before this one took its last, so they are running and wait on nothing.
+template <int D, int NW, bool TWO>
+__device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int np, int p,
+                                      int role, float* own /* [16][D] o, then [16] lse */,
+                                      float* msm /* 6 * kMergeSlots floats */,
+                                      int* rowtbl /* kMaxMergeGroups */) {
   constexpr int NT = NW * 64;
   constexpr int TPR = D / 4;
   const int t = threadIdx.x;
   const int G = a.G;
   const int Pm = a.max_partitions;
-  const int per_group = G * TPR;
-  const int ngroups = per_group <= NT ? NT / per_group : 1;
-  const int nslots = per_group * ngroups;
   const size_t head0 = (size_t)b * a.Hq + kvh * G;
   const __amdgpu_buffer_rsrc_t po_rs = buffer_rsrc(a.partial_out + head0 * Pm * D, G * Pm * D * 4);
   const __amdgpu_buffer_rsrc_t pl_rs = buffer_rsrc(a.partial_lse + head0 * Pm, G * Pm * 4);
+  if (TWO) asm volatile("" : "+s"(np));  // recomputed, not kept from the ticket's request
+  const MergeGroups mg = TWO ? merge_groups(np) : MergeGroups{1, np, 0};
+  const int k = TWO ? p / mg.gs : 0;
+  const int lo = k * mg.gs;
+  int32_t* rows_w = a.counters + ((size_t)b * a.Hkv + kvh) * kCounterStride + kGroupRowWord;
+
+  // The first merge: the whole pair (one group), or this workgroup's group.
+  // out: 0 the step's output, 1 the group result into this partition's row,
+  // 2 the group result into LDS (then the merge of the groups).
+  const bool flat = !TWO || mg.ng == 1;
+  int n = flat ? np : min(mg.gs, np - lo);
+  int q_own = flat ? p : p - lo;
+  int row0 = flat ? 0 : lo;
+  bool use_tbl = false;
+  int out = flat ? 0 : role;
+
+  // Pair merger: request the other groups' result rows now, so they arrive
+  // with the first batch of its group's rows.
+  int rid = 0;
+  if (TWO && out == 2 && t < mg.ng && t != k)
+    rid = __hip_atomic_load(rows_w + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  const int per_group = G * TPR;
+  const int ngroups = per_group <= NT ? NT / per_group : 1;
+  const int nslots = per_group * ngroups;
   const f32x4 unwritten4 = zero4f();
-  for (int slot = t; slot < nslots; slot += NT) {
-    const int grp = slot / per_group;
-    const int hc = slot % per_group;
-    const int hh = hc / TPR;
-    const int cc = hc % TPR;
-    const f32x4 own_x = *reinterpret_cast<const f32x4*>(own + hh * D + 4 * cc);
-    const float own_l = own[16 * D + hh];
-    float M = -INFINITY, L = 0.0f;
-    f32x4 acc = zero4f();
-    // rows in flight per thread: its share of the pair's partitions, 2 to 8
-    const int rows = (np + ngroups - 1) / ngroups;
-    if (rows <= 2)
-      merge_rows<D, 2>(po_rs, pl_rs, Pm, np, p_own, grp, ngroups, hh, cc, own_x, own_l, M, L, acc);
-    else if (rows <= 4)
-      merge_rows<D, 4>(po_rs, pl_rs, Pm, np, p_own, grp, ngroups, hh, cc, own_x, own_l, M, L, acc);
-    else
-      merge_rows<D, kMergeRowsInFlight>(po_rs, pl_rs, Pm, np, p_own, grp, ngroups, hh, cc, own_x,
-                                        own_l, M, L, acc);
-    // Back to "not written" for the next launch: this thread's data words as
-    // soon as its last slot's rows are read (no load of this call follows
-    // them then, and loads and stores count down one in-order counter); the
-    // lse words, which every thread of a head reads, after the barrier below.
-    if (slot + NT >= nslots) {
-      for (int s2 = t; s2 <= slot; s2 += NT) {
-        const int g2 = s2 / per_group;
-        const int h2 = (s2 % per_group) / TPR;
-        const int c2 = (s2 % per_group) % TPR;
-        for (int q = g2; q < np; q += ngroups)
-          if (q != p_own) store_coherent4(po_rs, ((h2 * Pm + q) * D + 4 * c2) * 4, unwritten4);
+  for (;;) {
+    auto row_of = [&](int q) { return TWO && use_tbl ? rowtbl[q] : row0 + q; };
+    for (int slot = t; slot < nslots; slot += NT) {
+      const int grp = slot / per_group;
+      const int hc = slot % per_group;
+      const int hh = hc / TPR;
+      const int cc = hc % TPR;
+      const f32x4 own_x = *reinterpret_cast<const f32x4*>(own + hh * D + 4 * cc);
+      const float own_l = own[16 * D + hh];
+      float M = -INFINITY, L = 0.0f;
+      f32x4 acc = zero4f();
+      // rows in flight per thread: its share of the items, 2 to 8
+      const int rows = (n + ngroups - 1) / ngroups;
+      if (rows <= 2)
+        merge_rows<D, 2>(po_rs, pl_rs, Pm, n, q_own, rowtbl, TWO && use_tbl, row0, grp, ngroups,
+                         hh, cc, own_x, own_l, M, L, acc);
+      else if (rows <= 4)
+        merge_rows<D, 4>(po_rs, pl_rs, Pm, n, q_own, rowtbl, TWO && use_tbl, row0, grp, ngroups,
+                         hh, cc, own_x, own_l, M, L, acc);
+      else
+        merge_rows<D, kMergeRowsInFlight>(po_rs, pl_rs, Pm, n, q_own, rowtbl, TWO && use_tbl,
+                                          row0, grp, ngroups, hh, cc, own_x, own_l, M, L, acc);
+      // Back to "not written" for the next launch: this thread's data words
+      // as soon as its last slot's rows are read (no load of this merge
+      // follows them then, and loads and stores count down one in-order
+      // counter); the lse words, which every thread of a head reads, after
+      // the barrier below.
+      if (slot + NT >= nslots) {
+        for (int s2 = t; s2 <= slot; s2 += NT) {
+          const int g2 = s2 / per_group;
+          const int h2 = (s2 % per_group) / TPR;
+          const int c2 = (s2 % per_group) % TPR;
+          for (int q = g2; q < n; q += ngroups) {
+            const int r = row_of(q);
+            if (q != q_own && (!use_tbl || (r >= 0 && r < Pm)))
+              store_coherent4(po_rs, ((h2 * Pm + r) * D + 4 * c2) * 4, unwritten4);
+          }
+        }
+      }
+      float* rr = msm + 6 * slot;
+      rr[0] = M;
+      rr[1] = L;
+      rr[2] = acc[0];
+      rr[3] = acc[1];
+      rr[4] = acc[2];
+      rr[5] = acc[3];
+    }
+    __syncthreads();
+    for (int i = t; i < G * n; i += NT) {
+      const int q = i % n;
+      const int r = row_of(q);
+      if (q != q_own && (!use_tbl || (r >= 0 && r < Pm)))
+        store_coherent1(pl_rs, ((i / n) * Pm + r) * 4, 0.0f);
+    }
+    for (int hc = t; hc < per_group; hc += NT) {
+      float M = -INFINITY;
+      for (int gi = 0; gi < ngroups; ++gi) M = fmaxf(M, msm[6 * (gi * per_group + hc)]);
+      const float mu = M == -INFINITY ? 0.0f : M;
+      float L = 0.0f;
+      f32x4 acc = zero4f();
+      for (int gi = 0; gi < ngroups; ++gi) {
+        const float* rr = msm + 6 * (gi * per_group + hc);
+        const float e = fast_exp2((rr[0] - mu) * kLog2e);
+        L += e * rr[1];
+        acc[0] += e * rr[2];
+        acc[1] += e * rr[3];
+        acc[2] += e * rr[4];
+        acc[3] += e * rr[5];
+      }
+      const int hh = hc / TPR;
+      const int cc = hc % TPR;
+      const float inv = recip_or_zero(L);
+      if (!TWO || out == 0) {
+        const int h = kvh * G + hh;
+        f16x4 o;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[v] = (f16)(acc[v] * inv);
+        *reinterpret_cast<f16x4*>(a.out + ((size_t)b * a.Hq + h) * D + 4 * cc) = o;
+        if (a.lse_out != nullptr && cc == 0)
+          a.lse_out[(size_t)b * a.Hq + h] = L > 0.0f ? M + logf(L) : -INFINITY;
+      } else {
+        // the group's result as a partial: normalised o and its lse
+        f32x4 x;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x[v] = acc[v] * inv;
+        const float lse = L > 0.0f ? M + logf(L) : -INFINITY;
+        if (out == 2) {
+          *reinterpret_cast<f32x4*>(own + hh * D + 4 * cc) = x;
+          if (cc == 0) own[16 * D + hh] = lse;
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) x[v] = encode_partial(x[v]);
+          store_coherent4(po_rs, ((hh * Pm + p) * D + 4 * cc) * 4, x);
+          if (cc == 0) store_coherent1(pl_rs, (hh * Pm + p) * 4, encode_partial(lse));
+        }
       }
     }
-    float* r = msm + 6 * slot;
-    r[0] = M;
-    r[1] = L;
-    r[2] = acc[0];
-    r[3] = acc[1];
-    r[4] = acc[2];
-    r[5] = acc[3];
-  }
-  __syncthreads();
-  for (int i = t; i < G * np; i += NT) {
-    const int q = i % np;
-    if (q != p_own)
-      store_coherent1(pl_rs, ((i / np) * Pm + q) * 4, 0.0f);
-  }
-  for (int hc = t; hc < per_group; hc += NT) {
-    float M = -INFINITY;
-    for (int gi = 0; gi < ngroups; ++gi) M = fmaxf(M, msm[6 * (gi * per_group + hc)]);
-    const float mu = M == -INFINITY ? 0.0f : M;
-    float L = 0.0f;
-    f32x4 acc = zero4f();
-    for (int gi = 0; gi < ngroups; ++gi) {
-      const float* r = msm + 6 * (gi * per_group + hc);
-      const float e = fast_exp2((r[0] - mu) * kLog2e);
-      L += e * r[1];
-      acc[0] += e * r[2];
-      acc[1] += e * r[3];
-      acc[2] += e * r[4];
-      acc[3] += e * r[5];
+    if (!TWO || out != 2) return;
+
+    // The group results' rows; the words go back to zero for the next launch.
+    if (t < mg.ng) {
+      if (t == k) {
+        rowtbl[t] = p;
+      } else {
+        const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
+        while (rid == 0 && (long long)__builtin_amdgcn_s_memrealtime() - t0 < kSpinTicks) {
+          __builtin_amdgcn_s_sleep(1);
+          rid = __hip_atomic_load(rows_w + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __hip_atomic_store(rows_w + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        rowtbl[t] = rid - 1;  // -1 after a broken contract: read as zeros, never written
+      }
     }
-    const int h = kvh * a.G + hc / TPR;
-    const int cc = hc % TPR;
-    const float inv = recip_or_zero(L);
-    f16x4 o;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) o[v] = (f16)(acc[v] * inv);
-    *reinterpret_cast<f16x4*>(a.out + ((size_t)b * a.Hq + h) * D + 4 * cc) = o;
-    if (a.lse_out != nullptr && cc == 0)
-      a.lse_out[(size_t)b * a.Hq + h] = L > 0.0f ? M + logf(L) : -INFINITY;
+    __syncthreads();  // own holds the group's result; rowtbl is complete
+    n = mg.ng;
+    q_own = k;
+    row0 = 0;
+    use_tbl = true;
+    out = 0;
   }
 }
 
@@ -802,6 +971,8 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
 // MODE 2: fused decode step: the split pass plus, in the same launch, the
 //         step's cache write and the LSE merge of each (sequence, KV head)
 //         by one of its workgroups.
+// MODE 3: MODE 2 with the two-level merge (merge_groups), for launches with
+//         more than kFlatMerge partitions per pair.
 //
 // Fused-step hand-off.  Each workgroup of a (b, kvh) with more than one
 // partition takes a ticket from the pair's counter early (its latency hides
@@ -820,7 +991,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   constexpr int KC = D / 32;   // QK MFMAs (16x16x32) per subtile
   constexpr int NDB = D / 16;  // PV MFMA column blocks (16 dims each)
   constexpr bool SPLIT = MODE >= 1;
-  constexpr bool STEP = MODE == 2;
+  constexpr bool STEP = MODE >= 2;
+  constexpr bool TWO = MODE == 3;
   using SM = LineSmem<D, NS>;
   using LM = LineMap<D>;
 
@@ -975,10 +1147,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   }
   // Fused step: the ticket (issued after the first K/V requests; waited for
   // only at the end).
-  int ticket = 0;
-  if (STEP && n_parts > 1 && threadIdx.x == 0)
-    ticket = __hip_atomic_fetch_add(a.counters + ((size_t)b * Hkv + kvh) * kCounterStride, 1,
-                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  unsigned long long ticket = 0;
+  if (STEP && n_parts > 1 && threadIdx.x == 0) ticket = take_step_ticket<TWO>(a, b, kvh, n_parts, p);
   for (int u0 = 0; u0 < n_tiles; u0 += DEPTH) {
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) {
@@ -1005,18 +1175,12 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   // wave merge reads it from those lanes only).
   const float l_tot = NW == 1 ? __shfl(st.lsum[0], g) : st.lsum[0];
 
-  // Fused step: publish whether this workgroup merges (its ticket is the
-  // pair's last), before the barriers of the wave merge; the merger resets
-  // the counter at once (every ticket of this launch is taken).
+  // Fused step: publish whether and what this workgroup merges (its ticket
+  // closes its group, or the pair), before the barriers of the wave merge.
   __shared__ int s_merge;
   __shared__ __attribute__((aligned(16))) float own[STEP ? 16 * D + 16 : 4];
-  if (STEP && n_parts > 1 && threadIdx.x == 0) {
-    const bool m = ticket == n_parts - 1;
-    if (m)
-      __hip_atomic_store(a.counters + ((size_t)b * Hkv + kvh) * kCounterStride, 0,
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_merge = m;
-  }
+  if (STEP && n_parts > 1 && threadIdx.x == 0)
+    s_merge = step_merge_role<TWO>(a, b, kvh, n_parts, p, ticket);
   if (NW == 1 && STEP) __syncthreads();
 
   // Fused step: the append of the new token's row of this head (after the
@@ -1083,7 +1247,8 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   if (!STEP || n_parts <= 1 || !s_merge) return;
   __syncthreads();  // the merger's own partial is complete in LDS
   __shared__ float msm[6 * kMergeSlots];
-  merge_step_partitions<D, NW>(a, b, kvh, n_parts, p, own, msm);
+  __shared__ int rowtbl[kMaxMergeGroups];
+  merge_step_partitions<D, NW, TWO>(a, b, kvh, n_parts, p, s_merge, own, msm, rowtbl);
 }
 
 // Direct grid.  Unsplit decode: one workgroup per (sequence, KV head),
@@ -1140,7 +1305,7 @@ __global__ __launch_bounds__(NW * 64) void attn_compact_kernel(const AttnParams 
     int ctx = a.context_lens[j];
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
     int n = (ctx + a.partition_size - 1) / a.partition_size;
-    if (MODE == 2 && n == 0) n = 1;
+    if (MODE >= 2 && n == 0) n = 1;
     prefix[j] = n;  // the count for now; each thread touches its own indices only
     local += n;
   }

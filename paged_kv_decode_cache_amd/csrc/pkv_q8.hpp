@@ -371,14 +371,16 @@ __device__ __forceinline__ void consume_tile8(KVTile8<D, NS>& T, SoftmaxState<D>
 // launch, the quantising cache write of each sequence's new token and the
 // merge of each (sequence, KV head) by the holder of its last ticket, with
 // the fp16 step's hand-off (device-coherent partial rows polled until
-// written; merge_step_partitions).
+// written; merge_step_partitions).  MODE 3: MODE 2 with the two-level merge
+// of launches with more than kFlatMerge partitions per pair.
 template <int D, int NS, int NW, int DEPTH, int MODE, bool DUAL>
 __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   constexpr int KC = D / 32;
   constexpr int NDB = D / 16;
   constexpr int DC = D / 64;  // 16-code chunks per lane and row
   constexpr bool SPLIT = MODE >= 1;
-  constexpr bool STEP = MODE == 2;
+  constexpr bool STEP = MODE >= 2;
+  constexpr bool TWO = MODE == 3;
   using SM = AttnSmem<D, NS>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[NW * SM::kWaveBytes];
   const AttnParams& a = P.a;
@@ -496,10 +498,8 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   }
   // Fused step: the ticket (issued after the first K/V requests; waited for
   // only at the end).
-  int ticket = 0;
-  if (STEP && n_parts > 1 && threadIdx.x == 0)
-    ticket = __hip_atomic_fetch_add(a.counters + ((size_t)b * Hkv + kvh) * kCounterStride, 1,
-                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  unsigned long long ticket = 0;
+  if (STEP && n_parts > 1 && threadIdx.x == 0) ticket = take_step_ticket<TWO>(a, b, kvh, n_parts, p);
   for (int u0 = 0; u0 < n_tiles; u0 += DEPTH) {
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) {
@@ -525,17 +525,12 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   float l_tot = lsum + __shfl_xor(lsum, 16);
   l_tot += __shfl_xor(l_tot, 32);
 
-  // Fused step: whether this workgroup merges (its ticket is the pair's
-  // last); the merger resets the counter at once (every ticket is taken).
+  // Fused step: whether and what this workgroup merges (its ticket closes
+  // its group, or the pair).
   __shared__ int s_merge;
   __shared__ __attribute__((aligned(16))) float own[STEP ? 16 * D + 16 : 4];
-  if (STEP && n_parts > 1 && threadIdx.x == 0) {
-    const bool m = ticket == n_parts - 1;
-    if (m)
-      __hip_atomic_store(a.counters + ((size_t)b * Hkv + kvh) * kCounterStride, 0,
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_merge = m;
-  }
+  if (STEP && n_parts > 1 && threadIdx.x == 0)
+    s_merge = step_merge_role<TWO>(a, b, kvh, n_parts, p, ticket);
   if (NW == 1 && STEP) __syncthreads();
 
   // Fused step: the new token's codes and scale of this head, at (block,
@@ -608,7 +603,8 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   if (!STEP || n_parts <= 1 || !s_merge) return;
   __syncthreads();  // the merger's own partial is complete in LDS
   __shared__ float msm[6 * kMergeSlots];
-  merge_step_partitions<D, NW>(a, b, kvh, n_parts, p, own, msm);
+  __shared__ int rowtbl[kMaxMergeGroups];
+  merge_step_partitions<D, NW, TWO>(a, b, kvh, n_parts, p, s_merge, own, msm, rowtbl);
 }
 
 }  // namespace pkv

@@ -326,3 +326,48 @@ def test_step_wide_merge_large_group():
     torch.cuda.synchronize()
     check_fp16(out4, want, "step G=16 at 4 waves")
 
+
+
+# Partition counts around every shape of the two-level merge: one level up
+# to 16 partitions, then groups of about 8 (17 -> 3 groups of 6/6/5, 128 ->
+# 16 groups of 8, 129 -> 16 groups of 9 with a last group of 4, 256 -> 12
+# groups of 22 with a last of 14, 1000 -> 9 groups of 112 with a last of 104).
+TWO_LEVEL_NP = [1, 2, 15, 16, 17, 18, 23, 24, 25, 33, 64, 65, 127, 128, 129, 200, 255, 256,
+                257, 1000]
+
+
+@pytest.mark.parametrize("P,launch", [(16, None), (64, None), (16, dict(waves=8)),
+                                      (64, dict(grid="compact"))])
+def test_step_two_level_merge_group_shapes(P, launch):
+    """Sequences whose partition counts cross every group boundary of the
+    two-level merge (ragged last partitions), against the oracle's append +
+    decode, twice on one workspace (other queries and lengths the second
+    time); every call leaves the workspace zero, and a repeated call gives
+    bit-identical outputs."""
+    rng = np.random.default_rng(160)
+    nps = [n for n in TWO_LEVEL_NP if n * P <= 16000 or n == 1000 and P == 16]
+    lens = [max(1, n * P - int(rng.integers(0, P))) for n in nps]
+    c = workloads.custom_case(f"step_two_level_P{P}", B=len(lens), Hq=14, Hkv=2, D=64,
+                              block_size=16, lens=lens, seed=161, q_mult=2.0)
+    say(f"step two-level merge P={P} launch={launch} partitions={nps}")
+    g = to_gpu(c)
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    out, lse = _step(g, c, P, ws, launch=launch)
+    torch.cuda.synchronize()
+    want, want_lse, kp, vp = _oracle_step(c)
+    check_fp16(out, want, f"two-level P={P}")
+    _check_lse(lse, want_lse)
+    assert np.array_equal(g.k_pool.cpu().numpy().view(np.uint16), kp.view(np.uint16))
+    _check_workspace_restored(ws)
+    # shorter contexts and new queries: other group shapes on the same workspace
+    q2 = (rng.standard_normal(c.q.shape) * 2.0).astype(np.float16)
+    ctx2 = np.maximum(c.context_lens - rng.integers(0, 4 * P, c.B), 0).astype(np.int32)
+    g.q = torch.from_numpy(q2).to(g.q.device)
+    g.ctx = torch.from_numpy(ctx2).to(g.q.device)
+    out2 = _step(g, c, P, ws, append=False, want_lse=False, launch=launch).clone()
+    out3 = _step(g, c, P, ws, append=False, want_lse=False, launch=launch)
+    torch.cuda.synchronize()
+    want2 = ref.paged_attention_decode(q2, kp, vp, c.block_tables, ctx2, c.scale)
+    check_fp16(out2, want2, f"two-level P={P} second call")
+    assert torch.equal(out2.view(torch.int16), out3.view(torch.int16))
+    _check_workspace_restored(ws)
