@@ -947,6 +947,12 @@ def run_sweep(args):
 
         us_unsplit = time_it(lambda i: pkv.paged_attention_decode(
             rot.q, rot.k_pool, rot.v_pool, rot.bt[i % R], rot.ctx, case.scale, out=out))
+
+        def append_unsplit(i):
+            pkv.kv_cache_append(rot.k_pool, rot.v_pool, rot.k_new, rot.v_new, rot.slots[i % R])
+            pkv.paged_attention_decode(rot.q, rot.k_pool, rot.v_pool, rot.bt[i % R], rot.ctx,
+                                       case.scale, out=out)
+        us_append_unsplit = time_it(append_unsplit)
         best = None
         best_step = None
         for P in (128, 256, 512, 1024, 2048, 4096):
@@ -965,9 +971,13 @@ def run_sweep(args):
             def fused(i):
                 pkv.paged_decode_step(rot.q, rot.k_pool, rot.v_pool, rot.bt[i % R], rot.ctx,
                                       case.scale, P, workspace=ws, out=out)
+            def three(i, split=split):
+                pkv.kv_cache_append(rot.k_pool, rot.v_pool, rot.k_new, rot.v_new, rot.slots[i % R])
+                split(i)
+
             us = time_it(split)
             if best is None or us < best[1]:
-                best = (P, us)
+                best = (P, us, time_it(three))
             us = time_it(fused)
             if best_step is None or us < best_step[1]:
                 best_step = (P, us)
@@ -978,6 +988,8 @@ def run_sweep(args):
                 "unsplit_gbs": round(nbytes / us_unsplit / 1e3, 1),
                 "split_best_partition": best[0], "split_us": round(best[1], 3),
                 "split_gbs": round(nbytes / best[1] / 1e3, 1),
+                "append_split_merge_us": round(best[2], 3),
+                "append_unsplit_us": round(us_append_unsplit, 3),
                 "fused_best_partition": best_step[0], "fused_us": round(best_step[1], 3),
                 "fused_gbs": round(nbytes / best_step[1] / 1e3, 1)}
         print(json.dumps(line), flush=True)
