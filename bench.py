@@ -68,6 +68,8 @@ def parse():
     ap.add_argument("--depth", type=int, default=0, help="split pass tiles in flight (0=default)")
     ap.add_argument("--sets", type=int, default=0, help="rotation sets (0 = auto, >= 4x LLC)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-large", action="store_true",
+                    help="skip the fused step at the larger B x ctx points")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", default="", help="write the full sweep as JSON lines to this file")
     ap.add_argument("--path", choices=("step", "split"), default="step",
@@ -577,9 +579,58 @@ def run_headline(args, gate=None):
         res["kernel_gate"] = gate
         if fused and gate.get("fused_kernel_traced_avg_us"):
             res["roofline"]["kernel_traced_avg_us"] = gate["fused_kernel_traced_avg_us"]
+    if not args.no_large and (B, ctx, P) == (32, 4096, 1024):
+        del g_fused, g_three, g_split, g_uns, rot, ws, po, pl
+        torch.cuda.empty_cache()
+        res["large_points"] = time_large_points(trials, K, device)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     return res
+
+
+# Larger points of the sweep's shapes inside B >= 32, ctx >= 4096, each with the
+# fused step's best partition size in the sweep.
+LARGE_POINTS = ((64, 8192, 4096), (128, 8192, 4096), (256, 8192, 4096))
+
+
+def time_large_points(trials, K, device):
+    """The fused step at LARGE_POINTS, timed as the headline (rotation over
+    >= 4x the Infinity Cache, graph replays, p50 of the trials)."""
+    import torch
+    import paged_kv_decode_cache_amd as pkv
+    import workloads
+    out_lines = []
+    for B, ctx, P in LARGE_POINTS:
+        case = workloads.extra_case(B, ctx)
+        R = max(2, math.ceil(4 * LLC_BYTES / case.kv_bytes()))
+        rot = Rotation(case, R, device)
+        ws = pkv.StepWorkspace(B, case.Hq, case.Hkv, case.D, case.max_partitions(P), device)
+        out = torch.empty((B, case.Hq, case.D), dtype=torch.float16, device=device)
+
+        def step(i, rot=rot, ws=ws, out=out, case=case, P=P, R=R):
+            r = i % R
+            pkv.paged_decode_step(rot.q, rot.k_pool, rot.v_pool, rot.bt[r], rot.ctx, case.scale,
+                                  P, k_new=rot.k_new, v_new=rot.v_new, slot_mapping=rot.slots[r],
+                                  workspace=ws, out=out)
+        for i in range(2 * R):
+            step(i)
+        torch.cuda.synchronize()
+        g = capture([lambda r=r: step(r) for r in range(R)])
+        t = time_trials(g, R, K, trials)
+        ctx_sum = int(case.context_lens.astype(np.int64).sum())
+        nbytes = alg_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D) + append_bytes(B, case.Hkv,
+                                                                                 case.D)
+        us = pct(t, 50)
+        out_lines.append({"B": B, "ctx": ctx, "partition_size": P, "rotation_sets": R,
+                          "algorithmic_bytes_per_step": nbytes,
+                          "us_per_step_p10": round(pct(t, 10), 3),
+                          "us_per_step_p50": round(us, 3),
+                          "us_per_step_p90": round(pct(t, 90), 3),
+                          "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                          "pct_of_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / PEAK_GBS, 2)})
+        del g, rot, ws, out
+        torch.cuda.empty_cache()
+    return out_lines
 
 
 PREFILL_METRIC = "chunked prefill attention: achieved TFLOP/s (% of fp16 MFMA peak) and µs/call"
