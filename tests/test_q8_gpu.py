@@ -398,3 +398,30 @@ def test_q8_step_wide_merge_large_group():
     fin = np.isfinite(want_lse)
     assert float(np.abs(g_lse[fin] - want_lse[fin]).max()) <= PARTIAL_ATOL
 
+
+
+def test_q8_step_two_level_merge_g16_d128():
+    """The 8-bit step's two-level merge with groups of 16 heads at head_dim
+    128 (partition counts 17..200 at P=32), against the oracle's 8-bit append
+    + decode; the cache write bit-exact and the workspace zero afterwards."""
+    rng = np.random.default_rng(180)
+    P = 32
+    nps = [1, 17, 33, 64, 129, 200]
+    lens = [max(1, n * P - int(rng.integers(0, P))) for n in nps]
+    c = workloads.custom_case("q8_step_two_level_g16", B=len(lens), Hq=32, Hkv=2, D=128,
+                              block_size=16, lens=lens, seed=181)
+    kc, vc, ks, vs = workloads.q8_pools(c)
+    g = to_gpu(c)
+    gq = _gpu_q8(kc, vc, ks, vs)
+    say(f"q8 step two-level G=16 D=128 P={P} partitions={nps}")
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    out, lse = _step_q8(g, gq, c, P, ws)
+    torch.cuda.synchronize()
+    want_pools = ref.kv_cache_append_q8(kc, vc, ks, vs, c.k_new, c.v_new, c.slot_mapping)
+    _check_pools_q8(gq, want_pools)
+    want, want_lse = _oracle_decode_q8(c, *want_pools)
+    check_fp16(out, want, "q8 step two-level G=16 D=128")
+    g_lse = host64(lse)
+    fin = np.isfinite(want_lse)
+    assert float(np.abs(g_lse[fin] - want_lse[fin]).max()) <= PARTIAL_ATOL
+    _check_workspace_restored(ws)

@@ -371,3 +371,28 @@ def test_step_two_level_merge_group_shapes(P, launch):
     check_fp16(out2, want2, f"two-level P={P} second call")
     assert torch.equal(out2.view(torch.int16), out3.view(torch.int16))
     _check_workspace_restored(ws)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,bs", [(32, 2, 64, 16), (32, 2, 128, 16), (16, 4, 128, 32)])
+def test_step_two_level_merge_other_shapes(Hq, Hkv, D, bs):
+    """The two-level merge with groups of 16 heads (no dual columns; at
+    head_dim 128 one merge thread set spans the whole workgroup) and with
+    head_dim 128 at block size 32: partition counts on both sides of the
+    group boundaries, against the oracle's append + decode, workspace zero
+    afterwards."""
+    P = 2 * bs
+    rng = np.random.default_rng(170 + D + Hq)
+    nps = [1, 17, 33, 64, 129, 200]
+    lens = [max(1, n * P - int(rng.integers(0, P))) for n in nps]
+    c = workloads.custom_case(f"step_two_level_G{Hq // Hkv}_D{D}", B=len(lens), Hq=Hq, Hkv=Hkv,
+                              D=D, block_size=bs, lens=lens, seed=171, q_mult=2.0)
+    say(f"step two-level Hq={Hq} Hkv={Hkv} D={D} bs={bs} P={P} partitions={nps}")
+    g = to_gpu(c)
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    out, lse = _step(g, c, P, ws)
+    torch.cuda.synchronize()
+    want, want_lse, kp, _ = _oracle_step(c)
+    check_fp16(out, want, f"two-level G={Hq // Hkv} D={D}")
+    _check_lse(lse, want_lse)
+    assert np.array_equal(g.k_pool.cpu().numpy().view(np.uint16), kp.view(np.uint16))
+    _check_workspace_restored(ws)
