@@ -192,11 +192,12 @@ def test_step_other_shapes(Hq, Hkv, D, bs):
     _check_lse(lse, want_lse)
 
 
-def test_step_in_hip_graph_replays():
+@pytest.mark.parametrize("name,P", [("sweep:32:1024", 256), ("long:1:32768", 512)])
+def test_step_in_hip_graph_replays(name, P):
     """The step is capture-safe: replays of a captured step, with eager work
-    and synchronisation between them, all equal the eager result."""
-    c = case("sweep:32:1024")
-    P = 256
+    and synchronisation between them, all equal the eager result (one-level
+    merge, and the two-level merge at 64 partitions per pair)."""
+    c = case(name)
     g = to_gpu(c)
     ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
     out = torch.empty((c.B, c.Hq, c.D), dtype=torch.float16, device=g.q.device)
