@@ -34,7 +34,10 @@ def _noalloc(g, c, P, out, lse):
 
 
 @pytest.mark.parametrize("calls", [(("qwen", 256), ("tiny", 16)),
-                                   (("sweep:32:4096", 1024), ("sweep:8:512", 128))])
+                                   (("sweep:32:4096", 1024), ("sweep:8:512", 128)),
+                                   # the two-level merge (64 partitions per pair), then a
+                                   # smaller one-level call on the same scratch
+                                   (("long:1:32768", 512), ("qwen", 256))])
 def test_noalloc_step_equals_workspace_step(calls):
     for name, P in calls:
         c = case(name)
