@@ -397,3 +397,34 @@ def test_step_two_level_merge_other_shapes(Hq, Hkv, D, bs):
     _check_lse(lse, want_lse)
     assert np.array_equal(g.k_pool.cpu().numpy().view(np.uint16), kp.view(np.uint16))
     _check_workspace_restored(ws)
+
+
+def test_step_two_level_merge_stress_against_three_launch_path():
+    """20 fused steps on one workspace with new queries and random context
+    lengths at P=64 (1..100 partitions per sequence, so the launches switch
+    between the one- and two-level merges and every group shape), each
+    against the append-free three-launch path, the workspace zero after each."""
+    rng = np.random.default_rng(190)
+    lens = rng.integers(1, 6401, 12).tolist()
+    c = workloads.custom_case("step_two_level_stress", B=12, Hq=14, Hkv=2, D=64, block_size=16,
+                              lens=lens, seed=191, max_blocks=400)
+    P = 64
+    g = to_gpu(c)
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    gen = torch.Generator(device=g.q.device).manual_seed(192)
+    cpu_gen = torch.Generator().manual_seed(193)
+    worst = 0.0
+    for it in range(20):
+        g.q = torch.randn(g.q.shape, generator=gen, device=g.q.device).to(torch.float16)
+        g.ctx = torch.randint(0, 400 * 16 + 1, (c.B,), generator=cpu_gen,
+                              dtype=torch.int32).to(g.q.device)
+        if it % 5 == 0:
+            g.ctx[0] = 400 * 16  # a launch with 100 partitions on one pair
+        fused = _step(g, c, P, ws, append=False, want_lse=False)
+        po, pl = pkv.paged_attention_decode_split(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale,
+                                                  P)
+        ref3 = pkv.split_reduce(po, pl, g.ctx, P)
+        torch.cuda.synchronize()
+        worst = max(worst, (fused.float() - ref3.float()).abs().max().item())
+        _check_workspace_restored(ws)
+    assert worst <= 2e-3, worst
