@@ -1133,9 +1133,13 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   // DEPTH-slot software pipeline over the wave's tiles: up to DEPTH tiles of
   // K/V are in flight while one is consumed.  The block ids of tile u+DEPTH
   // are requested right after the K/V of tile u, so the in-order wait for
-  // them only ever waits for tiles already consumed.  Loads past the wave's
-  // last tile go through empty resources (no memory access), so every
-  // iteration issues the same loads.
+  // them only ever waits for tiles already consumed.  The loop runs while a
+  // tile remains to be requested, and every iteration issues the same loads
+  // (past the wave's last tile through empty resources: no memory access), so
+  // the waits inside it stay partial.  The tiles still in flight after it are
+  // consumed with no further requests: requests past the end would still
+  // return through the memory pipeline, and the code after the loop waits for
+  // all of them (0.15-0.5 us per step measured).
   const int n_tiles = s_first < sub_end ? (sub_end - s_first + TSTEP - 1) / TSTEP : 0;
   KVTile<D, NS> buf[DEPTH];
 #pragma unroll
@@ -1149,19 +1153,24 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   // only at the end).
   unsigned long long ticket = 0;
   if (STEP && n_parts > 1 && threadIdx.x == 0) ticket = take_step_ticket<TWO>(a, b, kvh, n_parts, p);
-  for (int u0 = 0; u0 < n_tiles; u0 += DEPTH) {
+  int u0 = 0;
+  for (; u0 + DEPTH < n_tiles; u0 += DEPTH) {
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) {
       const int u = u0 + i;
-      if (u < n_tiles)
-        consume_tile<D, NS, DUAL, STEP>(buf[i], st, qb, stage, c, t_end, lane, ones, rem_mul,
-                                        s_new, tok_new, slot, new_off, a.block_size, kn, vn);
+      consume_tile<D, NS, DUAL, STEP>(buf[i], st, qb, stage, c, t_end, lane, ones, rem_mul,
+                                      s_new, tok_new, slot, new_off, a.block_size, kn, vn);
       load_kv_lines<D, NS>(buf[i], a, ids[i], s_first + (u + DEPTH) * TSTEP, sub_end, t_end,
                            spb, spb_shift, tok_stride, kvh, lane_off, s_new);
       ids[i] = load_block_ids<NS>(bt_rs, s_first + (u + 2 * DEPTH) * TSTEP, sub_end, spb,
                                   spb_shift, lane);
     }
   }
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i)
+    if (u0 + i < n_tiles)
+      consume_tile<D, NS, DUAL, STEP>(buf[i], st, qb, stage, c, t_end, lane, ones, rem_mul,
+                                      s_new, tok_new, slot, new_off, a.block_size, kn, vn);
 
   // DUAL: fold the remainder columns (8..15) into the head columns (0..7).
   if (DUAL) {

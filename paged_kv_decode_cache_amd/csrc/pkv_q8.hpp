@@ -486,6 +486,8 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   float lsum = 0.0f;
   f16* stage = reinterpret_cast<f16*>(smem + wave * SM::kWaveBytes);
 
+  // The fp16 kernel's pipeline: the loop runs while a tile remains to be
+  // requested, then the tiles in flight are consumed with no more requests.
   const int n_tiles = s_first < sub_end ? (sub_end - s_first + TSTEP - 1) / TSTEP : 0;
   KVTile8<D, NS> buf[DEPTH];
 #pragma unroll
@@ -500,20 +502,26 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   // only at the end).
   unsigned long long ticket = 0;
   if (STEP && n_parts > 1 && threadIdx.x == 0) ticket = take_step_ticket<TWO>(a, b, kvh, n_parts, p);
-  for (int u0 = 0; u0 < n_tiles; u0 += DEPTH) {
+  int u0 = 0;
+  for (; u0 + DEPTH < n_tiles; u0 += DEPTH) {
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) {
       const int u = u0 + i;
-      if (u < n_tiles)
-        consume_tile8<D, NS, DUAL, STEP>(buf[i], st, lsum, qb, stage, c, t_end, lane, rem_mul,
-                                         s_new, tok_new, slot, new_off, a.block_size, kq, vq,
-                                         ksc, vsc);
+      consume_tile8<D, NS, DUAL, STEP>(buf[i], st, lsum, qb, stage, c, t_end, lane, rem_mul,
+                                       s_new, tok_new, slot, new_off, a.block_size, kq, vq,
+                                       ksc, vsc);
       load_kv_tile8<D, NS>(buf[i], P, ids[i], s_first + (u + DEPTH) * TSTEP, sub_end, t_end,
                            spb, spb_shift, kvh, lane, s_new);
       ids[i] = load_block_ids<NS>(bt_rs, s_first + (u + 2 * DEPTH) * TSTEP, sub_end, spb,
                                   spb_shift, lane);
     }
   }
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i)
+    if (u0 + i < n_tiles)
+      consume_tile8<D, NS, DUAL, STEP>(buf[i], st, lsum, qb, stage, c, t_end, lane, rem_mul,
+                                       s_new, tok_new, slot, new_off, a.block_size, kq, vq,
+                                       ksc, vsc);
 
   if (DUAL) {
 #pragma unroll

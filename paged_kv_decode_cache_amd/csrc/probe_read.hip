@@ -52,7 +52,11 @@ __global__ __launch_bounds__(kWaves * 64) void paged_read_kernel(
     const int* __restrict__ bt, int max_blocks, int num_blocks, int Hkv, int ctx,
     int partition_size, u32x4* sink) {
   const int kvh = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // The wave index must be known to be wave-uniform: taken straight from
+  // threadIdx it is a vector value, the bounds check below becomes per-lane,
+  // and each load of the second subtile turns into a readfirstlane loop over
+  // its buffer resource (measured 13.4 against 12.0 us at 32 x 4096).
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = p * partition_size;
   const int t1 = min(ctx, t0 + partition_size);
   const int s_begin = t0 >> 4, s_end = (t1 + 15) >> 4;
