@@ -493,8 +493,8 @@ def run_headline(args, gate=None):
         ms_per_step = fused_us * 1e-3
         kern_us = fused_us
         kbytes = step_bytes + app_bytes
-        kname = (f"void pkv::attn_kernel<{case.D}, {ns_step}, {nw}, {depth}, 2, {dual}>"
-                 "(pkv::AttnParams)")
+        kname = (f"void pkv::attn_kernel<{case.D}, {ns_step}, {nw}, {depth}, "
+                 f"{step_mode(case.max_partitions(P))}, {dual}>(pkv::AttnParams)")
         step_desc = "paged_decode_step (append + split pass + merge in one launch)"
     else:
         ms_per_step = three_us * 1e-3
@@ -1055,7 +1055,14 @@ def run_sweep(args):
 GATE_STEPS = 32
 
 
-def gate_expected(D, G, args):
+def step_mode(max_partitions):
+    """The fused step's kernel instantiation as the library picks it by
+    partitions per pair: the two-level merge past 32 (MODE 3), the direct
+    merge at 4 or fewer (MODE 4), else the merge through LDS (MODE 2)."""
+    return 3 if max_partitions > 32 else (4 if max_partitions <= 4 else 2)
+
+
+def gate_expected(D, G, Pm, args):
     """Kernel names one fused step and one three-launch step must launch, at
     the library's default shapes (or the explicit ones)."""
     dual = "true" if G <= 8 else "false"
@@ -1063,7 +1070,7 @@ def gate_expected(D, G, args):
     ns = args.subtiles or (2 if D == 64 else 1)
     nw, depth = args.waves or 4, args.depth or 2
     return {
-        "fused": [f"void pkv::attn_kernel<{D}, {ns_step}, {nw}, {depth}, 2, {dual}>"
+        "fused": [f"void pkv::attn_kernel<{D}, {ns_step}, {nw}, {depth}, {step_mode(Pm)}, {dual}>"
                   "(pkv::AttnParams)"],
         "three_launch": ["pkv::append_kernel(pkv::AppendParams)",
                          f"void pkv::attn_kernel<{D}, {ns}, {nw}, {depth}, 1, {dual}>"
@@ -1149,7 +1156,8 @@ def run_kernel_gate(args):
     case = workloads.sweep_case(args.batch, args.ctx) if (
         args.batch in workloads.SWEEP_B and args.ctx in workloads.SWEEP_CTX) else None
     Hq, Hkv, D = (case.Hq, case.Hkv, case.D) if case else (14, 2, 64)
-    want = gate_expected(D, Hq // Hkv, args)
+    Pm = case.max_partitions(args.partition) if case else -(-args.ctx // args.partition)
+    want = gate_expected(D, Hq // Hkv, Pm, args)
     problems = []
     matched = set()
     for path, names in want.items():

@@ -170,14 +170,18 @@ bool step_wide_merge(int head_dim, int64_t grid, int max_partitions, int group) 
 
 // MODE: 0 unsplit, 1 split pass, 2 fused step; the fused step's launches
 // with more than kFlatMerge partitions per pair take MODE 3 (the two-level
-// merge), the others keep the one-level code.
+// merge), those with at most kDirectMergeItems MODE 4 (the direct merge),
+// the others keep the one-level code with the merge through LDS.  Each is
+// its own instantiation: merge code a launch does not use still costs the
+// kernel registers and time.
 template <int MODE>
 int launch_attn(const AttnParams& p, int head_dim, const pkv_launch_config* cfg,
                 hipStream_t st) {
   if constexpr (MODE == 2) {
     if (p.max_partitions > pkv::kFlatMerge) return launch_attn<3>(p, head_dim, cfg, st);
+    if (p.max_partitions <= pkv::kDirectMergeItems) return launch_attn<4>(p, head_dim, cfg, st);
   }
-  constexpr int SHAPE_MODE = MODE == 3 ? 2 : MODE;
+  constexpr int SHAPE_MODE = MODE >= 2 ? 2 : MODE;
   Shape s = pick_shape(SHAPE_MODE, head_dim, cfg);
   if constexpr (MODE >= 1) {
     Shape d = default_shape(SHAPE_MODE, head_dim);

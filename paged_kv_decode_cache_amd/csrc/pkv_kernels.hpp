@@ -647,6 +647,12 @@ __device__ __forceinline__ void merge_waves_impl(const SoftmaxState<D>& st, floa
 
 constexpr int kMergeSlots = 512;  // >= 16 heads x 128/4 dims
 constexpr int kMergeRowsInFlight = 8;  // the merge's largest batch of partition rows per thread
+// One-level fused-step launches with at most this many partitions per pair
+// take MODE 4: each merging thread takes every partition of its (head,
+// 4 dims) in one batch and writes the output itself, with no LDS staging and
+// no barrier (measured faster at 4 partitions, slower at 8, and slower
+// everywhere when both merges share one instantiation).
+constexpr int kDirectMergeItems = 4;
 // The merger's wait for the other workgroups' rows is bounded in time: a
 // workspace that breaks its contract (rows reset under a running writer, a
 // stale counter) costs at most this long and gives wrong numbers, never a
@@ -801,15 +807,18 @@ __device__ __forceinline__ int step_merge_role(const AttnParams& a, int b, int k
 // LDS at `own`), every other item's row polled until none of its words is
 // still unwritten and set back to unwritten for the next launch once read.
 // Threads cover (head, 4 dims) x item groups with a streaming LSE merge, and
-// the item groups combine through LDS.  Results do not depend on which
+// the item groups combine through LDS; with DIRECT (one level, at most
+// kDirectMergeItems items), one thread takes every item of its (head,
+// 4 dims) and writes the result itself.  Results do not depend on which
 // workgroups merge: items are merged in partition, then group, order.
 // The waits end: the workgroups whose rows are read took their tickets
 // before this one took its last, so they are running and wait on nothing.
-template <int D, int NW, bool TWO>
+template <int D, int NW, bool TWO, bool DIRECT = false>
 __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int np, int p,
                                       int role, float* own /* [16][D] o, then [16] lse */,
                                       float* msm /* 6 * kMergeSlots floats */,
                                       int* rowtbl /* kMaxMergeGroups */) {
+  static_assert(!(TWO && DIRECT), "the direct merge is one-level");
   constexpr int NT = NW * 64;
   constexpr int TPR = D / 4;
   const int t = threadIdx.x;
@@ -841,80 +850,14 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
     rid = __hip_atomic_load(rows_w + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   const int per_group = G * TPR;
-  const int ngroups = per_group <= NT ? NT / per_group : 1;
+  const int ngroups = !DIRECT && per_group <= NT ? NT / per_group : 1;
   const int nslots = per_group * ngroups;
   const f32x4 unwritten4 = zero4f();
   for (;;) {
     auto row_of = [&](int q) { return TWO && use_tbl ? rowtbl[q] : row0 + q; };
-    for (int slot = t; slot < nslots; slot += NT) {
-      const int grp = slot / per_group;
-      const int hc = slot % per_group;
-      const int hh = hc / TPR;
-      const int cc = hc % TPR;
-      const f32x4 own_x = *reinterpret_cast<const f32x4*>(own + hh * D + 4 * cc);
-      const float own_l = own[16 * D + hh];
-      float M = -INFINITY, L = 0.0f;
-      f32x4 acc = zero4f();
-      // rows in flight per thread: its share of the items, 2 to 8
-      const int rows = (n + ngroups - 1) / ngroups;
-      if (rows <= 2)
-        merge_rows<D, 2>(po_rs, pl_rs, Pm, n, q_own, rowtbl, TWO && use_tbl, row0, grp, ngroups,
-                         hh, cc, own_x, own_l, M, L, acc);
-      else if (rows <= 4)
-        merge_rows<D, 4>(po_rs, pl_rs, Pm, n, q_own, rowtbl, TWO && use_tbl, row0, grp, ngroups,
-                         hh, cc, own_x, own_l, M, L, acc);
-      else
-        merge_rows<D, kMergeRowsInFlight>(po_rs, pl_rs, Pm, n, q_own, rowtbl, TWO && use_tbl,
-                                          row0, grp, ngroups, hh, cc, own_x, own_l, M, L, acc);
-      // Back to "not written" for the next launch: this thread's data words
-      // as soon as its last slot's rows are read (no load of this merge
-      // follows them then, and loads and stores count down one in-order
-      // counter); the lse words, which every thread of a head reads, after
-      // the barrier below.
-      if (slot + NT >= nslots) {
-        for (int s2 = t; s2 <= slot; s2 += NT) {
-          const int g2 = s2 / per_group;
-          const int h2 = (s2 % per_group) / TPR;
-          const int c2 = (s2 % per_group) % TPR;
-          for (int q = g2; q < n; q += ngroups) {
-            const int r = row_of(q);
-            if (q != q_own && (!use_tbl || (r >= 0 && r < Pm)))
-              store_coherent4(po_rs, ((h2 * Pm + r) * D + 4 * c2) * 4, unwritten4);
-          }
-        }
-      }
-      float* rr = msm + 6 * slot;
-      rr[0] = M;
-      rr[1] = L;
-      rr[2] = acc[0];
-      rr[3] = acc[1];
-      rr[4] = acc[2];
-      rr[5] = acc[3];
-    }
-    __syncthreads();
-    for (int i = t; i < G * n; i += NT) {
-      const int q = i % n;
-      const int r = row_of(q);
-      if (q != q_own && (!use_tbl || (r >= 0 && r < Pm)))
-        store_coherent1(pl_rs, ((i / n) * Pm + r) * 4, 0.0f);
-    }
-    for (int hc = t; hc < per_group; hc += NT) {
-      float M = -INFINITY;
-      for (int gi = 0; gi < ngroups; ++gi) M = fmaxf(M, msm[6 * (gi * per_group + hc)]);
-      const float mu = M == -INFINITY ? 0.0f : M;
-      float L = 0.0f;
-      f32x4 acc = zero4f();
-      for (int gi = 0; gi < ngroups; ++gi) {
-        const float* rr = msm + 6 * (gi * per_group + hc);
-        const float e = fast_exp2((rr[0] - mu) * kLog2e);
-        L += e * rr[1];
-        acc[0] += e * rr[2];
-        acc[1] += e * rr[3];
-        acc[2] += e * rr[4];
-        acc[3] += e * rr[5];
-      }
-      const int hh = hc / TPR;
-      const int cc = hc % TPR;
+    // The merged value of (hh, cc): the step's output, the group's result
+    // into this partition's row, or the group's result into LDS.
+    auto finish = [&](int hh, int cc, float M, float L, f32x4 acc) {
       const float inv = recip_or_zero(L);
       if (!TWO || out == 0) {
         const int h = kvh * G + hh;
@@ -940,6 +883,90 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
           if (cc == 0) store_coherent1(pl_rs, (hh * Pm + p) * 4, encode_partial(lse));
         }
       }
+    };
+    for (int slot = t; slot < nslots; slot += NT) {
+      const int grp = slot / per_group;
+      const int hc = slot % per_group;
+      const int hh = hc / TPR;
+      const int cc = hc % TPR;
+      const f32x4 own_x = *reinterpret_cast<const f32x4*>(own + hh * D + 4 * cc);
+      const float own_l = own[16 * D + hh];
+      float M = -INFINITY, L = 0.0f;
+      f32x4 acc = zero4f();
+      if constexpr (DIRECT) {
+        merge_rows<D, kDirectMergeItems>(po_rs, pl_rs, Pm, n, q_own, rowtbl, false, row0, 0, 1,
+                                         hh, cc, own_x, own_l, M, L, acc);
+        // Back to "not written" for the next launch.  The threads that read
+        // a head's lse words are TPR consecutive lanes of one wave, all past
+        // their loads here, so its first lane resets them.
+        for (int q = 0; q < n; ++q) {
+          if (q == q_own) continue;
+          store_coherent4(po_rs, ((hh * Pm + row0 + q) * D + 4 * cc) * 4, unwritten4);
+          if (cc == 0) store_coherent1(pl_rs, (hh * Pm + row0 + q) * 4, 0.0f);
+        }
+        finish(hh, cc, M, L, acc);
+      } else {
+        // rows in flight per thread: its share of the items, 2 to 8
+        const int rows = (n + ngroups - 1) / ngroups;
+        if (rows <= 2)
+          merge_rows<D, 2>(po_rs, pl_rs, Pm, n, q_own, rowtbl, TWO && use_tbl, row0, grp,
+                           ngroups, hh, cc, own_x, own_l, M, L, acc);
+        else if (rows <= 4)
+          merge_rows<D, 4>(po_rs, pl_rs, Pm, n, q_own, rowtbl, TWO && use_tbl, row0, grp,
+                           ngroups, hh, cc, own_x, own_l, M, L, acc);
+        else
+          merge_rows<D, kMergeRowsInFlight>(po_rs, pl_rs, Pm, n, q_own, rowtbl, TWO && use_tbl,
+                                            row0, grp, ngroups, hh, cc, own_x, own_l, M, L, acc);
+        // Back to "not written" for the next launch: this thread's data words
+        // as soon as its last slot's rows are read (no load of this merge
+        // follows them then, and loads and stores count down one in-order
+        // counter); the lse words, which every thread of a head reads, after
+        // the barrier below.
+        if (slot + NT >= nslots) {
+          for (int s2 = t; s2 <= slot; s2 += NT) {
+            const int g2 = s2 / per_group;
+            const int h2 = (s2 % per_group) / TPR;
+            const int c2 = (s2 % per_group) % TPR;
+            for (int q = g2; q < n; q += ngroups) {
+              const int r = row_of(q);
+              if (q != q_own && (!use_tbl || (r >= 0 && r < Pm)))
+                store_coherent4(po_rs, ((h2 * Pm + r) * D + 4 * c2) * 4, unwritten4);
+            }
+          }
+        }
+        float* rr = msm + 6 * slot;
+        rr[0] = M;
+        rr[1] = L;
+        rr[2] = acc[0];
+        rr[3] = acc[1];
+        rr[4] = acc[2];
+        rr[5] = acc[3];
+      }
+    }
+    if constexpr (DIRECT) return;
+    __syncthreads();
+    for (int i = t; i < G * n; i += NT) {
+      const int q = i % n;
+      const int r = row_of(q);
+      if (q != q_own && (!use_tbl || (r >= 0 && r < Pm)))
+        store_coherent1(pl_rs, ((i / n) * Pm + r) * 4, 0.0f);
+    }
+    for (int hc = t; hc < per_group; hc += NT) {
+      float M = -INFINITY;
+      for (int gi = 0; gi < ngroups; ++gi) M = fmaxf(M, msm[6 * (gi * per_group + hc)]);
+      const float mu = M == -INFINITY ? 0.0f : M;
+      float L = 0.0f;
+      f32x4 acc = zero4f();
+      for (int gi = 0; gi < ngroups; ++gi) {
+        const float* rr = msm + 6 * (gi * per_group + hc);
+        const float e = fast_exp2((rr[0] - mu) * kLog2e);
+        L += e * rr[1];
+        acc[0] += e * rr[2];
+        acc[1] += e * rr[3];
+        acc[2] += e * rr[4];
+        acc[3] += e * rr[5];
+      }
+      finish(hc / TPR, hc % TPR, M, L, acc);
     }
     if (!TWO || out != 2) return;
 
@@ -973,6 +1000,8 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
 //         by one of its workgroups.
 // MODE 3: MODE 2 with the two-level merge (merge_groups), for launches with
 //         more than kFlatMerge partitions per pair.
+// MODE 4: MODE 2 with the direct merge, for launches with at most
+//         kDirectMergeItems partitions per pair.
 //
 // Fused-step hand-off.  Each workgroup of a (b, kvh) with more than one
 // partition takes a ticket from the pair's counter early (its latency hides
@@ -993,6 +1022,7 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   constexpr bool SPLIT = MODE >= 1;
   constexpr bool STEP = MODE >= 2;
   constexpr bool TWO = MODE == 3;
+  constexpr bool DIRECT = MODE == 4;
   using SM = LineSmem<D, NS>;
   using LM = LineMap<D>;
 
@@ -1255,9 +1285,9 @@ __device__ __forceinline__ void attn_item(const AttnParams& a, const int b, cons
   }
   if (!STEP || n_parts <= 1 || !s_merge) return;
   __syncthreads();  // the merger's own partial is complete in LDS
-  __shared__ float msm[6 * kMergeSlots];
+  __shared__ float msm[DIRECT ? 4 : 6 * kMergeSlots];
   __shared__ int rowtbl[kMaxMergeGroups];
-  merge_step_partitions<D, NW, TWO>(a, b, kvh, n_parts, p, s_merge, own, msm, rowtbl);
+  merge_step_partitions<D, NW, TWO, DIRECT>(a, b, kvh, n_parts, p, s_merge, own, msm, rowtbl);
 }
 
 // Direct grid.  Unsplit decode: one workgroup per (sequence, KV head),

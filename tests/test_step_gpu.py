@@ -192,11 +192,13 @@ def test_step_other_shapes(Hq, Hkv, D, bs):
     _check_lse(lse, want_lse)
 
 
-@pytest.mark.parametrize("name,P", [("sweep:32:1024", 256), ("long:1:32768", 512)])
+@pytest.mark.parametrize("name,P", [("sweep:32:1024", 256), ("sweep:32:1024", 64),
+                                    ("long:1:32768", 512)])
 def test_step_in_hip_graph_replays(name, P):
     """The step is capture-safe: replays of a captured step, with eager work
-    and synchronisation between them, all equal the eager result (one-level
-    merge, and the two-level merge at 64 partitions per pair)."""
+    and synchronisation between them, all equal the eager result (the direct
+    merge at 4 partitions per pair, the merge through LDS at 16, and the
+    two-level merge at 64)."""
     c = case(name)
     g = to_gpu(c)
     ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
@@ -420,6 +422,77 @@ def test_step_two_level_merge_stress_against_three_launch_path():
                               dtype=torch.int32).to(g.q.device)
         if it % 5 == 0:
             g.ctx[0] = 400 * 16  # a launch with 100 partitions on one pair
+        fused = _step(g, c, P, ws, append=False, want_lse=False)
+        po, pl = pkv.paged_attention_decode_split(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale,
+                                                  P)
+        ref3 = pkv.split_reduce(po, pl, g.ctx, P)
+        torch.cuda.synchronize()
+        worst = max(worst, (fused.float() - ref3.float()).abs().max().item())
+        _check_workspace_restored(ws)
+    assert worst <= 2e-3, worst
+
+
+# Pairs with 0 to 4 partitions of 256 positions (max_blocks 64: at most 4
+# partitions per pair, so every launch takes the direct merge).
+DIRECT_LENS = [0, 1, 255, 256, 257, 511, 512, 700, 1023, 1024]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,grid", [(14, 2, 64, "auto"), (32, 2, 64, "auto"),
+                                           (16, 2, 128, "auto"), (32, 2, 128, "auto"),
+                                           (14, 2, 64, "compact")])
+def test_step_direct_merge(Hq, Hkv, D, grid):
+    """Launches with at most 4 partitions per pair, where each merging thread
+    takes every partition of its (head, 4 dims) and writes the output itself:
+    groups of 7 and 16 heads, head_dim 64 and 128 (at 16 heads of 128 dims a
+    thread takes two (head, 4 dims) slots), the direct and compact grids;
+    every sequence against the oracle's append + decode, two calls in a row
+    on one workspace, the second bit-identical to a repeat of itself."""
+    c = workloads.custom_case("step_direct", B=len(DIRECT_LENS), Hq=Hq, Hkv=Hkv, D=D,
+                              block_size=16, lens=DIRECT_LENS, seed=140, max_blocks=64)
+    P = 256
+    assert c.max_partitions(P) == 4
+    g = to_gpu(c)
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    out, lse = _step(g, c, P, ws, launch=dict(grid=grid))
+    torch.cuda.synchronize()
+    want, want_lse, kp, vp = _oracle_step(c)
+    check_fp16(out, want, f"direct merge {Hq}/{Hkv}/{D} {grid}")
+    _check_lse(lse, want_lse)
+    assert int((out[0] != 0).sum()) == 0
+    assert np.array_equal(g.k_pool.cpu().numpy().view(np.uint16), kp.view(np.uint16))
+    assert np.array_equal(g.v_pool.cpu().numpy().view(np.uint16), vp.view(np.uint16))
+    _check_workspace_restored(ws)
+    # a second call (no append) with other queries: the decode of the pool
+    # as the first call left it, and a repeat gives the same bits
+    g.q = torch.randn(g.q.shape, generator=torch.Generator(device=g.q.device).manual_seed(141),
+                      device=g.q.device).to(torch.float16)
+    again = _step(g, c, P, ws, append=False, want_lse=False, launch=dict(grid=grid)).clone()
+    repeat = _step(g, c, P, ws, append=False, want_lse=False, launch=dict(grid=grid))
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int16), repeat.view(torch.int16))
+    want2 = ref.paged_attention_decode(g.q.cpu().numpy(), kp, vp, c.block_tables,
+                                       c.context_lens, c.scale)
+    check_fp16(again, want2, f"direct merge second call {Hq}/{Hkv}/{D} {grid}")
+    _check_workspace_restored(ws)
+
+
+def test_step_direct_merge_stress_against_three_launch_path():
+    """40 fused steps at 4 partitions per pair (the direct merge) with new
+    queries and new context lengths, each against append + split pass +
+    split_reduce."""
+    c = case("sweep:32:1024")
+    P = 256
+    assert c.max_partitions(P) == 4
+    g = to_gpu(c)
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    gen = torch.Generator(device=g.q.device).manual_seed(15)
+    cpu_gen = torch.Generator().manual_seed(16)
+    full = g.ctx.clone()
+    worst = 0.0
+    for it in range(40):
+        g.q = torch.randn(g.q.shape, generator=gen, device=g.q.device).to(torch.float16)
+        g.ctx = (torch.randint(0, 1025, (c.B,), generator=cpu_gen, dtype=torch.int32)
+                 .to(g.q.device) if it % 2 else full)
         fused = _step(g, c, P, ws, append=False, want_lse=False)
         po, pl = pkv.paged_attention_decode_split(g.q, g.k_pool, g.v_pool, g.bt, g.ctx, c.scale,
                                                   P)
