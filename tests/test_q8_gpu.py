@@ -299,14 +299,16 @@ def test_q8_step_edge_lengths_and_slots():
         assert int((out[0] != 0).sum()) == 0
 
 
+@pytest.mark.parametrize("P", [256, 1024])
 @pytest.mark.parametrize("Hq,Hkv,D,bs", [(16, 1, 128, 32), (32, 8, 128, 16), (12, 1, 64, 16)])
-def test_q8_step_other_shapes(Hq, Hkv, D, bs):
+def test_q8_step_other_shapes(Hq, Hkv, D, bs, P):
+    """Other shapes at 10 and at 3 partitions per pair."""
     c = workloads.custom_case("q8_step_shapes", B=4, Hq=Hq, Hkv=Hkv, D=D, block_size=bs,
                               lens=[3, 200, 1000, 2500], seed=121)
     kc, vc, ks, vs = workloads.q8_pools(c)
     g = to_gpu(c)
     gq = _gpu_q8(kc, vc, ks, vs)
-    out = _step_q8(g, gq, c, 256, want_lse=False)
+    out = _step_q8(g, gq, c, P, want_lse=False)
     torch.cuda.synchronize()
     want_pools = ref.kv_cache_append_q8(kc, vc, ks, vs, c.k_new, c.v_new, c.slot_mapping)
     _check_pools_q8(gq, want_pools)
@@ -314,12 +316,13 @@ def test_q8_step_other_shapes(Hq, Hkv, D, bs):
     check_fp16(out, want, f"q8 step shapes {Hq}/{Hkv}/{D}/{bs}")
 
 
-def test_q8_step_in_hip_graph_replays():
+@pytest.mark.parametrize("P", [256, 64])
+def test_q8_step_in_hip_graph_replays(P):
     """Replays of a captured 8-bit step, with eager work and synchronisation
     between them, equal the eager result bitwise (the append rewrites the same
-    slots with the same codes, so every replay sees the same cache)."""
+    slots with the same codes, so every replay sees the same cache); at 4
+    and at 16 partitions per pair."""
     c = case("sweep:32:1024")
-    P = 256
     kc, vc, ks, vs = workloads.q8_pools(c)
     g = to_gpu(c)
     gq = _gpu_q8(kc, vc, ks, vs)
