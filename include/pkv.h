@@ -291,11 +291,11 @@ int paged_attention_decode_split_ex(float* partial_out, float* partial_lse,
  * in the launch by its workgroups: each takes a ticket from the pair's
  * counter line early, and the holder of the last ticket merges, reading the
  * other partitions' rows once none of their words is zero (device-coherent
- * accesses; the others never wait).  Past 16 partitions the merge has two
- * levels: the partitions form groups of about 8, the last ticket of each
- * group merges the group into its own row, and the pair's last ticket
- * merges the group results.  Mergers set the rows and words they read back
- * to zero.  Their waits are bounded in time (20 ms): a workspace that breaks
+ * accesses; the others never wait).  A pair with more than 32 partitions
+ * merges in two levels: the partitions form groups of about 8, the last
+ * ticket of each group merges the group into its own row, and the pair's
+ * last ticket merges the group results.  Mergers set the rows and words they
+ * read back to zero.  Their waits are bounded in time (20 ms): a workspace that breaks
  * the contract above gives wrong numbers, not a stalled queue.  A sequence
  * that fits one partition is written directly.  Results equal append +
  * split pass + split_reduce up to fp32 summation order, and do not depend
