@@ -262,6 +262,8 @@ def _probe_lib():
     lib.pkv_probe_stream_read.argtypes = [P, L, P, I, I, P]
     lib.pkv_probe_paged_read.restype = I
     lib.pkv_probe_paged_read.argtypes = [P, P, P, I, I, I, I, I, I, P, P]
+    lib.pkv_probe_paged_read_q8.restype = I
+    lib.pkv_probe_paged_read_q8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P]
     return lib
 
 
@@ -871,6 +873,24 @@ def run_q8(args):
         if best_split is None or us_split < best_split[1]:
             best_split = (P, us_split)
     us_unsplit = time_it(unsplit)
+    # the split pass's code and scale reads through the tables with no
+    # arithmetic, at its best partition size
+    probe_us = None
+    plib = _probe_lib()
+    if plib is not None and case.D == 64 and case.block_size == 16 and \
+            int(case.context_lens.min()) == int(case.context_lens.max()):
+        import ctypes
+        sink = torch.zeros(4, dtype=torch.int32, device=device)
+        vp = lambda x: ctypes.c_void_p(x.data_ptr())
+
+        def probe(r):
+            st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            rc = plib.pkv_probe_paged_read_q8(vp(codes_k), vp(codes_v), vp(sc_k), vp(sc_v),
+                                              vp(bt[r]), B, case.Hkv, ctx, R * NB,
+                                              bt[r].shape[1], best_split[0], vp(sink), st)
+            if rc != 0:
+                raise RuntimeError(f"8-bit paged probe launch failed: {rc}")
+        probe_us = time_it(probe)
     P, us_step = best
     step_bytes = q8_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
     app = 2 * B * case.Hkv * (case.D * 2 + case.D + 4) + 8 * B   # fp16 in, codes + scale out
@@ -909,6 +929,13 @@ def run_q8(args):
         "split_pass_best_partition": best_split[0],
         "unsplit_decode_us": round(us_unsplit, 3),
         "unsplit_decode_gbs": round(step_bytes / (us_unsplit * 1e-6) / 1e9, 1),
+        "probe_paged_q8_us": None if probe_us is None else round(probe_us, 3),
+        "probe_paged_q8_gbs": (None if probe_us is None else
+                               round(ctx_sum * case.Hkv * (case.D + 4) * 2 /
+                                     (probe_us * 1e-6) / 1e9, 1)),
+        "probe_paged_q8_shape": "the split pass's code and scale reads through the block "
+                                "tables (4 waves per workgroup, two subtiles in flight, "
+                                "one 16-byte load per lane per 1 KiB of codes), no arithmetic",
     }
     return res
 

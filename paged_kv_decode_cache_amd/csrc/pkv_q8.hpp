@@ -184,6 +184,13 @@ __device__ __forceinline__ void quantize_row_lanes(const f16* row, int quad,
   scale = amax / 127.0f;
 }
 
+// Codes and scales are each read once per pass: non-temporal loads, as the
+// fp16 kernels' K/V lines (bit-cast through a float vector, as load_b128).
+__device__ __forceinline__ f32x4 load_b128_stream(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(f32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNonTemporal));
+}
+
 template <int D, int NS>
 __device__ __forceinline__ void load_kv_tile8(KVTile8<D, NS>& T, const Q8Params& P, int ids,
                                               int s0, int sub_end, int t_end, int spb,
@@ -213,13 +220,13 @@ __device__ __forceinline__ void load_kv_tile8(KVTile8<D, NS>& T, const Q8Params&
     const int lo = (lane & 15) * D + 16 * quad;
 #pragma unroll
     for (int c = 0; c < D / 64; ++c) {
-      T.k[j][c] = __builtin_bit_cast(u32x4, load_b128(kr, lo + 64 * c));
-      T.v[j][c] = __builtin_bit_cast(u32x4, load_b128(vr, lo + 64 * c));
+      T.k[j][c] = __builtin_bit_cast(u32x4, load_b128_stream(kr, lo + 64 * c));
+      T.v[j][c] = __builtin_bit_cast(u32x4, load_b128_stream(vr, lo + 64 * c));
     }
     const __amdgpu_buffer_rsrc_t ksr = buffer_rsrc(P.k_scales + so, ok ? 64 : 0);
     const __amdgpu_buffer_rsrc_t vsr = buffer_rsrc(P.v_scales + so, ok ? 64 : 0);
-    T.ks[j] = load_b128(ksr, 16 * quad);
-    T.vs[j] = load_b128(vsr, 16 * quad);
+    T.ks[j] = load_b128_stream(ksr, 16 * quad);
+    T.vs[j] = load_b128_stream(vsr, 16 * quad);
   }
   T.okmask = okm;
   T.new_phys = new_phys;

@@ -12,6 +12,11 @@
 //                           16-token subtiles round-robin through the block
 //                           table, two subtiles in flight, whole 128-byte
 //                           head rows per 8 lanes, non-temporal.
+//   pkv_probe_paged_read_q8 the same over the 8-bit cache: per subtile one
+//                           head's 16 rows of 64 codes (1 KiB, one 16-byte
+//                           load per lane) of K and of V, and their 16 scales
+//                           (a 16-byte load per lane quad), as the 8-bit
+//                           decode kernels read them.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -93,6 +98,52 @@ __global__ __launch_bounds__(kWaves * 64) void paged_read_kernel(
     sink[0] = acc;
 }
 
+// 8-bit cache, head_dim 64, block size 16: codes [num_blocks, Hkv, 16, 64]
+// int8, scales [num_blocks, Hkv, 16] fp32.  A subtile is one block of one
+// head: 1 KiB of codes (lane l reads bytes 16l..16l+15) and 64 bytes of
+// scales (lane quad q reads tokens 4q..4q+3), for K and for V.
+__global__ __launch_bounds__(kWaves * 64) void paged_read_q8_kernel(
+    const unsigned char* __restrict__ kc, const unsigned char* __restrict__ vc,
+    const unsigned char* __restrict__ ks, const unsigned char* __restrict__ vs,
+    const int* __restrict__ bt, int max_blocks, int num_blocks, int Hkv, int ctx,
+    int partition_size, u32x4* sink) {
+  const int kvh = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t0 = p * partition_size;
+  const int t1 = min(ctx, t0 + partition_size);
+  const int s_begin = t0 >> 4, s_end = (t1 + 15) >> 4;
+  const int* row = bt + (size_t)b * max_blocks;
+  const int mine = s_begin + wave + kWaves * lane;
+  const int ids = mine < s_end ? row[mine] : 0;
+  const int coff = lane * 16, soff = (lane >> 4) * 16;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int i0 = 0; s_begin + wave + kWaves * i0 < s_end; i0 += 2) {
+    u32x4 x[2][4];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const int s = s_begin + wave + kWaves * (i0 + d);
+      const int blk = __builtin_amdgcn_readlane(ids, (i0 + d) & 63);
+      const bool ok = s < s_end && blk >= 0 && blk < num_blocks;
+      const size_t unit = (size_t)(ok ? blk : 0) * Hkv + kvh;  // (block, head)
+      const auto kr = rsrc(kc + unit * 1024, ok ? 1024 : 0);
+      const auto vr = rsrc(vc + unit * 1024, ok ? 1024 : 0);
+      const auto ksr = rsrc(ks + unit * 64, ok ? 64 : 0);
+      const auto vsr = rsrc(vs + unit * 64, ok ? 64 : 0);
+      x[d][0] = __builtin_amdgcn_raw_buffer_load_b128(kr, coff, 0, 2);
+      x[d][1] = __builtin_amdgcn_raw_buffer_load_b128(vr, coff, 0, 2);
+      x[d][2] = __builtin_amdgcn_raw_buffer_load_b128(ksr, soff, 0, 2);
+      x[d][3] = __builtin_amdgcn_raw_buffer_load_b128(vsr, soff, 0, 2);
+    }
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc ^= x[d][m];
+  }
+  if (acc[0] == 0x9E3779B9u && acc[1] == 0x7F4A7C15u && acc[2] == 0x85EBCA6Bu &&
+      acc[3] == 0xC2B2AE35u)
+    sink[0] = acc;
+}
+
 }  // namespace
 
 // Reads `bytes` (a multiple of 16) of src: grid workgroups of 256 lanes,
@@ -129,6 +180,32 @@ extern "C" int pkv_probe_paged_read(const void* k_pool, const void* v_pool,
                      static_cast<hipStream_t>(stream),
                      static_cast<const unsigned char*>(k_pool),
                      static_cast<const unsigned char*>(v_pool), block_tables, max_blocks,
+                     num_blocks, Hkv, ctx, partition_size, static_cast<u32x4*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+// The code and scale reads of an 8-bit split pass over B sequences of ctx
+// positions each (head_dim 64, block size 16: codes [num_blocks, Hkv, 16, 64]
+// int8, scales [num_blocks, Hkv, 16] fp32; tables [B, max_blocks]), no
+// arithmetic.
+extern "C" int pkv_probe_paged_read_q8(const void* k_codes, const void* v_codes,
+                                       const void* k_scales, const void* v_scales,
+                                       const int32_t* block_tables, int B, int Hkv, int ctx,
+                                       int num_blocks, int max_blocks, int partition_size,
+                                       void* sink, void* stream) {
+  if (!k_codes || !v_codes || !k_scales || !v_scales || !block_tables || !sink || B <= 0 ||
+      B > 65535 || Hkv <= 0 || ctx <= 0 || num_blocks <= 0 || max_blocks <= 0 ||
+      ctx > max_blocks * 16 || partition_size <= 0 || partition_size % 16 != 0 ||
+      partition_size > 16 * 64 * kWaves || (int64_t)num_blocks * Hkv * 1024 > ((int64_t)1 << 40))
+    return -1;
+  const int parts = (ctx + partition_size - 1) / partition_size;
+  if (parts > 65535) return -1;
+  hipLaunchKernelGGL(paged_read_q8_kernel, dim3(Hkv, parts, B), dim3(kWaves * 64), 0,
+                     static_cast<hipStream_t>(stream),
+                     static_cast<const unsigned char*>(k_codes),
+                     static_cast<const unsigned char*>(v_codes),
+                     static_cast<const unsigned char*>(k_scales),
+                     static_cast<const unsigned char*>(v_scales), block_tables, max_blocks,
                      num_blocks, Hkv, ctx, partition_size, static_cast<u32x4*>(sink));
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
