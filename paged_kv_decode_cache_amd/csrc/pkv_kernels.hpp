@@ -745,6 +745,75 @@ __device__ __forceinline__ void merge_rows(__amdgpu_buffer_rsrc_t po_rs,
   }
 }
 
+// The direct merge of n <= NO + 1 partitions (one level, no table): only the
+// other partitions' rows are requested, NO at once; the merge then takes the
+// items in partition order, the own partial at its place.
+template <int D, int NO>
+__device__ __forceinline__ void merge_direct_others(__amdgpu_buffer_rsrc_t po_rs,
+                                                    __amdgpu_buffer_rsrc_t pl_rs, int Pm, int n,
+                                                    int q_own, int hh, int cc, f32x4 own_x,
+                                                    float own_l, float& M, float& L,
+                                                    f32x4& acc) {
+  int xo[NO], lo[NO];
+  f32x4 x[NO];
+  float l[NO];
+  bool ok[NO], other[NO];
+#pragma unroll
+  for (int j = 0; j < NO; ++j) {
+    const int q = j < q_own ? j : j + 1;
+    other[j] = q < n;
+    xo[j] = other[j] ? ((hh * Pm + q) * D + 4 * cc) * 4 : kOutOfRange;
+    lo[j] = other[j] ? (hh * Pm + q) * 4 : kOutOfRange;
+    x[j] = load_coherent4(po_rs, xo[j]);
+    l[j] = load_coherent1(pl_rs, lo[j]);
+  }
+  bool all_ok = true;
+#pragma unroll
+  for (int j = 0; j < NO; ++j) {
+    ok[j] = !other[j] || row_written(x[j], l[j]);
+    all_ok = all_ok && ok[j];
+  }
+  const long long t_spin = __all(all_ok) ? 0 : (long long)__builtin_amdgcn_s_memrealtime();
+  while (!__all(all_ok) &&
+         (long long)__builtin_amdgcn_s_memrealtime() - t_spin < kSpinTicks) {
+    __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
+    f32x4 nx[NO];
+    float nl[NO];
+#pragma unroll
+    for (int j = 0; j < NO; ++j) {
+      nx[j] = load_coherent4(po_rs, ok[j] ? kOutOfRange : xo[j]);
+      nl[j] = load_coherent1(pl_rs, ok[j] ? kOutOfRange : lo[j]);
+    }
+    all_ok = true;
+#pragma unroll
+    for (int j = 0; j < NO; ++j) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) x[j][v] = ok[j] ? x[j][v] : nx[j][v];
+      l[j] = ok[j] ? l[j] : nl[j];
+      ok[j] = !other[j] || row_written(x[j], l[j]);
+      all_ok = all_ok && ok[j];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q <= NO; ++q) {
+    const bool mine = q == q_own;
+    const int j = q < q_own ? q : (q > 0 ? q - 1 : 0);
+    f32x4 xd;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) xd[v] = decode_partial(x[j][v]);
+    const float lq = q < n ? (mine ? own_l : decode_partial(l[j])) : -INFINITY;
+    const f32x4 xq = mine ? own_x : (q < n ? xd : zero4f());
+    const float Mn = fmaxf(M, lq);
+    const float mu = Mn == -INFINITY ? 0.0f : Mn;
+    const float sa = fast_exp2((M - mu) * kLog2e);
+    const float sb = fast_exp2((lq - mu) * kLog2e);
+    acc = acc * sa + xq * sb;
+    L = L * sa + sb;
+    M = Mn;
+  }
+}
+
 // The ticket word of (b, kvh) (words 0-1 of its counter line).
 __device__ __forceinline__ unsigned long long* step_ticket_word(const AttnParams& a, int b,
                                                                 int kvh) {
@@ -894,8 +963,8 @@ __device__ void merge_step_partitions(const AttnParams& a, int b, int kvh, int n
       float M = -INFINITY, L = 0.0f;
       f32x4 acc = zero4f();
       if constexpr (DIRECT) {
-        merge_rows<D, kDirectMergeItems>(po_rs, pl_rs, Pm, n, q_own, rowtbl, false, row0, 0, 1,
-                                         hh, cc, own_x, own_l, M, L, acc);
+        merge_direct_others<D, kDirectMergeItems - 1>(po_rs, pl_rs, Pm, n, q_own, hh, cc,
+                                                      own_x, own_l, M, L, acc);
         // Back to "not written" for the next launch.  The threads that read
         // a head's lse words are TPR consecutive lanes of one wave, all past
         // their loads here, so its first lane resets them.
