@@ -263,7 +263,7 @@ int launch_prefill(const pkv::PrefillParams& p, int64_t grid, hipStream_t st) {
 // fused step, which takes 1 (as the fp16 step: 15.9 vs 16.8 us at
 // B=32 x 4096, 11.3 vs 11.45 us at B=8 x 4096, 0.6% slower at B=128 x 8192).
 // MODE: 0 unsplit, 1 split pass, 2 fused decode step (3 with the two-level
-// merge).
+// merge, 4 with the direct merge).
 template <int D, int NW, int MODE>
 void launch_q8_nw(const pkv::Q8Params& p, int64_t grid, hipStream_t st) {
   constexpr int NS = (D == 64 && MODE < 2) ? 2 : 1;
@@ -280,6 +280,7 @@ template <int D, int MODE>
 int launch_q8(const pkv::Q8Params& p, int64_t grid, hipStream_t st) {
   if constexpr (MODE == 2) {
     if (p.a.max_partitions > pkv::kFlatMerge) return launch_q8<D, 3>(p, grid, st);
+    if (p.a.max_partitions <= pkv::kDirectMergeItems) return launch_q8<D, 4>(p, grid, st);
   }
   if constexpr (MODE >= 2 && D == 64) {
     if (step_wide_merge(D, grid, p.a.max_partitions, p.a.G))

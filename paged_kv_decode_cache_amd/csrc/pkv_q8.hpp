@@ -379,7 +379,8 @@ __device__ __forceinline__ void consume_tile8(KVTile8<D, NS>& T, SoftmaxState<D>
 // merge of each (sequence, KV head) by the holder of its last ticket, with
 // the fp16 step's hand-off (device-coherent partial rows polled until
 // written; merge_step_partitions).  MODE 3: MODE 2 with the two-level merge
-// of launches with more than kFlatMerge partitions per pair.
+// of launches with more than kFlatMerge partitions per pair; MODE 4: MODE 2
+// with the direct merge of launches with at most kDirectMergeItems.
 template <int D, int NS, int NW, int DEPTH, int MODE, bool DUAL>
 __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   constexpr int KC = D / 32;
@@ -388,6 +389,7 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   constexpr bool SPLIT = MODE >= 1;
   constexpr bool STEP = MODE >= 2;
   constexpr bool TWO = MODE == 3;
+  constexpr bool DIRECT = MODE == 4;
   using SM = AttnSmem<D, NS>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[NW * SM::kWaveBytes];
   const AttnParams& a = P.a;
@@ -617,9 +619,9 @@ __global__ __launch_bounds__(NW * 64) void attn_q8_kernel(const Q8Params P) {
   }
   if (!STEP || n_parts <= 1 || !s_merge) return;
   __syncthreads();  // the merger's own partial is complete in LDS
-  __shared__ float msm[6 * kMergeSlots];
+  __shared__ float msm[DIRECT ? 4 : 6 * kMergeSlots];
   __shared__ int rowtbl[kMaxMergeGroups];
-  merge_step_partitions<D, NW, TWO>(a, b, kvh, n_parts, p, s_merge, own, msm, rowtbl);
+  merge_step_partitions<D, NW, TWO, DIRECT>(a, b, kvh, n_parts, p, s_merge, own, msm, rowtbl);
 }
 
 }  // namespace pkv
