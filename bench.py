@@ -897,7 +897,8 @@ def run_q8(args):
     value = (step_bytes + app) / (us_step * 1e-6) / 1e9
     fp16_bytes = alg_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
     G = case.Hq // case.Hkv
-    q8_kernel = (f"void pkv::attn_q8_kernel<{case.D}, 1, 4, 2, {step_mode(case.max_partitions(P))}, "
+    q8_kernel = (f"void pkv::attn_q8_kernel<{case.D}, {2 if case.D == 64 else 1}, 4, 2, "
+                 f"{step_mode(case.max_partitions(P))}, "
                  f"{'true' if G <= 8 else 'false'}>(pkv::Q8Params)")
     traffic = (profiled_traffic(q8_kernel, TRAFFIC_PROFILES["q8"], Q8_KERNEL_SOURCES, P)
                if (B, ctx) == (32, 4096) and case.D == 64 else None)

@@ -258,15 +258,20 @@ int launch_prefill(const pkv::PrefillParams& p, int64_t grid, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
-// 8-bit decode: unsplit (8 waves), split pass or fused step (4 waves), 2
-// tiles in flight; 2 subtiles per tile at head_dim 64 (1 at 128), except the
-// fused step, which takes 1 (as the fp16 step: 15.9 vs 16.8 us at
-// B=32 x 4096, 11.3 vs 11.45 us at B=8 x 4096, 0.6% slower at B=128 x 8192).
+// 8-bit decode: unsplit (8 waves), split pass or fused step (4 waves, 8 on
+// long contexts over few pairs), 2 tiles in flight; 2 subtiles per tile at
+// head_dim 64 (1 at 128).  Unlike the fp16 step, the 4-wave 8-bit step takes
+// 2 as well: a wave's range is half the bytes, so one subtile per tile
+// leaves it more round trips per range (at its best partition size:
+// B=8 x 4096 11.1 -> 10.7 us, B=32 x 2048 11.5 -> 10.95 us, B=128 x 8192
+// 70.1 -> 69.2 us, B=32 x 4096 15.3 -> 15.2 us).  The 8-wave step keeps 1:
+// with 2, B=4 x 32768 was 0.4 us slower, B=1 x 32768 0.4 us faster and
+// B=1 x 131072 level.
 // MODE: 0 unsplit, 1 split pass, 2 fused decode step (3 with the two-level
 // merge, 4 with the direct merge).
 template <int D, int NW, int MODE>
 void launch_q8_nw(const pkv::Q8Params& p, int64_t grid, hipStream_t st) {
-  constexpr int NS = (D == 64 && MODE < 2) ? 2 : 1;
+  constexpr int NS = D == 64 && (MODE < 2 || NW == 4) ? 2 : 1;
   if (p.a.G <= 8)
     hipLaunchKernelGGL((pkv::attn_q8_kernel<D, NS, NW, 2, MODE, true>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, st, p);
