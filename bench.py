@@ -352,7 +352,14 @@ def profiled_traffic(kernel_name, profile, sources=KERNEL_SOURCES, partition_siz
     h = hashlib.sha256()
     for rel in sources:
         h.update(open(os.path.join(ROOT, rel), "rb").read())
-    if kv.get("kernel_sources_sha256") != h.hexdigest() or kv.get("kernel") != kernel_name:
+    if kv.get("kernel_sources_sha256") != h.hexdigest():
+        return None
+    if partition_size is not None and f"kernel_p{partition_size}" in kv:
+        # a summary may also give the kernel and bytes at other partition sizes
+        if kv[f"kernel_p{partition_size}"] != kernel_name:
+            return None
+        return int(kv[f"traffic_bytes_p{partition_size}"])
+    if kv.get("kernel") != kernel_name:
         return None
     if "partition_size" in kv and partition_size is not None and \
             int(kv["partition_size"]) != partition_size:
