@@ -502,8 +502,10 @@ def run_headline(args, gate=None):
         ms_per_step = fused_us * 1e-3
         kern_us = fused_us
         kbytes = step_bytes + app_bytes
-        kname = (f"void pkv::attn_kernel<{case.D}, {ns_step}, {nw}, {depth}, "
-                 f"{step_mode(case.max_partitions(P))}, {dual}>(pkv::AttnParams)")
+        Pm_s = case.max_partitions(P)
+        nw_step = args.waves or step_waves(case.D, B, case.Hkv, Pm_s)
+        kname = (f"void pkv::attn_kernel<{case.D}, {ns_step}, {nw_step}, {depth}, "
+                 f"{step_mode(Pm_s)}, {dual}>(pkv::AttnParams)")
         step_desc = "paged_decode_step (append + split pass + merge in one launch)"
     else:
         ms_per_step = three_us * 1e-3
@@ -904,8 +906,9 @@ def run_q8(args):
     value = (step_bytes + app) / (us_step * 1e-6) / 1e9
     fp16_bytes = alg_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
     G = case.Hq // case.Hkv
-    q8_kernel = (f"void pkv::attn_q8_kernel<{case.D}, {2 if case.D == 64 else 1}, 4, 2, "
-                 f"{step_mode(case.max_partitions(P))}, "
+    nw8 = step_waves(case.D, B, case.Hkv, case.max_partitions(P))
+    q8_kernel = (f"void pkv::attn_q8_kernel<{case.D}, {2 if case.D == 64 and nw8 == 4 else 1}, "
+                 f"{nw8}, 2, {step_mode(case.max_partitions(P))}, "
                  f"{'true' if G <= 8 else 'false'}>(pkv::Q8Params)")
     traffic = (profiled_traffic(q8_kernel, TRAFFIC_PROFILES["q8"], Q8_KERNEL_SOURCES, P)
                if (B, ctx) == (32, 4096) and case.D == 64 else None)
@@ -1097,15 +1100,23 @@ def step_mode(max_partitions):
     return 3 if max_partitions > 32 else (4 if max_partitions <= 4 else 2)
 
 
-def gate_expected(D, G, Pm, args):
+def step_waves(D, B, Hkv, Pm):
+    """Waves per workgroup of the fused step at the library's default shape:
+    8 at head_dim 64 when the grid is at most 256 workgroups and a pair has
+    at least 8 partitions, else 4."""
+    return 8 if D == 64 and B * Hkv * Pm <= 256 and Pm >= 8 else 4
+
+
+def gate_expected(D, G, Pm, args, B=32, Hkv=2):
     """Kernel names one fused step and one three-launch step must launch, at
     the library's default shapes (or the explicit ones)."""
     dual = "true" if G <= 8 else "false"
     ns_step = args.subtiles or 1
     ns = args.subtiles or (2 if D == 64 else 1)
     nw, depth = args.waves or 4, args.depth or 2
+    nw_step = args.waves or step_waves(D, B, Hkv, Pm)
     return {
-        "fused": [f"void pkv::attn_kernel<{D}, {ns_step}, {nw}, {depth}, {step_mode(Pm)}, {dual}>"
+        "fused": [f"void pkv::attn_kernel<{D}, {ns_step}, {nw_step}, {depth}, {step_mode(Pm)}, {dual}>"
                   "(pkv::AttnParams)"],
         "three_launch": ["pkv::append_kernel(pkv::AppendParams)",
                          f"void pkv::attn_kernel<{D}, {ns}, {nw}, {depth}, 1, {dual}>"
@@ -1192,7 +1203,7 @@ def run_kernel_gate(args):
         args.batch in workloads.SWEEP_B and args.ctx in workloads.SWEEP_CTX) else None
     Hq, Hkv, D = (case.Hq, case.Hkv, case.D) if case else (14, 2, 64)
     Pm = case.max_partitions(args.partition) if case else -(-args.ctx // args.partition)
-    want = gate_expected(D, Hq // Hkv, Pm, args)
+    want = gate_expected(D, Hq // Hkv, Pm, args, args.batch, Hkv)
     problems = []
     matched = set()
     for path, names in want.items():

@@ -154,18 +154,20 @@ void launch_compact(const AttnParams& p, int64_t wgs, hipStream_t st) {
 }
 
 // The fused steps (fp16 and 8-bit) take 8 waves when the grid is at most
-// one workgroup per CU and either a pair has more than 16 partitions (few
-// workgroups stream long contexts, and the merges are large) or the merging
-// workgroup's threads at 4 waves would hold more partition rows than one
-// batch of loads (groups of 16 query heads).  With 16 partitions or fewer
-// and one batch, or with more workgroups than CUs, 4 waves stay faster.
+// one workgroup per CU and a pair has at least 8 partitions: few workgroups
+// then stream the context, twice the waves keep twice the requests in
+// flight, and the merge spreads its rows over twice the threads.  Same-box
+// A/B of the fp16 step, 4 -> 8 waves (us): B=1 x 4096 P=256 8.4 -> 7.6,
+// B=8 x 4096 P=256 9.4 -> 9.0, B=8 x 4096 P=512 9.7-10.2 -> 8.9-9.3,
+// B=8 x 2048 P=256 7.9 -> 7.5, B=1 x 2048 P=256 7.3 -> 6.9.  With 4
+// partitions it was level or slower (B=32 x 1024 P=256 7.7 -> 8.0,
+// B=8 x 512 P=128 5.6 -> 5.9, B=32 x 4096 P=1024 15.2 -> 15.65), and with
+// more workgroups than CUs 4 waves stay faster.
 constexpr int64_t kStepWideMergeMaxGrid = 256;
-bool step_wide_merge(int head_dim, int64_t grid, int max_partitions, int group) {
-  if (head_dim != 64 || grid > kStepWideMergeMaxGrid || max_partitions < 2) return false;
-  if (max_partitions > 16) return true;
-  const int per_set = group * (64 / 4);  // merge threads per set of partitions (4 dims each)
-  const int sets4 = per_set <= 4 * 64 ? 4 * 64 / per_set : 1;
-  return (max_partitions + sets4 - 1) / sets4 > pkv::kMergeRowsInFlight;
+constexpr int kStepWideMinPartitions = 8;
+bool step_wide_merge(int head_dim, int64_t grid, int max_partitions, int /*group*/) {
+  return head_dim == 64 && grid <= kStepWideMergeMaxGrid &&
+         max_partitions >= kStepWideMinPartitions;
 }
 
 // MODE: 0 unsplit, 1 split pass, 2 fused step; the fused step's launches
