@@ -906,7 +906,8 @@ def run_q8(args):
     value = (step_bytes + app) / (us_step * 1e-6) / 1e9
     fp16_bytes = alg_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
     G = case.Hq // case.Hkv
-    nw8 = step_waves(case.D, B, case.Hkv, case.max_partitions(P))
+    nw8 = 8 if case.D == 64 and step_mode(case.max_partitions(P)) == 4 else \
+        step_waves(case.D, B, case.Hkv, case.max_partitions(P))
     q8_kernel = (f"void pkv::attn_q8_kernel<{case.D}, {2 if case.D == 64 and nw8 == 4 else 1}, "
                  f"{nw8}, 2, {step_mode(case.max_partitions(P))}, "
                  f"{'true' if G <= 8 else 'false'}>(pkv::Q8Params)")

@@ -266,14 +266,15 @@ int launch_prefill(const pkv::PrefillParams& p, int64_t grid, hipStream_t st) {
 // 2 as well: a wave's range is half the bytes, so one subtile per tile
 // leaves it more round trips per range (at its best partition size:
 // B=8 x 4096 11.1 -> 10.7 us, B=32 x 2048 11.5 -> 10.95 us, B=128 x 8192
-// 70.1 -> 69.2 us, B=32 x 4096 15.3 -> 15.2 us).  The 8-wave step keeps 1:
-// with 2, B=4 x 32768 was 0.4 us slower, B=1 x 32768 0.4 us faster and
-// B=1 x 131072 level.
+// 70.1 -> 69.2 us, B=32 x 4096 15.3 -> 15.2 us).  8-wave launches (step
+// or split pass) take 1: with 2, the step at B=4 x 32768 was 0.4 us
+// slower, at B=1 x 32768 0.4 us faster and at B=1 x 131072 level, and the
+// direct-merge step at B=128 x 4096 37.6 -> 45.2 us.
 // MODE: 0 unsplit, 1 split pass, 2 fused decode step (3 with the two-level
 // merge, 4 with the direct merge).
 template <int D, int NW, int MODE>
 void launch_q8_nw(const pkv::Q8Params& p, int64_t grid, hipStream_t st) {
-  constexpr int NS = D == 64 && (MODE < 2 || NW == 4) ? 2 : 1;
+  constexpr int NS = D == 64 && (MODE == 0 || NW == 4) ? 2 : 1;
   if (p.a.G <= 8)
     hipLaunchKernelGGL((pkv::attn_q8_kernel<D, NS, NW, 2, MODE, true>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, st, p);
@@ -282,7 +283,13 @@ void launch_q8_nw(const pkv::Q8Params& p, int64_t grid, hipStream_t st) {
                        dim3(NW * 64), 0, st, p);
 }
 
-// The fused step takes 8 waves where the fp16 step does (step_wide_merge).
+// The fused step takes 8 waves where the fp16 step does (step_wide_merge),
+// and always with the direct merge (MODE 4): its loop is latency-bound, and
+// two waves per SIMD at 4 partitions per pair beat 8 partitions of 4-wave
+// workgroups (same-box A/B, us: B=32 x 4096 at P=1024 15.25-15.43 ->
+// 13.56-13.79, B=32 x 2048 at P=512 11.28 -> 10.29-10.36, B=8 x 1024 at
+// P=512 10.12-10.15 -> 9.42-9.65, B=128 x 4096 at P=1024 level).  The fp16
+// step keeps 4 waves there (15.2 -> 15.65 us at B=32 x 4096).
 template <int D, int MODE>
 int launch_q8(const pkv::Q8Params& p, int64_t grid, hipStream_t st) {
   if constexpr (MODE == 2) {
@@ -290,7 +297,19 @@ int launch_q8(const pkv::Q8Params& p, int64_t grid, hipStream_t st) {
     if (p.a.max_partitions <= pkv::kDirectMergeItems) return launch_q8<D, 4>(p, grid, st);
   }
   if constexpr (MODE >= 2 && D == 64) {
-    if (step_wide_merge(D, grid, p.a.max_partitions, p.a.G))
+    if (MODE == 4 || step_wide_merge(D, grid, p.a.max_partitions, p.a.G))
+      launch_q8_nw<D, 8, MODE>(p, grid, st);
+    else
+      launch_q8_nw<D, 4, MODE>(p, grid, st);
+  } else if constexpr (MODE == 1 && D == 64) {
+    // The split pass likewise takes 8 waves (one subtile) at partitions of
+    // 1024 positions or more on at most one workgroup per CU: same-box A/B
+    // in both orders, us: B=32 x 4096 at P=1024 12.1 -> 10.35 (its best
+    // partition size now; 10.8-11.2 at P=512 with 4 waves), B=4 x 32768
+    // 10.8 -> 10.3-10.8.  Shorter partitions and larger grids keep 4 waves
+    // (8 was 0.05-0.13 us slower at B=1 x 4096, B=1 x 32768 and B=8 x 4096,
+    // and 1.7 us slower at B=128 x 8192).
+    if (grid <= kStepWideMergeMaxGrid && p.a.partition_size >= 1024)
       launch_q8_nw<D, 8, MODE>(p, grid, st);
     else
       launch_q8_nw<D, 4, MODE>(p, grid, st);

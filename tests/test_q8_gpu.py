@@ -87,7 +87,10 @@ def test_decode_q8_matches_oracle(name):
 
 
 @pytest.mark.parametrize("name,P", [("qwen", 256), ("sweep:32:4096", 512), ("tiny", 16),
-                                    ("long:1:32768", 512), ("sweep:8:1024", 64)])
+                                    ("long:1:32768", 512), ("sweep:8:1024", 64),
+                                    # 8-wave split passes (long partitions, <= 256 workgroups)
+                                    ("sweep:32:4096", 1024), ("long:4:32768", 1024),
+                                    ("sweep:8:4096", 2048)])
 def test_split_q8_matches_oracle(name, P):
     c = case(name)
     say(f"split q8 {name} P={P}")
