@@ -883,8 +883,8 @@ def run_q8(args):
             best_split = (P, us_split)
     us_unsplit = time_it(unsplit)
     # the split pass's code and scale reads through the tables with no
-    # arithmetic, at its best partition size
-    probe_us = None
+    # arithmetic (a 4-wave read per partition), at its fastest partition size
+    probe_us, probe_P = None, None
     plib = _probe_lib()
     if plib is not None and case.D == 64 and case.block_size == 16 and \
             int(case.context_lens.min()) == int(case.context_lens.max()):
@@ -892,14 +892,17 @@ def run_q8(args):
         sink = torch.zeros(4, dtype=torch.int32, device=device)
         vp = lambda x: ctypes.c_void_p(x.data_ptr())
 
-        def probe(r):
+        def probe(r, P):
             st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
             rc = plib.pkv_probe_paged_read_q8(vp(codes_k), vp(codes_v), vp(sc_k), vp(sc_v),
                                               vp(bt[r]), B, case.Hkv, ctx, R * NB,
-                                              bt[r].shape[1], best_split[0], vp(sink), st)
+                                              bt[r].shape[1], P, vp(sink), st)
             if rc != 0:
                 raise RuntimeError(f"8-bit paged probe launch failed: {rc}")
-        probe_us = time_it(probe)
+        for Pp in (256, 512, 1024):
+            us = time_it(lambda r, Pp=Pp: probe(r, Pp))
+            if probe_us is None or us < probe_us:
+                probe_us, probe_P = us, Pp
     P, us_step = best
     step_bytes = q8_bytes(B, ctx_sum, case.Hq, case.Hkv, case.D)
     app = 2 * B * case.Hkv * (case.D * 2 + case.D + 4) + 8 * B   # fp16 in, codes + scale out
@@ -942,6 +945,7 @@ def run_q8(args):
         "unsplit_decode_us": round(us_unsplit, 3),
         "unsplit_decode_gbs": round(step_bytes / (us_unsplit * 1e-6) / 1e9, 1),
         "probe_paged_q8_us": None if probe_us is None else round(probe_us, 3),
+        "probe_paged_q8_partition": probe_P,
         "probe_paged_q8_gbs": (None if probe_us is None else
                                round(ctx_sum * case.Hkv * (case.D + 4) * 2 /
                                      (probe_us * 1e-6) / 1e9, 1)),
