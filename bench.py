@@ -867,7 +867,7 @@ def run_q8(args):
     # each path at its best partition size: the fused step (the step of
     # record), the three-launch step and the split pass alone
     best, best3, best_split = None, None, None
-    for P in (256, 512, 1024):
+    for P in [P for P in (256, 512, 1024, 2048, 4096) if P == 256 or P <= int(case.context_lens.max())]:
         Pm = case.max_partitions(P)
         po = torch.empty((B, case.Hq, Pm, case.D), dtype=torch.float32, device=device)
         pl = torch.empty((B, case.Hq, Pm), dtype=torch.float32, device=device)
