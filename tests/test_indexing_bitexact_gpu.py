@@ -183,9 +183,12 @@ def _q8_hot_v(c, vc, hot):
     return (rows.astype(np.float64) * 2.0 ** -6).astype(np.float16)
 
 
-@pytest.mark.parametrize("path", ["decode", "split64", "split256", "step64", "step256",
-                                  "step_compact"])
+@pytest.mark.parametrize("path", ["decode", "split64", "split256", "split1024", "step64",
+                                  "step256", "step512", "step_compact"])
 def test_q8_argmax_probe_bit_exact(path):
+    """split1024 is the 8-wave split pass (long partitions, few workgroups);
+    step256 and step512 the 8-wave step with the direct merge; step64 the
+    4-wave step with the merge through LDS."""
     c, kc, vc, ks, vs, q, hot = _q8_probe()
     g = to_gpu(c)
     g.q = _t(q)
@@ -283,11 +286,12 @@ def test_block_permutation_bit_identical_q8():
 
     def run(g, pools, bt, slots):
         o = {"decode": pkv.paged_attention_decode_q8(g.q, *pools, bt, g.ctx, c.scale)}
-        po, pl = pkv.paged_attention_decode_split_q8(g.q, *pools, bt, g.ctx, c.scale, 256)
-        o["split"] = pkv.split_reduce(po, pl, g.ctx, 256)
-        o["step"] = pkv.paged_decode_step_q8(g.q, *[x.clone() for x in pools], bt, g.ctx,
-                                             c.scale, 256, k_new=g.k_new, v_new=g.v_new,
-                                             slot_mapping=slots)
+        for P in (256, 1024):  # 4- and 8-wave split passes; LDS and direct merges
+            po, pl = pkv.paged_attention_decode_split_q8(g.q, *pools, bt, g.ctx, c.scale, P)
+            o[f"split{P}"] = pkv.split_reduce(po, pl, g.ctx, P)
+            o[f"step{P}"] = pkv.paged_decode_step_q8(g.q, *[x.clone() for x in pools], bt,
+                                                     g.ctx, c.scale, P, k_new=g.k_new,
+                                                     v_new=g.v_new, slot_mapping=slots)
         torch.cuda.synchronize()
         return o
 
