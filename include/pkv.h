@@ -106,8 +106,7 @@ int pkv_version(void);
  *                      sequence unsplit, one partition in the split pass and
  *                      the fused step).  Defaults: 8 unsplit, 4 split; the
  *                      fused step takes 4, or 8 when the grid is at most 256
- *                      workgroups and the merging workgroup's threads would
- *                      each hold more than 8 partition rows at 4 waves.
+ *                      workgroups and a pair has at least 8 partitions.
  *   subtiles_per_tile  16-token subtiles a wave loads per tile: 1, 2 or 4
  *                      (defaults: 2 at head_dim 64 except the fused step's 1;
  *                      1 at head_dim 128).

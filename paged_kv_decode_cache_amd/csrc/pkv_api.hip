@@ -260,8 +260,8 @@ int launch_prefill(const pkv::PrefillParams& p, int64_t grid, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
-// 8-bit decode: unsplit (8 waves), split pass or fused step (4 waves, 8 on
-// long contexts over few pairs), 2 tiles in flight; 2 subtiles per tile at
+// 8-bit decode: unsplit (8 waves), split pass or fused step (4 waves, or 8
+// under the rules of launch_q8), 2 tiles in flight; 2 subtiles per tile at
 // head_dim 64 (1 at 128).  Unlike the fp16 step, the 4-wave 8-bit step takes
 // 2 as well: a wave's range is half the bytes, so one subtile per tile
 // leaves it more round trips per range (at its best partition size:
