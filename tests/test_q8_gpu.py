@@ -431,3 +431,36 @@ def test_q8_step_two_level_merge_g16_d128():
     fin = np.isfinite(want_lse)
     assert float(np.abs(g_lse[fin] - want_lse[fin]).max()) <= PARTIAL_ATOL
     _check_workspace_restored(ws)
+
+
+@pytest.mark.parametrize("P", [256, 1024])
+def test_q8_step_8wave_stress_against_three_launch_path(P):
+    """20 fused 8-bit steps with new queries and new context lengths, each
+    against the 8-bit split pass + split_reduce at the same partition size:
+    at P=256 four partitions per pair (the 8-wave direct merge), at P=1024
+    one (the 8-wave split pass beside it).  Each step is also repeated on
+    the same inputs and must match itself bitwise."""
+    c = case("sweep:32:1024")
+    assert c.max_partitions(256) == 4
+    kc, vc, ks, vs = workloads.q8_pools(c)
+    g = to_gpu(c)
+    gq = _gpu_q8(kc, vc, ks, vs)
+    ws = pkv.StepWorkspace(c.B, c.Hq, c.Hkv, c.D, c.max_partitions(P), g.q.device)
+    gen = torch.Generator(device=g.q.device).manual_seed(25)
+    cpu_gen = torch.Generator().manual_seed(26)
+    full = g.ctx.clone()
+    worst = 0.0
+    say(f"q8 8-wave stress P={P}")
+    for it in range(20):
+        g.q = torch.randn(g.q.shape, generator=gen, device=g.q.device).to(torch.float16)
+        g.ctx = (torch.randint(0, 1025, (c.B,), generator=cpu_gen, dtype=torch.int32)
+                 .to(g.q.device) if it % 2 else full)
+        fused = pkv.paged_decode_step_q8(g.q, *gq, g.bt, g.ctx, c.scale, P, workspace=ws)
+        again = pkv.paged_decode_step_q8(g.q, *gq, g.bt, g.ctx, c.scale, P, workspace=ws)
+        po, pl = pkv.paged_attention_decode_split_q8(g.q, *gq, g.bt, g.ctx, c.scale, P)
+        ref3 = pkv.split_reduce(po, pl, g.ctx, P)
+        torch.cuda.synchronize()
+        assert torch.equal(fused.view(torch.int16), again.view(torch.int16)), f"repeat {it}"
+        worst = max(worst, (fused.float() - ref3.float()).abs().max().item())
+        _check_workspace_restored(ws)
+    assert worst <= 2e-3, worst
