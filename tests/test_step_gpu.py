@@ -49,7 +49,10 @@ def _check_lse(got, want, rows=None):
                                     ("sweep:32:4096", 512), ("sweep:1:128", 512),
                                     ("sweep:8:2048", 256), ("long:1:32768", 512),
                                     ("long:4:32768", 2048), ("long:4:32768", 1024),
-                                    ("long:4:32768", 512)])
+                                    ("long:4:32768", 512),
+                                    # 8-wave defaults on small grids (8 and 16 partitions)
+                                    ("sweep:8:4096", 256), ("sweep:1:4096", 256),
+                                    ("sweep:8:4096", 512)])
 def test_step_matches_append_then_decode(name, P):
     c = case(name)
     say(f"step {name} P={P}")
